@@ -1,0 +1,275 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: a library
+attention routine, a brute-force pure-Python top-N, hand-built cases with a known
+answer, invariants and the worked example of the explainer page. Together they
+fail on a dropped scale, a sign error in the softmax, a wrong key/value head map,
+a transposed operand, '>' instead of '>=', or a wrong refresh schedule.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import saga_oracle as orc
+from sparse_decode_attention_saga_amd import bytemodel
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(seed, B=2, h_q=8, h_k=2, h_v=4, d=16, L_max=40, lens=(40, 23)):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, h_q, d))
+    K = rng.standard_normal((B, h_k, L_max, d))
+    V = rng.standard_normal((B, h_v, L_max, d))
+    return q, K, V, np.array(lens[:B])
+
+
+def sdpa_row(q_j, K_rows, V_rows, mask=None):
+    """torch's attention on one query row (float64, CPU); default scale 1/sqrt(d)."""
+    qt = torch.from_numpy(q_j)[None, None, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(K_rows))[None, None]
+    vt = torch.from_numpy(np.ascontiguousarray(V_rows))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None, None, :]
+    return F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)[0, 0, 0].numpy()
+
+
+def brute_topn(q_j, K_rows, N):
+    """Pure-Python: logits by explicit loops, then the N best indices by a full sort."""
+    d = len(q_j)
+    s = 1.0 / math.sqrt(d)
+    scores = [sum(float(q_j[c]) * float(K_rows[i][c]) for c in range(d)) * s
+              for i in range(len(K_rows))]
+    order = sorted(range(len(scores)), key=lambda i: -scores[i])
+    return sorted(order[:N]), scores
+
+
+# --- dense limit (N >= l_kv) and GQA reduce to library attention ----------------
+
+@pytest.mark.parametrize("h_k,h_v", [(2, 4), (1, 8), (4, 4), (8, 2)])
+def test_dense_limit_equals_library_attention(h_k, h_v):
+    q, K, V, lens = rand_case(1, h_q=8, h_k=h_k, h_v=h_v)
+    r = orc.saga_decode_step(q, K, V, lens, N=10 ** 6, refresh_period=1, step=0)
+    for b in range(q.shape[0]):
+        L = lens[b]
+        for j in range(8):
+            g, v = j * h_k // 8, j * h_v // 8
+            ref = sdpa_row(q[b, j], K[b, g, :L], V[b, v, :L])
+            np.testing.assert_allclose(r.O[b, j], ref, rtol=0, atol=1e-12)
+            assert r.sel[b][j].tolist() == list(range(L))
+            assert r.tau[b, j] == -np.inf
+
+
+def test_equal_heads_is_grouped_query_attention():
+    # h_k == h_v: the library's own grouped-query attention (enable_gqa) fixes the
+    # head grouping independently of the oracle's head maps.
+    q, K, V, _ = rand_case(2, B=2, h_q=8, h_k=2, h_v=2, L_max=30, lens=(30, 30))
+    lens = np.array([30, 30])
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(K), torch.from_numpy(V),
+        enable_gqa=True)[:, :, 0].numpy()
+    sparse = orc.saga_decode_step(q, K, V, lens, N=30, refresh_period=1, step=0)
+    np.testing.assert_allclose(sparse.O, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(orc.dense_gqa(q, K, V, lens), ref, rtol=0, atol=1e-12)
+
+
+def test_dense_gqa_ragged_lengths():
+    q, K, V, lens = rand_case(3, h_k=4, h_v=4)
+    O = orc.dense_gqa(q, K, V, lens)
+    for b in range(2):
+        for j in range(8):
+            ref = sdpa_row(q[b, j], K[b, j // 2, :lens[b]], V[b, j // 2, :lens[b]])
+            np.testing.assert_allclose(O[b, j], ref, rtol=0, atol=1e-12)
+
+
+# --- refresh step = exact top-N (eq. 6-7) ---------------------------------------
+
+@pytest.mark.parametrize("N", [1, 2, 7, 22, 23])
+def test_refresh_equals_bruteforce_topn(N):
+    q, K, V, lens = rand_case(4, h_q=4, h_k=1, h_v=2, d=8, L_max=30, lens=(30, 23))
+    r = orc.saga_decode_step(q, K, V, lens, N=N, refresh_period=1, step=0)
+    for b in range(2):
+        L = lens[b]
+        for j in range(4):
+            want, scores = brute_topn(q[b, j], K[b, 0, :L], N)
+            assert r.sel[b][j].tolist() == want
+            mask = np.zeros(L, bool)
+            mask[want] = True
+            ref = sdpa_row(q[b, j], K[b, 0, :L], V[b, j // 2, :L], mask)
+            np.testing.assert_allclose(r.O[b, j], ref, rtol=0, atol=1e-12)
+            if N < L:
+                assert math.isclose(r.tau[b, j], sorted(scores)[::-1][N - 1], rel_tol=1e-12)
+                assert len(want) == N
+
+
+def test_nth_largest_matches_partition_with_repeats():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        L = int(rng.integers(1, 60))
+        a = rng.integers(-4, 5, size=L).astype(np.float64) * 0.5  # many repeats, +-0
+        N = int(rng.integers(1, L + 3))
+        want = -np.inf if N >= L else np.partition(a, L - N)[L - N]
+        assert orc.nth_largest(a, N) == want
+
+
+# --- threshold semantics: >=, ties kept, largest not smallest -------------------
+
+def test_ties_at_threshold_are_all_kept():
+    # d=4, q = e0, so logit_i = K[i,0] / 2; five keys tie at the 3rd-largest value.
+    q = np.zeros((1, 1, 4)); q[0, 0, 0] = 1.0
+    col = np.array([10., 8., 6., 6., 6., 4., 2.])
+    K = np.zeros((1, 1, 7, 4)); K[0, 0, :, 0] = col
+    V = np.arange(7 * 4, dtype=np.float64).reshape(1, 1, 7, 4)
+    lens = np.array([7])
+    expect = {1: [0], 2: [0, 1], 3: [0, 1, 2, 3, 4], 5: [0, 1, 2, 3, 4], 6: [0, 1, 2, 3, 4, 5], 7: list(range(7))}
+    for N, idx in expect.items():
+        r = orc.saga_decode_step(q, K, V, lens, N=N, refresh_period=1, step=0)
+        assert r.sel[0][0].tolist() == idx, N
+        if N < 7:
+            assert r.tau[0, 0] == col[N - 1] / 2
+
+
+def test_identical_keys_keep_everything_and_average_values():
+    # All logits equal: the N-th largest equals every logit, all tie and are kept,
+    # and the softmax is uniform, so O is the mean of the value rows.
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 2, 8))
+    K = np.repeat(rng.standard_normal((1, 1, 1, 8)), 50, axis=2)
+    V = rng.standard_normal((1, 2, 50, 8))
+    r = orc.saga_decode_step(q, K, V, np.array([50]), N=5, refresh_period=1, step=0)
+    for j in range(2):
+        assert r.sel[0][j].size == 50
+        np.testing.assert_allclose(r.O[0, j], V[0, j].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_head_maps_and_largest_entry():
+    # h_q=6, h_k=2, h_v=3. Key head g holds one huge key at position p[g]; with
+    # N=1 query head j must pick p[g(j)] and return value row V[v(j), p[g(j)]].
+    h_q, h_k, h_v, d, L = 6, 2, 3, 8, 20
+    rng = np.random.default_rng(7)
+    p = [3, 11]
+    q = np.zeros((1, h_q, d)); q[0, :, 0] = 1.0
+    K = 0.01 * rng.standard_normal((1, h_k, L, d))
+    K[0, 0, p[0], 0] = 10.0
+    K[0, 1, p[1], 0] = 10.0
+    K[0, 0, p[1], 0] = -10.0          # the other head's spike is a minimum here
+    V = np.zeros((1, h_v, L, d))
+    for h in range(h_v):
+        for i in range(L):
+            V[0, h, i, 0], V[0, h, i, 1] = h, i
+    r = orc.saga_decode_step(q, K, V, np.array([L]), N=1, refresh_period=1, step=0)
+    g_of = [0, 0, 0, 1, 1, 1]
+    v_of = [0, 0, 1, 1, 2, 2]
+    for j in range(h_q):
+        assert r.sel[0][j].tolist() == [p[g_of[j]]]
+        assert r.O[0, j, 0] == v_of[j] and r.O[0, j, 1] == p[g_of[j]]
+
+
+# --- invariants ------------------------------------------------------------------
+
+def test_probabilities_sum_to_one_and_output_is_convex():
+    q, K, V, lens = rand_case(8, d=32, L_max=200, lens=(200, 150))
+    for N in (1, 5, 64):
+        r = orc.saga_decode_step(q, K, V, lens, N=N, refresh_period=1, step=0)
+        assert np.all(np.abs(r.sum_p - 1.0) <= 1e-12)
+        for b in range(2):
+            for j in range(8):
+                rows = V[b, j * 4 // 8, r.sel[b][j]]
+                assert np.all(r.O[b, j] >= rows.min(axis=0) - 1e-12)
+                assert np.all(r.O[b, j] <= rows.max(axis=0) + 1e-12)
+
+
+def test_key_permutation_permutes_selection_only():
+    q, K, V, lens = rand_case(9, B=1, lens=(40,))
+    perm = np.random.default_rng(10).permutation(40)
+    r1 = orc.saga_decode_step(q, K, V, lens, N=6, refresh_period=1, step=0)
+    r2 = orc.saga_decode_step(q, K[:, :, perm], V[:, :, perm], lens, N=6, refresh_period=1, step=0)
+    np.testing.assert_allclose(r1.O, r2.O, rtol=0, atol=1e-12)
+    for j in range(8):
+        assert sorted(perm[r2.sel[0][j]].tolist()) == r1.sel[0][j].tolist()
+
+
+def test_empty_sequence():
+    q, K, V, _ = rand_case(11)
+    tau_in = np.full((2, 8), 0.25)
+    r = orc.saga_decode_step(q, K, V, np.array([0, 23]), N=4, refresh_period=4, step=1, tau_in=tau_in)
+    assert np.all(r.O[0] == 0) and np.all(r.tau[0] == 0.25)
+    assert all(s.size == 0 for s in r.sel[0])
+
+
+# --- periodic refresh and stale thresholds ---------------------------------------
+
+def test_stale_threshold_reused_between_refreshes():
+    # Frozen q and K: stale steps keep exactly the refresh step's selection; the
+    # exact threshold is recomputed at t = 0 and t = 3 only (period n = 3).
+    q, K, V, lens = rand_case(12, B=1, lens=(40,))
+    tau = None
+    sels = []
+    for t in range(6):
+        r = orc.saga_decode_step(q, K, V, lens, N=5, refresh_period=3, step=t, tau_in=tau)
+        assert bool(r.refreshed.all()) == (t % 3 == 0)
+        assert not r.fallback.any()
+        sels.append([s.tolist() for s in r.sel[0]])
+        tau = r.tau
+    assert all(s == sels[0] for s in sels)
+
+
+def test_appended_keys_compare_against_stale_threshold():
+    q, K, V, lens = rand_case(13, B=1, h_q=2, h_k=1, h_v=1, d=8, L_max=40, lens=(30,))
+    r0 = orc.saga_decode_step(q, K, V, lens, N=4, refresh_period=8, step=0)
+    K2 = K.copy()
+    # Position 30 gets a key far above head 0's threshold, position 31 far below.
+    K2[0, 0, 30] = 20.0 * q[0, 0] / np.linalg.norm(q[0, 0])
+    K2[0, 0, 31] = -20.0 * q[0, 0] / np.linalg.norm(q[0, 0])
+    r1 = orc.saga_decode_step(q, K2, V, np.array([32]), N=4, refresh_period=8, step=1, tau_in=r0.tau)
+    assert r1.tau[0, 0] == r0.tau[0, 0]
+    assert r1.sel[0][0].tolist() == sorted(r0.sel[0][0].tolist() + [30])
+    assert 31 not in r1.sel[0][1].tolist() or r1.logits[0][1][31] >= r0.tau[0, 1]
+    # The next refresh (t = 8) recomputes the 4-th largest of the grown row: 5 -> 4 kept.
+    r8 = orc.saga_decode_step(q, K2, V, np.array([32]), N=4, refresh_period=8, step=8, tau_in=r1.tau)
+    assert r8.sel[0][0].size == 4 and 30 in r8.sel[0][0].tolist()
+
+
+def test_empty_stale_selection_forces_refresh():
+    q, K, V, lens = rand_case(14)
+    tau_in = np.full((2, 8), np.inf)
+    tau_in[1, 3] = -np.inf            # this row keeps everything under its stale threshold
+    r = orc.saga_decode_step(q, K, V, lens, N=3, refresh_period=5, step=2, tau_in=tau_in)
+    exact = orc.saga_decode_step(q, K, V, lens, N=3, refresh_period=1, step=0)
+    for b in range(2):
+        for j in range(8):
+            if (b, j) == (1, 3):
+                assert not r.fallback[b, j] and r.sel[b][j].size == lens[b]
+                continue
+            assert r.fallback[b, j]
+            assert r.sel[b][j].tolist() == exact.sel[b][j].tolist()
+            np.testing.assert_allclose(r.O[b, j], exact.O[b, j], rtol=0, atol=0)
+
+
+# --- the explainer's worked example pins the byte model --------------------------
+
+def test_explainer_vector_read_table():
+    rows, ratios = {}, {}
+    with open(os.path.join(GOLDEN, "explainer_vector_reads.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0] == "ratio":
+                ratios[parts[1]] = float(parts[2])
+            else:
+                rows[parts[0]] = parts[1:]
+    for name, (h_q, h_k, h_v, L, N, kr, vr, tot) in rows.items():
+        got = bytemodel.vector_reads(int(h_q), int(h_k), int(h_v), int(L), None if N == "-" else int(N))
+        assert got == (int(kr), int(vr), int(tot)), name
+    d = dict((k, int(v[-1])) for k, v in rows.items())
+    kg = int(rows["gqa_topn"][5])
+    assert round(kg / d["gqa_topn"], 2) == ratios["keys_share_gqa_topn"]
+    assert round(d["gqa_topn"] / d["saga_topn"], 1) == ratios["gqa_topn_over_saga"]
+    assert round(d["dense_gqa"] / d["saga_topn"], 1) == ratios["dense_over_saga"]
+    # bytes: keys stream h_k * l_kv * d * s; dense streams keys and values
+    assert bytemodel.key_bytes(4, 64, [131072], 2) == 524288 * 64 * 2
+    assert bytemodel.dense_bytes(8, 64, [131072], 2) == 2097152 * 64 * 2
