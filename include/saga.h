@@ -1,0 +1,137 @@
+/*
+ * saga.h - C ABI of the SAGA + Atop-N single-token decode-attention library (gfx950).
+ *
+ * The operation (paper "More Value per Key: Asymmetric Sparse Attention for Faster
+ * LLM Decoding", summary page picx.dev DRD92V):
+ *   - eq. (2): A[b,j,i] = (q[b,j,:] . K[b,g(j),i,:]) * scale over the l_kv[b] cached keys,
+ *     with only h_k key heads (section "SAGA Architecture");
+ *   - section "Methodology > Atop-N Attention": entries are kept by comparing A with a
+ *     per-row threshold, the N-th largest logit of the row; the exact threshold is
+ *     recomputed once every `refresh_period` decode steps (the pages' n) and reused;
+ *   - eq. (7): O[b,j,:] = softmax(A[b,j,S]) V[b,v(j),S,:] over the kept set S, with
+ *     h_v >= h_k value heads.
+ *   g(j) = floor(j*h_k/h_q), v(j) = floor(j*h_v/h_q) (contiguous head groups).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns all memory;
+ *     the library allocates nothing, keeps no pointer after returning, never
+ *     synchronises the stream, never prints and never aborts.
+ *   - Layouts (row-major, contiguous): q [B,h_q,d]; K [B,h_k,l_max,d]; V [B,h_v,l_max,d];
+ *     out [B,h_q,d]; l_kv [B] int32; tau [B,h_q] float32. Rows >= l_kv[b] are never read.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     Results are valid once the stream reaches the call.
+ *   - Arguments are checked on the host before anything is launched; on any error
+ *     nothing is enqueued and no output is written.
+ *   - Device-side values cannot be checked: l_kv[b] must lie in [0, max_l_kv] and the
+ *     inputs must be finite. l_kv[b] == 0 yields a zero output row, sel_count 0 and an
+ *     unchanged threshold.
+ *   - Workspace: `saga_workspace_bytes` bytes of device memory, zero-filled before
+ *     its first use (saga_workspace_init does that). Every call leaves the counters it
+ *     uses back at zero, so a workspace is reused across calls without clearing.
+ *     Calls sharing one workspace must be ordered on one stream; concurrent calls
+ *     need separate workspaces.
+ */
+#ifndef SAGA_H
+#define SAGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum saga_status {
+  SAGA_OK = 0,
+  SAGA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SAGA_ERR_SHAPE = 2,       /* inconsistent sizes: heads not divisible, N < 1, period < 1, ... */
+  SAGA_ERR_UNSUPPORTED = 3, /* valid but not built: d not in {64,128}, unknown dtype, too long */
+  SAGA_ERR_WORKSPACE = 4,   /* workspace smaller than saga_workspace_bytes() */
+  SAGA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} saga_status;
+
+typedef enum saga_dtype { SAGA_F32 = 0, SAGA_BF16 = 1 } saga_dtype;
+
+/* Head counts and sizes, named as on the pages (section "Attention Mechanism
+ * Formalization": h heads of dimension d; section "SAGA Architecture": h_k, h_v). */
+typedef struct saga_shape {
+  int32_t batch;      /* B >= 1 sequences, one decode token each */
+  int32_t h_q;        /* query heads; multiple of h_k and of h_v */
+  int32_t h_k;        /* key heads */
+  int32_t h_v;        /* value heads */
+  int32_t d;          /* head dimension of q, K and V: 64 or 128 */
+  int32_t l_max;      /* cache capacity: row stride (in tokens) of K and V */
+  int32_t dtype;      /* saga_dtype of q, K and V */
+  int32_t out_dtype;  /* saga_dtype of out (bf16 output is rounded to nearest even) */
+  float scale;        /* logit scale; 0 selects 1/sqrt(d) as in eq. (2) */
+} saga_shape;
+
+/* Status name, e.g. "SAGA_ERR_SHAPE"; a static string, never NULL. */
+const char* saga_status_str(int32_t status);
+
+/* Bytes of workspace the calls below need for `s`, top-N size N and contexts up to
+ * max_l_kv tokens. 0 if the shape is invalid. Pure host arithmetic. */
+size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv);
+
+/* Enqueue a zero fill of `bytes` bytes of `workspace` (first-use initialisation). */
+saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* One SAGA + Atop-N decode step (eq. (2), the Atop-N threshold rule, eq. (7)).
+ *   max_l_kv (host): upper bound of l_kv[], sizes the launch grid.
+ *   N: top-N size (>= 1). refresh_period (>= 1) and step (host) choose the exact
+ *     threshold refresh: when step % refresh_period == 0, tau[b,j] is recomputed as the
+ *     N-th largest fp32 logit of its row (-inf when N >= l_kv[b]) before selecting;
+ *     otherwise the tau passed in is used as is.
+ *   tau [B,h_q] in/out: the per-(sequence, query head) threshold state.
+ *   Kept set S[b,j] = { i < l_kv[b] : A[b,j,i] >= tau[b,j] } (ties kept). If a stale
+ *     threshold keeps nothing, that row is refreshed exactly at this step.
+ *   out [B,h_q,d] (out_dtype): eq. (7) over S.
+ *   sel_count [B,h_q] (optional, may be NULL): |S[b,j]|.
+ *   sel_idx [B,h_q,sel_cap] (optional): the first min(|S|, sel_cap) kept indices,
+ *     in no particular order; entries past that are left untouched.
+ *   flags [B,h_q] (optional): bit 0 = the threshold was refreshed at this step,
+ *     bit 1 = the refresh was forced by an empty stale selection. */
+saga_status saga_decode_attn(const saga_shape* s, const void* q, const void* k, const void* v,
+                             const int32_t* l_kv, int32_t max_l_kv, int32_t N,
+                             int32_t refresh_period, int64_t step, float* tau, void* out,
+                             int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap,
+                             int32_t* flags, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* The exact threshold alone (section "Methodology > Atop-N Attention", refresh step):
+ * tau[b,j] = N-th largest fp32 logit of row (b,j), counting repeats; -inf when
+ * N >= l_kv[b]; unchanged when l_kv[b] == 0. */
+saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const void* k,
+                                   const int32_t* l_kv, int32_t max_l_kv, int32_t N,
+                                   float* tau, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Dense grouped-query attention, eq. (2)-(4) over every cached key and value:
+ * the baseline the pages compare against (Figure 2). Requires h_k == h_v. */
+saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* k,
+                                const void* v, const int32_t* l_kv, int32_t max_l_kv,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* The two stages of a non-refresh decode step, callable separately on one stream
+ * with one workspace (saga_decode_attn with step % refresh_period != 0 is exactly
+ * saga_qk_select followed by saga_sparse_gather).
+ * saga_qk_select: scores every cached key of the h_k key heads (eq. (2)) and keeps,
+ *   per query head, the entries >= tau into the workspace (Atop-N comparison step).
+ * saga_sparse_gather: softmax over the kept entries and the gather of their value
+ *   rows (eq. (7)); outputs as in saga_decode_attn (flags bit 0 is never set here).
+ *   q, k, N and tau are needed for the forced refresh of a row that kept nothing. */
+saga_status saga_qk_select(const saga_shape* s, const void* q, const void* k,
+                           const int32_t* l_kv, int32_t max_l_kv, const float* tau,
+                           void* workspace, size_t workspace_bytes, void* stream);
+saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k,
+                               const void* v, const int32_t* l_kv, int32_t max_l_kv,
+                               int32_t N, float* tau, void* out, int32_t* sel_count,
+                               int32_t* sel_idx, int32_t sel_cap, int32_t* flags,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGA_H */

@@ -1,0 +1,237 @@
+"""Thin Python binding of libsaga.so (ctypes): argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels. PyTorch provides
+device memory (tensor storage) and the stream (torch's current stream). If the
+library is not built, every call raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+F32, BF16 = 0, 1
+EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "saga_decode_attn",
+           "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather")
+FLAG_REFRESHED, FLAG_FORCED = 1, 2
+
+
+class SagaShape(ctypes.Structure):
+    """Mirror of `saga_shape` in include/saga.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_k", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d", ctypes.c_int32), ("l_max", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class SagaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)}")
+        self.status = status
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "saga_status_str": (ctypes.c_char_p, [_I32]),
+    "saga_workspace_bytes": (_SZ, [_P, _I32, _I32]),
+    "saga_workspace_init": (_I32, [_P, _SZ, _P]),
+    "saga_decode_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_refresh_threshold": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
+    "saga_dense_gqa_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_qk_select": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_sparse_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+}
+
+
+def lib(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsaga.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m sparse_decode_attention_saga_amd.build`")
+        cdll = ctypes.CDLL(p)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(cdll, name)
+            fn.restype, fn.argtypes = res, args
+        _LIB = cdll
+    return _LIB
+
+
+def status_str(status: int) -> str:
+    return lib().saga_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise SagaError(status, where)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {dt}: use float32 or bfloat16")
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
+               out_dtype: Optional[torch.dtype] = None, scale: float = 0.0) -> SagaShape:
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, h_q, d] and k [B, h_k, l_max, d]")
+    B, h_q, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k does not match q")
+    h_v = k.shape[1]
+    if v is not None:
+        if v.dim() != 4 or v.shape[0] != B or v.shape[2] != k.shape[2] or v.shape[3] != d:
+            raise ValueError("v must be [B, h_v, l_max, d] matching k")
+        if v.dtype != q.dtype:
+            raise ValueError("q, k and v must share one dtype")
+        h_v = v.shape[1]
+    if k.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    return SagaShape(B, h_q, k.shape[1], h_v, d, k.shape[2], dtype_code(q.dtype),
+                     dtype_code(out_dtype or q.dtype), float(scale))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def workspace_bytes(shape: SagaShape, N: int, max_l_kv: int) -> int:
+    n = lib().saga_workspace_bytes(ctypes.byref(shape), int(N), int(max_l_kv))
+    if n == 0:
+        raise ValueError("invalid shape for the workspace")
+    return int(n)
+
+
+class Workspace:
+    """Device workspace for one shape: zero-filled once by the library's fill kernel."""
+
+    def __init__(self, shape: SagaShape, N: int, max_l_kv: int, device, stream=None):
+        self.nbytes = workspace_bytes(shape, N, max_l_kv)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        _check(lib().saga_workspace_init(_ptr(self.buf), self.nbytes, _stream(self.buf.device, stream)),
+               "saga_workspace_init")
+
+    @classmethod
+    def for_inputs(cls, q, k, v=None, N: int = 1, max_l_kv: Optional[int] = None):
+        shape = make_shape(q, k, v)
+        return cls(shape, N, k.shape[2] if max_l_kv is None else max_l_kv, q.device)
+
+
+def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale):
+    for name, t in (("q", q), ("k", k)):
+        _dev(t, name)
+    if v is not None:
+        _dev(v, "v")
+    _dev(l_kv, "l_kv", torch.int32)
+    shape = make_shape(q, k, v, out_dtype, scale)
+    if l_kv.numel() != shape.batch:
+        raise ValueError("l_kv must have one entry per sequence")
+    if tau is not None:
+        _dev(tau, "tau", torch.float32)
+        if tau.numel() != shape.batch * shape.h_q:
+            raise ValueError("tau must be [B, h_q]")
+    if max_l_kv is None:
+        max_l_kv = shape.l_max
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _dev(out, "out")
+        if tuple(out.shape) != tuple(q.shape) or dtype_code(out.dtype) != shape.out_dtype:
+            raise ValueError("out must be [B, h_q, d] in the output dtype")
+    return shape, int(max_l_kv), out
+
+
+def _ws(ws: Optional[Workspace], shape, N, max_l_kv, device):
+    if ws is None:
+        ws = Workspace(shape, N, max_l_kv, device)
+    return ws
+
+
+def decode_attn(q, k, v, l_kv, tau, *, N: int, refresh_period: int, step: int,
+                max_l_kv: Optional[int] = None, out=None, out_dtype=None, sel_count=None,
+                sel_idx=None, flags=None, workspace: Optional[Workspace] = None,
+                scale: float = 0.0, stream=None):
+    """saga_decode_attn: one SAGA + Atop-N decode step. `tau` [B, h_q] float32 is
+    read and updated in place. Returns `out`."""
+    shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
+    for name, t in (("sel_count", sel_count), ("sel_idx", sel_idx), ("flags", flags)):
+        if t is not None:
+            _dev(t, name, torch.int32)
+    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    ws = _ws(workspace, shape, N, max_l_kv, q.device)
+    st = lib().saga_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
+                                int(refresh_period), int(step), _ptr(tau), _ptr(out), _ptr(sel_count),
+                                _ptr(sel_idx), cap, _ptr(flags), _ptr(ws.buf), ws.nbytes,
+                                _stream(q.device, stream))
+    _check(st, "saga_decode_attn")
+    return out
+
+
+def refresh_threshold(q, k, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
+                      workspace: Optional[Workspace] = None, scale: float = 0.0, stream=None):
+    """saga_refresh_threshold: writes the exact threshold into `tau` [B, h_q]."""
+    shape, max_l_kv, _ = _prep(q, k, None, l_kv, tau, q, None, max_l_kv, scale)
+    ws = _ws(workspace, shape, N, max_l_kv, q.device)
+    st = lib().saga_refresh_threshold(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(l_kv), max_l_kv, int(N),
+                                      _ptr(tau), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_refresh_threshold")
+    return tau
+
+
+def qk_select(q, k, l_kv, tau, *, max_l_kv: Optional[int] = None, workspace: Optional[Workspace] = None,
+              scale: float = 0.0, stream=None):
+    """saga_qk_select: the scoring and threshold-comparison stage (into the workspace)."""
+    shape, max_l_kv, _ = _prep(q, k, None, l_kv, tau, q, None, max_l_kv, scale)
+    ws = _ws(workspace, shape, 1, max_l_kv, q.device)
+    st = lib().saga_qk_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(l_kv), max_l_kv, _ptr(tau),
+                              _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_qk_select")
+
+
+def sparse_gather(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None, out=None, out_dtype=None,
+                  sel_count=None, sel_idx=None, flags=None, workspace: Optional[Workspace] = None,
+                  scale: float = 0.0, stream=None):
+    """saga_sparse_gather: softmax and value gather over what saga_qk_select kept."""
+    shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
+    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    ws = _ws(workspace, shape, N, max_l_kv, q.device)
+    st = lib().saga_sparse_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
+                                  _ptr(tau), _ptr(out), _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags),
+                                  _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_sparse_gather")
+    return out
+
+
+def dense_gqa_attn(q, k, v, l_kv, *, max_l_kv: Optional[int] = None, out=None, out_dtype=None,
+                   workspace: Optional[Workspace] = None, scale: float = 0.0, stream=None):
+    """saga_dense_gqa_attn: dense grouped-query attention over every cached key (h_k == h_v)."""
+    shape, max_l_kv, out = _prep(q, k, v, l_kv, None, out, out_dtype, max_l_kv, scale)
+    ws = _ws(workspace, shape, 1, max_l_kv, q.device)
+    st = lib().saga_dense_gqa_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv,
+                                   _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_dense_gqa_attn")
+    return out

@@ -1,0 +1,326 @@
+// Host side of the C ABI declared in include/saga.h: argument checks, workspace
+// layout and kernel launches. Nothing here allocates, synchronises or prints.
+#include "saga.h"
+
+#include <cmath>
+#include <cstddef>
+
+#include "saga_kernels.cuh"
+
+using namespace saga;
+
+namespace {
+
+constexpr int kMaxGatherSplits = 64;   // partial slots per row of the sparse gather
+constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
+
+#define SAGA_DISPATCH(DT, DIM, ...)                                   \
+  do {                                                                \
+    if ((DT) == SAGA_BF16 && (DIM) == 128) {                          \
+      using T = bf16_t;                                               \
+      constexpr int D = 128;                                          \
+      __VA_ARGS__                                                     \
+    } else if ((DT) == SAGA_BF16 && (DIM) == 64) {                    \
+      using T = bf16_t;                                               \
+      constexpr int D = 64;                                           \
+      __VA_ARGS__                                                     \
+    } else if ((DT) == SAGA_F32 && (DIM) == 128) {                    \
+      using T = float;                                                \
+      constexpr int D = 128;                                          \
+      __VA_ARGS__                                                     \
+    } else {                                                          \
+      using T = float;                                                \
+      constexpr int D = 64;                                           \
+      __VA_ARGS__                                                     \
+    }                                                                 \
+  } while (0)
+
+int chunk_keys(int dtype, int d) {
+  int ch = 0;
+  SAGA_DISPATCH(dtype, d, ch = StreamCfg<T, D>::kChunk;);
+  return ch;
+}
+
+saga_status check_shape(const saga_shape* s) {
+  if (!s) return SAGA_ERR_NULL;
+  if (s->batch < 1 || s->h_q < 1 || s->h_k < 1 || s->h_v < 1 || s->d < 1 || s->l_max < 1)
+    return SAGA_ERR_SHAPE;
+  if (s->h_q % s->h_k || s->h_q % s->h_v) return SAGA_ERR_SHAPE;
+  if (!(s->scale >= 0.f) || !std::isfinite(s->scale)) return SAGA_ERR_SHAPE;
+  if ((s->dtype != SAGA_F32 && s->dtype != SAGA_BF16) || (s->out_dtype != SAGA_F32 && s->out_dtype != SAGA_BF16))
+    return SAGA_ERR_UNSUPPORTED;
+  if (s->d != 64 && s->d != 128) return SAGA_ERR_UNSUPPORTED;
+  if (s->batch > 65535 || s->h_q > 65535 || s->l_max > kMaxContext) return SAGA_ERR_UNSUPPORTED;
+  return SAGA_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  int rows, ch, nch, S, P;
+  long long lpad;
+  size_t hist, cand_cnt, done, row_done, scores, surv_idx, surv_val, chunk_cnt, chunk_max, part, dpart, total;
+};
+
+Layout layout(const saga_shape* s, int max_l_kv) {
+  Layout w{};
+  w.rows = s->batch * s->h_q;
+  w.ch = chunk_keys(s->dtype, s->d);
+  w.nch = max_l_kv > 0 ? (max_l_kv + w.ch - 1) / w.ch : 1;
+  w.lpad = (long long)w.nch * w.ch;
+  int S = (w.nch + 7) / 8;
+  w.S = S < 1 ? 1 : (S > kMaxGatherSplits ? kMaxGatherSplits : S);
+  w.P = max_l_kv > 0 ? (max_l_kv + kSelSlice - 1) / kSelSlice : 1;
+  const size_t rows = (size_t)w.rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  // counters first: they must be zero before the first call
+  w.hist = take(rows * 256 * 4);
+  w.cand_cnt = take(rows * 4);
+  w.done = take(rows * 4);
+  w.row_done = take(rows * 4);
+  w.scores = take(rows * (size_t)w.lpad * 4);
+  w.surv_idx = take(rows * (size_t)w.lpad * 4);
+  w.surv_val = take(rows * (size_t)w.lpad * 4);
+  w.chunk_cnt = take(rows * (size_t)w.nch * 4);
+  w.chunk_max = take(rows * (size_t)w.nch * 4);
+  w.part = take(rows * (size_t)w.S * (s->d + 4) * 4);
+  w.dpart = take(rows * (size_t)w.nch * (s->d + 4) * 4);
+  w.total = off;
+  return w;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
+}
+
+StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const void* q, const void* k,
+                       const int32_t* l_kv, int32_t max_l_kv, const float* tau, int N) {
+  StreamArgs a{};
+  a.q = q;
+  a.k = k;
+  a.l_kv = l_kv;
+  a.tau = tau;
+  a.scores = at<float>(ws, w.scores);
+  a.surv_idx = at<int32_t>(ws, w.surv_idx);
+  a.surv_val = at<float>(ws, w.surv_val);
+  a.chunk_cnt = at<int32_t>(ws, w.chunk_cnt);
+  a.chunk_max = at<float>(ws, w.chunk_max);
+  a.hist = at<unsigned>(ws, w.hist);
+  a.cand_cnt = at<unsigned>(ws, w.cand_cnt);
+  a.done = at<unsigned>(ws, w.done);
+  a.h_q = s->h_q;
+  a.h_k = s->h_k;
+  a.g_k = s->h_q / s->h_k;
+  a.htiles = (a.g_k + 15) / 16;
+  a.l_max = s->l_max;
+  a.nch = w.nch;
+  a.N = N;
+  a.max_l_kv = max_l_kv;
+  a.lpad = w.lpad;
+  a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
+  return a;
+}
+
+saga_status check_common(const saga_shape* s, int32_t max_l_kv, void* ws, size_t ws_bytes, int32_t N) {
+  const saga_status st = check_shape(s);
+  if (st != SAGA_OK) return st;
+  if (max_l_kv < 0 || max_l_kv > s->l_max) return SAGA_ERR_SHAPE;
+  if (N < 1) return SAGA_ERR_SHAPE;
+  if (!ws) return SAGA_ERR_NULL;
+  if (ws_bytes < layout(s, max_l_kv).total) return SAGA_ERR_WORKSPACE;
+  return SAGA_OK;
+}
+
+saga_status launched() { return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
+
+dim3 stream_grid(const saga_shape* s, const Layout& w) {
+  const int g_k = s->h_q / s->h_k;
+  return dim3(w.nch, s->h_k * ((g_k + 15) / 16), s->batch);
+}
+
+void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, float* tau, hipStream_t st) {
+  SAGA_DISPATCH(s->dtype, s->d, {
+    hipLaunchKernelGGL((k_scores_hist<T, D>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+  });
+  hipLaunchKernelGGL(k_threshold_select, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a, tau);
+}
+
+void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, hipStream_t st) {
+  SAGA_DISPATCH(s->dtype, s->d, {
+    if (from_scores)
+      hipLaunchKernelGGL((k_qk_select<T, D, true>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_qk_select<T, D, false>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+  });
+}
+
+void launch_gather(const saga_shape* s, const Layout& w, const GatherArgs& g, hipStream_t st) {
+  SAGA_DISPATCH(s->dtype, s->d, {
+    hipLaunchKernelGGL((k_sparse_gather<T, D>), dim3(w.S, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+  });
+}
+
+GatherArgs gather_args(const saga_shape* s, const Layout& w, void* ws, const StreamArgs& sa, const void* v,
+                       float* tau, void* out, int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap,
+                       int32_t* flags, bool refreshed) {
+  GatherArgs g{};
+  g.s = sa;
+  g.v = v;
+  g.tau = tau;
+  g.out = out;
+  g.sel_count = sel_count;
+  g.sel_idx = sel_idx;
+  g.flags = flags;
+  g.part = at<float>(ws, w.part);
+  g.row_done = at<unsigned>(ws, w.row_done);
+  g.h_v = s->h_v;
+  g.sel_cap = sel_idx ? sel_cap : 0;
+  g.out_bf16 = s->out_dtype == SAGA_BF16;
+  g.refreshed = refreshed ? 1 : 0;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* saga_status_str(int32_t status) {
+  switch (status) {
+    case SAGA_OK: return "SAGA_OK";
+    case SAGA_ERR_NULL: return "SAGA_ERR_NULL";
+    case SAGA_ERR_SHAPE: return "SAGA_ERR_SHAPE";
+    case SAGA_ERR_UNSUPPORTED: return "SAGA_ERR_UNSUPPORTED";
+    case SAGA_ERR_WORKSPACE: return "SAGA_ERR_WORKSPACE";
+    case SAGA_ERR_HIP: return "SAGA_ERR_HIP";
+    default: return "SAGA_ERR_UNKNOWN";
+  }
+}
+
+size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv) {
+  if (check_shape(s) != SAGA_OK || N < 1 || max_l_kv < 0 || max_l_kv > s->l_max) return 0;
+  return layout(s, max_l_kv).total;
+}
+
+saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return SAGA_ERR_NULL;
+  if (bytes == 0) return SAGA_OK;
+  (void)hipGetLastError();
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + kBlock - 1) / kBlock;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(kBlock), 0, (hipStream_t)stream,
+                     (uint8_t*)workspace, bytes);
+  return launched();
+}
+
+saga_status saga_decode_attn(const saga_shape* s, const void* q, const void* k, const void* v,
+                             const int32_t* l_kv, int32_t max_l_kv, int32_t N, int32_t refresh_period,
+                             int64_t step, float* tau, void* out, int32_t* sel_count, int32_t* sel_idx,
+                             int32_t sel_cap, int32_t* flags, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !tau || !out) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
+  if (st != SAGA_OK) return st;
+  if (refresh_period < 1 || step < 0 || (sel_idx && sel_cap < 1)) return SAGA_ERR_SHAPE;
+  const Layout w = layout(s, max_l_kv);
+  const hipStream_t hs = (hipStream_t)stream;
+  const bool refresh = (step % refresh_period) == 0;
+  (void)hipGetLastError();
+  const StreamArgs a = stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N);
+  if (max_l_kv > 0) {
+    if (refresh) launch_refresh(s, w, a, tau, hs);
+    launch_select(s, w, a, refresh, hs);
+  }
+  launch_gather(s, w, gather_args(s, w, workspace, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
+  return launched();
+}
+
+saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const void* k, const int32_t* l_kv,
+                                   int32_t max_l_kv, int32_t N, float* tau, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!s || !q || !k || !l_kv || !tau) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
+  if (st != SAGA_OK) return st;
+  const Layout w = layout(s, max_l_kv);
+  (void)hipGetLastError();
+  if (max_l_kv > 0) launch_refresh(s, w, stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N), tau, (hipStream_t)stream);
+  return launched();
+}
+
+saga_status saga_qk_select(const saga_shape* s, const void* q, const void* k, const int32_t* l_kv,
+                           int32_t max_l_kv, const float* tau, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!s || !q || !k || !l_kv || !tau) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
+  if (st != SAGA_OK) return st;
+  const Layout w = layout(s, max_l_kv);
+  (void)hipGetLastError();
+  if (max_l_kv > 0)
+    launch_select(s, w, stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, 1), false, (hipStream_t)stream);
+  return launched();
+}
+
+saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k, const void* v,
+                               const int32_t* l_kv, int32_t max_l_kv, int32_t N, float* tau, void* out,
+                               int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap, int32_t* flags,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !tau || !out) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
+  if (st != SAGA_OK) return st;
+  if (sel_idx && sel_cap < 1) return SAGA_ERR_SHAPE;
+  const Layout w = layout(s, max_l_kv);
+  (void)hipGetLastError();
+  const StreamArgs a = stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N);
+  launch_gather(s, w, gather_args(s, w, workspace, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, false),
+                (hipStream_t)stream);
+  return launched();
+}
+
+saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* k, const void* v,
+                                const int32_t* l_kv, int32_t max_l_kv, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !out) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
+  if (st != SAGA_OK) return st;
+  if (s->h_k != s->h_v) return SAGA_ERR_SHAPE;
+  const int g = s->h_q / s->h_k;
+  if (g > 16) return SAGA_ERR_UNSUPPORTED;
+  const Layout w = layout(s, max_l_kv);
+  const hipStream_t hs = (hipStream_t)stream;
+  DenseArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.l_kv = l_kv;
+  a.part = at<float>(workspace, w.dpart);
+  a.out = out;
+  a.h_q = s->h_q;
+  a.h_kv = s->h_k;
+  a.g = g;
+  a.l_max = s->l_max;
+  a.nchd = w.nch;
+  a.max_l_kv = max_l_kv;
+  a.out_bf16 = s->out_dtype == SAGA_BF16;
+  a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
+  (void)hipGetLastError();
+  SAGA_DISPATCH(s->dtype, s->d, {
+    if (max_l_kv > 0) {
+      const dim3 grid(w.nch, s->h_k, s->batch);
+      if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, D, 4>), grid, dim3(kBlock), 0, hs, a);
+      else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, D, 8>), grid, dim3(kBlock), 0, hs, a);
+      else hipLaunchKernelGGL((k_dense_partial<T, D, 16>), grid, dim3(kBlock), 0, hs, a);
+    }
+    hipLaunchKernelGGL((k_dense_combine<D>), dim3(D / 32, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
+                       (int)StreamCfg<T, D>::kChunk);
+  });
+  return launched();
+}
+
+}  // extern "C"

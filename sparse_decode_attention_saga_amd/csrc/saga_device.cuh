@@ -1,0 +1,298 @@
+// Device helpers for the SAGA + Atop-N decode kernels (gfx950, wave64).
+//
+// Score tiles use the CDNA matrix cores: a 16-key x 16-query-head tile of logits
+// A = K q^T (eq. (2) of the paper's "Attention Mechanism Formalization") is one
+// chain of MFMA instructions. The key tile is the A operand (rows = keys) and the
+// query heads are the B operand (columns = heads). Each lane supplies the same
+// slice of the head dimension to both operands, so the contraction is a plain
+// dot product whatever order the hardware sums the slices in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saga {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes seen as raw words, eight bf16 or four fp32.
+union V16 {
+  uint4 u;
+  bf16x8 h;
+  float f[4];
+};
+
+typedef uint16_t bf16_t;  // bf16 values are carried as their bit patterns
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Elements of type T in 16 bytes, as fp32. bf16: 8 values; fp32: 4 values.
+template <typename T> struct Unpack;
+template <> struct Unpack<bf16_t> {
+  static constexpr int kN = 8;
+  __device__ __forceinline__ static void run(const uint4& u, float (&x)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+};
+template <> struct Unpack<float> {
+  static constexpr int kN = 4;
+  __device__ __forceinline__ static void run(const uint4& u, float (&x)[4]) {
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z);
+    x[3] = __uint_as_float(u.w);
+  }
+};
+
+// Order-preserving map fp32 -> uint32 (larger float <=> larger key); -0 maps like +0.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_to_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ----------------------------------------------------------------------------
+// QK score tiles. One wave computes the logits of 16 consecutive keys against up
+// to 16 query heads. After mma(): lane l holds A[key = 4*(l>>4) + r][head = l&15]
+// in element r (the 16x16 MFMA accumulator layout).
+template <typename T, int D> struct QK;
+
+template <int D> struct QK<bf16_t, D> {
+  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+  static constexpr int kLoads = D / 32;  // 16-byte loads per lane per 16-key tile
+  bf16x8 qf[kLoads];
+
+  // q of local heads 0..nh-1 starts at `qh` (rows of D values); heads >= nh read as 0.
+  __device__ __forceinline__ void load_q(const bf16_t* qh, int nh, int lane) {
+    const int hh = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < kLoads; ++s) {
+      V16 x;
+      x.u = (hh < nh) ? ld16(qh + (size_t)hh * D + 32 * s + 8 * kq) : make_uint4(0, 0, 0, 0);
+      qf[s] = x.h;
+    }
+  }
+  // This lane's slices of key row `krow` (the row of key 16*tile + (lane & 15)).
+  __device__ __forceinline__ static void load_k(uint4 (&kb)[kLoads], const bf16_t* krow, int lane) {
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < kLoads; ++s) kb[s] = ld16(krow + 32 * s + 8 * kq);
+  }
+  __device__ __forceinline__ floatx4 mma(const uint4 (&kb)[kLoads]) const {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kLoads; ++s) {
+      V16 x;
+      x.u = kb[s];
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.h, qf[s], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+template <int D> struct QK<float, D> {
+  static_assert(D % 16 == 0, "head dim must be a multiple of 16");
+  static constexpr int kLoads = D / 16;
+  float4 qf[kLoads];
+
+  __device__ __forceinline__ void load_q(const float* qh, int nh, int lane) {
+    const int hh = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      V16 x;
+      x.u = (hh < nh) ? ld16(qh + (size_t)hh * D + 16 * u + 4 * kq) : make_uint4(0, 0, 0, 0);
+      qf[u] = make_float4(x.f[0], x.f[1], x.f[2], x.f[3]);
+    }
+  }
+  __device__ __forceinline__ static void load_k(uint4 (&kb)[kLoads], const float* krow, int lane) {
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) kb[u] = ld16(krow + 16 * u + 4 * kq);
+  }
+  __device__ __forceinline__ floatx4 mma(const uint4 (&kb)[kLoads]) const {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      V16 x;
+      x.u = kb[u];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.f[0], qf[u].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.f[1], qf[u].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.f[2], qf[u].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.f[3], qf[u].w, acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+// Scaled logits of TPW consecutive 16-key tiles starting at key `wbase` of the key
+// head whose rows start at `kh`. Rows past the valid length L are clamped to L-1 for
+// the load (always in bounds); callers mask them. Requires L >= 1.
+template <typename T, int D, int TPW>
+__device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& qk, const T* kh,
+                                            int wbase, int L, int lane, float scale) {
+  uint4 kb[TPW][QK<T, D>::kLoads];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int key = min(wbase + 16 * t + (lane & 15), L - 1);
+    QK<T, D>::load_k(kb[t], kh + (size_t)key * D, lane);
+  }
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const floatx4 a = qk.mma(kb[t]);
+    sc[t] = a * scale;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Block-wide helpers for 256-thread blocks. Every thread of the block must call them.
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the block in thread order; `total` gets the block sum.
+// `tmp` is __shared__ int[kWaves].
+__device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int inc = wave_incl_scan(x, lane);
+  if (lane == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int t = tmp[i];
+    off += (i < w) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// `tmp` is __shared__ float[kWaves].
+__device__ __forceinline__ float block_max(float x, float* tmp) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_max(x);
+  if (lane == 0) tmp[w] = x;
+  __syncthreads();
+  float r = tmp[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, tmp[i]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_sum(float x, float* tmp) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_sum(x);
+  if (lane == 0) tmp[w] = x;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r += tmp[i];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ int block_sum_i(int x, int* tmp) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_sum_i(x);
+  if (lane == 0) tmp[w] = x;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r += tmp[i];
+  __syncthreads();
+  return r;
+}
+
+// ----------------------------------------------------------------------------
+// MSB-first radix selection of the k-th largest (k >= 1) order key, 8 bits per pass.
+
+// Given a 256-bin histogram `hist` (shared), find the digit whose bin holds the k-th
+// largest element counting from the top bin; res[0] = digit, res[1] = rank of the
+// element inside that bin. If the bins hold fewer than k elements res is left at
+// (0, 1). `itmp` is __shared__ int[kWaves].
+__device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsigned k, int* itmp,
+                                                     unsigned* res) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    res[0] = 0u;
+    res[1] = 1u;
+  }
+  const int c = (int)hist[255 - t];
+  int total;
+  const int above = block_excl_scan(c, itmp, total);  // elements in bins above 255-t
+  if ((unsigned)above < k && k <= (unsigned)(above + c)) {
+    res[0] = (unsigned)(255 - t);
+    res[1] = k - (unsigned)above;
+  }
+  __syncthreads();
+}
+
+// The order key of the k-th largest of vals[0..n) among the values whose key
+// matches `prefix` on the bits of `mask`, resolving bits shift_start+7..0.
+__device__ __forceinline__ uint32_t radix_select_block(const float* vals, long long n, uint32_t prefix,
+                                                       uint32_t mask, int shift_start, unsigned k,
+                                                       unsigned* hist, int* itmp, unsigned* res) {
+  const int tid = threadIdx.x;
+  for (int shift = shift_start; shift >= 0; shift -= 8) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (long long i = tid; i < n; i += kBlock) {
+      const uint32_t u = order_key(vals[i]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    digit_of_kth_largest(hist, k, itmp, res);
+    prefix |= res[0] << shift;
+    mask |= 255u << shift;
+    k = res[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+}  // namespace saga

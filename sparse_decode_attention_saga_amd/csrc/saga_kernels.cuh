@@ -1,0 +1,767 @@
+// Kernels of the SAGA + Atop-N decode step and of the dense GQA baseline (gfx950).
+//
+// Steady step (threshold reused):  k_qk_select  ->  k_sparse_gather
+// Refresh step (exact threshold):  k_scores_hist -> k_threshold_select
+//                                   -> k_qk_select<from stored scores> -> k_sparse_gather
+// Dense GQA baseline:              k_dense_partial -> k_dense_combine
+//
+// Paper: "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding"
+// (summary page picx.dev DRD92V): eq. (2) logits, section "Methodology > Atop-N
+// Attention" (threshold = N-th largest logit, elementwise comparison, exact
+// threshold refreshed every n steps), eq. (7) sparse softmax-PV, section "SAGA
+// Architecture" (h_k key heads, h_v value heads).
+#pragma once
+
+#include "saga_device.cuh"
+
+namespace saga {
+
+// Keys per block of the key-streaming kernels: 4 waves x TPW tiles x 16 keys.
+template <typename T, int D> struct StreamCfg {
+  // ~16 KB of K per wave in flight: 4 x 16-byte loads per lane per tile at 256 B rows.
+  static constexpr int kTPW = (D * (int)sizeof(T) >= 512) ? 2 : (D * (int)sizeof(T) == 256 ? 4 : 8);
+  static constexpr int kChunk = 16 * kTPW * kWaves;
+};
+
+// ----------------------------------------------------------------------------
+// Shared argument blocks (passed by value).
+
+struct StreamArgs {
+  const void* q;           // [B, h_q, D]
+  const void* k;           // [B, h_k, l_max, D]
+  const int32_t* l_kv;     // [B]
+  const float* tau;        // [B*h_q] threshold (select kernels)
+  float* scores;           // [B*h_q, lpad] fp32 logits (refresh steps and forced refresh)
+  int32_t* surv_idx;       // [B*h_q, lpad] kept indices, one CH-segment per chunk
+  float* surv_val;         // [B*h_q, lpad] kept logits; also the threshold candidates
+  int32_t* chunk_cnt;      // [B*h_q, nch] kept entries per chunk
+  float* chunk_max;        // [B*h_q, nch] largest kept logit per chunk
+  unsigned* hist;          // [B*h_q, 256] top-digit histogram (zero between calls)
+  unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
+  unsigned* done;          // [B*h_q] block counter of the threshold select (zero between calls)
+  int h_q, h_k, g_k, htiles, l_max, nch, N;
+  int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
+  long long lpad;
+  float scale;
+};
+
+// ----------------------------------------------------------------------------
+// Logits of one chunk of keys for the (up to) 16 query heads of one head tile, then
+// the Atop-N comparison against each head's threshold. Kept (index, logit) pairs go
+// to the chunk's segment of the row's survivor list; the chunk's count and largest
+// kept logit are recorded. FROM_SCORES reads the logits stored by k_scores_hist
+// instead of recomputing them from K (refresh steps: the same fp32 values the
+// threshold was selected from).
+// grid = (nch, h_k * htiles, B), block = 256.
+template <typename T, int D, bool FROM_SCORES>
+__global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
+  constexpr int TPW = StreamCfg<T, D>::kTPW;
+  constexpr int CH = StreamCfg<T, D>::kChunk;
+  const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int base = c * CH;
+  if (base >= L) return;
+  const int g = gy / a.htiles, ht = gy - g * a.htiles;
+  const int j0 = g * a.g_k + ht * 16;
+  const int nh = min(16, a.g_k - ht * 16);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int hh = lane & 15, kq = lane >> 4;
+  const int row0 = b * a.h_q + j0;
+
+  __shared__ int s_cnt[16];
+  __shared__ unsigned s_max[16];
+  if (tid < 16) {
+    s_cnt[tid] = 0;
+    s_max[tid] = 0u;
+  }
+  const bool live = hh < nh;
+  const float tau_l = live ? a.tau[row0 + hh] : 0.f;
+  const int wbase = base + wv * 16 * TPW;
+
+  floatx4 sc[TPW];
+  if constexpr (FROM_SCORES) {
+    const float* srow = a.scores + (long long)(row0 + (live ? hh : 0)) * a.lpad;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) sc[t] = *reinterpret_cast<const floatx4*>(srow + wbase + 16 * t + 4 * kq);
+  } else {
+    QK<T, D> qk;
+    qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
+    const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_k + g) * a.l_max * D;
+    score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+  }
+  __syncthreads();
+
+  const long long seg = (long long)(row0 + hh) * a.lpad + base;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = wbase + 16 * t + 4 * kq + r;
+      const float s = sc[t][r];
+      if (live && key < L && s >= tau_l) {
+        const int slot = atomicAdd(&s_cnt[hh], 1);
+        a.surv_idx[seg + slot] = key;
+        a.surv_val[seg + slot] = s;
+        atomicMax(&s_max[hh], order_key(s));
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < nh) {
+    const long long o = (long long)(row0 + tid) * a.nch + c;
+    a.chunk_cnt[o] = s_cnt[tid];
+    a.chunk_max[o] = order_key_to_f32(s_max[tid]);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Refresh, pass 1: logits of every cached key stored as fp32, plus a histogram of
+// the top 8 bits of their order keys per query head (accumulated into a.hist).
+// grid = (nch, h_k * htiles, B), block = 256.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
+  constexpr int TPW = StreamCfg<T, D>::kTPW;
+  constexpr int CH = StreamCfg<T, D>::kChunk;
+  const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int base = c * CH;
+  if (base >= L) return;
+  const int g = gy / a.htiles, ht = gy - g * a.htiles;
+  const int j0 = g * a.g_k + ht * 16;
+  const int nh = min(16, a.g_k - ht * 16);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int hh = lane & 15, kq = lane >> 4;
+  const int row0 = b * a.h_q + j0;
+
+  __shared__ unsigned s_hist[16 * 256];
+  for (int e = tid; e < 16 * 256; e += kBlock) s_hist[e] = 0u;
+
+  QK<T, D> qk;
+  qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
+  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_k + g) * a.l_max * D;
+  const int wbase = base + wv * 16 * TPW;
+  floatx4 sc[TPW];
+  score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+  __syncthreads();
+
+  const bool live = hh < nh;
+  if (live) {
+    float* srow = a.scores + (long long)(row0 + hh) * a.lpad;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      floatx4 v = sc[t];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = wbase + 16 * t + 4 * kq + r;
+        if (key < L) atomicAdd(&s_hist[hh * 256 + (order_key(v[r]) >> 24)], 1u);
+        else v[r] = -INFINITY;
+      }
+      *reinterpret_cast<floatx4*>(srow + wbase + 16 * t + 4 * kq) = v;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nh * 256; e += kBlock) {
+    const unsigned h = s_hist[e];
+    if (h) atomicAdd(&a.hist[(long long)(row0 + e / 256) * 256 + (e & 255)], h);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Refresh, pass 2: the exact threshold tau = N-th largest stored logit of each row
+// (counting repeats; -inf when N >= l_kv). Each block copies the logits of its slice
+// that fall in the top-digit bin holding the N-th largest into the row's candidate
+// list; the last block of the row resolves the remaining 24 bits on the candidates
+// and writes tau. It also returns the row's counters and histogram to zero.
+// grid = (P, h_q, B) with P = ceil(max_l_kv / kSelSlice), block = 256.
+constexpr int kSelSlice = 4096;
+
+__global__ __launch_bounds__(kBlock) void k_threshold_select(const StreamArgs a, float* tau_out) {
+  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int row = b * a.h_q + j;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int N = a.N;
+  const int tid = threadIdx.x;
+  const long long rbase = (long long)row * a.lpad;
+
+  __shared__ unsigned s_hist[256];
+  __shared__ int s_itmp[kWaves];
+  __shared__ unsigned s_res[2];
+  __shared__ float s_cand[kSelSlice];
+  __shared__ int s_cc, s_base, s_last;
+
+  const bool active = L > 0 && N < L;
+  unsigned d1 = 0u, k1 = 1u;
+  if (active) {
+    s_hist[tid] = a.hist[(long long)row * 256 + tid];
+    if (tid == 0) s_cc = 0;
+    __syncthreads();
+    digit_of_kth_largest(s_hist, (unsigned)N, s_itmp, s_res);
+    d1 = s_res[0];
+    k1 = s_res[1];
+    const int lo = p * kSelSlice, hi = min(lo + kSelSlice, L);
+    for (int i = lo + tid; i < hi; i += kBlock) {
+      const float v = a.scores[rbase + i];
+      if ((order_key(v) >> 24) == d1) s_cand[atomicAdd(&s_cc, 1)] = v;
+    }
+    __syncthreads();
+    const int cnt = s_cc;
+    if (tid == 0 && cnt > 0) s_base = (int)atomicAdd(&a.cand_cnt[row], (unsigned)cnt);
+    __syncthreads();
+    for (int i = tid; i < cnt; i += kBlock) a.surv_val[rbase + s_base + i] = s_cand[i];
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&a.done[row], 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (L > 0) {
+    float tau = -INFINITY;
+    if (active) {
+      const unsigned C = __hip_atomic_load(&a.cand_cnt[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t u = radix_select_block(a.surv_val + rbase, (long long)C, d1 << 24, 0xff000000u, 16, k1,
+                                            s_hist, s_itmp, s_res);
+      tau = order_key_to_f32(u);
+    }
+    if (tid == 0) tau_out[row] = tau;
+  }
+  a.hist[(long long)row * 256 + tid] = 0u;
+  if (tid == 0) {
+    a.cand_cnt[row] = 0u;
+    a.done[row] = 0u;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Sparse softmax and value gather (eq. (7)) over the kept entries of one row.
+
+struct GatherArgs {
+  StreamArgs s;           // q, k, l_kv, scores, survivor lists, counts
+  const void* v;          // [B, h_v, l_max, D]
+  float* tau;             // [B*h_q] (written only by a forced refresh)
+  void* out;              // [B*h_q, D]
+  int32_t* sel_count;     // [B*h_q] or null
+  int32_t* sel_idx;       // [B*h_q, sel_cap] or null
+  int32_t* flags;         // [B*h_q] or null
+  float* part;            // [B*h_q, S, D+4] per-block partials
+  unsigned* row_done;     // [B*h_q] block counter (zero between calls)
+  int h_v, sel_cap, out_bf16, refreshed;
+};
+
+template <int D>
+__device__ __forceinline__ void store_out(const GatherArgs& a, long long row, int d, float x) {
+  if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16(x);
+  else reinterpret_cast<float*>(a.out)[row * D + d] = x;
+}
+
+// Accumulate w * V[i] over a list of (index, logit) pairs handed out to groups of G
+// lanes (one value row per group). acc gets this lane's EPL columns.
+template <typename T, int D>
+struct RowGather {
+  static constexpr int EPL = Unpack<T>::kN;  // columns per lane (16 bytes)
+  static constexpr int G = D / EPL;          // lanes per value row
+  static constexpr int NG = kBlock / G;      // rows in flight per block pass
+};
+
+// Reduce the per-group accumulators of a block into s_red[0..D) (+ Z in s_red[D]).
+template <typename T, int D>
+__device__ __forceinline__ void reduce_groups(const float* acc, float z, float* s_red_big, float* s_out /*[D+1]*/) {
+  using RG = RowGather<T, D>;
+  const int tid = threadIdx.x, grp = tid / RG::G, gl = tid - grp * RG::G;
+#pragma unroll
+  for (int e = 0; e < RG::EPL; ++e) s_red_big[grp * (D + 1) + gl * RG::EPL + e] = acc[e];
+  if (gl == 0) s_red_big[grp * (D + 1) + D] = z;
+  __syncthreads();
+  for (int col = tid; col <= D; col += kBlock) {
+    float x = 0.f;
+    for (int q = 0; q < RG::NG; ++q) x += s_red_big[q * (D + 1) + col];
+    s_out[col] = x;
+  }
+  __syncthreads();
+}
+
+// Forced refresh of one row by a single block (a stale threshold kept nothing):
+// logits of every key of the row with the same tiles as the streaming kernels, the
+// exact N-th largest, then the sparse softmax-PV over the new selection.
+template <typename T, int D>
+__device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, float* s_red_big, float* s_out) {
+  constexpr int TPW = StreamCfg<T, D>::kTPW;
+  constexpr int CH = StreamCfg<T, D>::kChunk;
+  using RG = RowGather<T, D>;
+  const StreamArgs& s = a.s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int row = b * s.h_q + j;
+  const long long rbase = (long long)row * s.lpad;
+  const int g = j / s.g_k;
+  const int jt = (j - g * s.g_k) / 16;
+  const int j0 = g * s.g_k + jt * 16;
+  const int nh = min(16, s.g_k - jt * 16);
+  const int jj = j - j0;
+
+  // 1) logits of head j for all keys, into the row's score buffer
+  {
+    QK<T, D> qk;
+    qk.load_q(reinterpret_cast<const T*>(s.q) + (size_t)(b * s.h_q + j0) * D, nh, lane);
+    const T* kh = reinterpret_cast<const T*>(s.k) + (size_t)(b * s.h_k + g) * s.l_max * D;
+    const int kq = lane >> 4;
+    for (int base = 0; base < L; base += CH) {
+      const int wbase = base + wv * 16 * TPW;
+      if (wbase < L) {
+        floatx4 sc[TPW];
+        score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, s.scale);
+        if ((lane & 15) == jj) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = wbase + 16 * t + 4 * kq + r;
+              if (key < L) s.scores[rbase + key] = sc[t][r];
+            }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  __shared__ unsigned s_hist[256];
+  __shared__ int s_itmp[kWaves];
+  __shared__ unsigned s_res[2];
+  __shared__ float s_ftmp[kWaves];
+  __shared__ int s_list_i[kBlock];
+  __shared__ float s_list_v[kBlock];
+  __shared__ int s_n;
+
+  // 2) exact threshold and the row maximum
+  const float* srow = s.scores + rbase;
+  float tau = -INFINITY;
+  if (s.N < L)
+    tau = order_key_to_f32(radix_select_block(srow, L, 0u, 0u, 24, (unsigned)s.N, s_hist, s_itmp, s_res));
+  float m = -INFINITY;
+  for (int i = tid; i < L; i += kBlock) m = fmaxf(m, srow[i]);
+  m = block_max(m, s_ftmp);
+
+  // 3) compare, compact 256 keys at a time, gather their value rows
+  const int vh = (int)(((long long)j * a.h_v) / s.h_q);
+  const int grp = tid / RG::G, gl = tid - grp * RG::G;
+  const T* vbase = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_v + vh) * s.l_max * D + gl * RG::EPL;
+  float acc[RG::EPL];
+#pragma unroll
+  for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
+  float z = 0.f;
+  int kept = 0;
+  for (int base = 0; base < L; base += kBlock) {
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    const int i = base + tid;
+    if (i < L) {
+      const float v = srow[i];
+      if (v >= tau) {
+        const int slot = atomicAdd(&s_n, 1);
+        s_list_i[slot] = i;
+        s_list_v[slot] = v;
+      }
+    }
+    __syncthreads();
+    const int n = s_n;
+    for (int p = grp; p < n; p += RG::NG) {
+      const int idx = s_list_i[p];
+      const float w = expf(s_list_v[p] - m);
+      float x[RG::EPL];
+      Unpack<T>::run(ld16(vbase + (size_t)idx * D), x);
+#pragma unroll
+      for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
+      z += w;
+      if (gl == 0 && a.sel_idx && kept + p < a.sel_cap) a.sel_idx[(long long)row * a.sel_cap + kept + p] = idx;
+    }
+    kept += n;
+    __syncthreads();
+  }
+  reduce_groups<T, D>(acc, z, s_red_big, s_out);
+  const float Z = s_out[D];
+  for (int d = tid; d < D; d += kBlock) store_out<D>(a, row, d, s_out[d] / Z);
+  if (tid == 0) {
+    a.tau[row] = tau;
+    if (a.sel_count) a.sel_count[row] = kept;
+    if (a.flags) a.flags[row] = 3;
+  }
+}
+
+// grid = (S, h_q, B), block = 256. Block s of row (b, j) takes the kept entries of
+// chunks [s*nch_b/S, (s+1)*nch_b/S), computes their softmax numerator and value sum
+// relative to its own maximum, and writes a partial (m, Z, count, o[D]). The last
+// block of the row merges the S partials (log-sum-exp), writes the output row and
+// the optional index export, and runs the forced refresh if the row kept nothing.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void k_sparse_gather(const GatherArgs a) {
+  constexpr int CH = StreamCfg<T, D>::kChunk;
+  using RG = RowGather<T, D>;
+  const StreamArgs& sa = a.s;
+  const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int S = gridDim.x;
+  const int row = b * sa.h_q + j;
+  const int L = min(sa.l_kv[b], sa.max_l_kv);
+  const int tid = threadIdx.x;
+
+  if (L <= 0) {
+    if (s == 0) {
+      for (int d = tid; d < D; d += kBlock) store_out<D>(a, row, d, 0.f);
+      if (tid == 0) {
+        if (a.sel_count) a.sel_count[row] = 0;
+        if (a.flags) a.flags[row] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ int s_pref[kBlock + 1];
+  __shared__ int s_itmp[kWaves];
+  __shared__ float s_ftmp[kWaves];
+  __shared__ float s_red_big[RG::NG * (D + 1)];
+  __shared__ float s_out[D + 1];
+  __shared__ float s_w[64];
+  __shared__ int s_last;
+
+  const long long rbase = (long long)row * sa.lpad;
+  const long long cbase = (long long)row * sa.nch;
+  const int nch_b = (L + CH - 1) / CH;
+  const int c0 = (int)(((long long)nch_b * s) / S), c1 = (int)(((long long)nch_b * (s + 1)) / S);
+
+  // this block's maximum kept logit and count
+  float m = -INFINITY;
+  int cnt_all = 0;
+  for (int cb = c0; cb < c1; cb += kBlock) {
+    const int c = cb + tid;
+    if (c < c1) {
+      const int n = sa.chunk_cnt[cbase + c];
+      cnt_all += n;
+      if (n > 0) m = fmaxf(m, sa.chunk_max[cbase + c]);
+    }
+  }
+  m = block_max(m, s_ftmp);
+  cnt_all = block_sum_i(cnt_all, s_itmp);
+
+  const int vh = (int)(((long long)j * a.h_v) / sa.h_q);
+  const int grp = tid / RG::G, gl = tid - grp * RG::G;
+  const T* vbase = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_v + vh) * sa.l_max * D + gl * RG::EPL;
+  float acc[RG::EPL];
+#pragma unroll
+  for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
+  float z = 0.f;
+
+  if (cnt_all > 0) {
+    for (int cb = c0; cb < c1; cb += kBlock) {
+      const int c = cb + tid;
+      const int n = (c < c1) ? sa.chunk_cnt[cbase + c] : 0;
+      int tot;
+      const int ex = block_excl_scan(n, s_itmp, tot);
+      s_pref[tid] = ex;
+      if (tid == kBlock - 1) s_pref[kBlock] = tot;
+      __syncthreads();
+      constexpr int U = 4;  // value rows in flight per group
+      for (int p0 = 0; p0 < tot; p0 += RG::NG * U) {
+        int idx[U];
+        float wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = p0 + u * RG::NG + grp;
+          idx[u] = -1;
+          wv[u] = 0.f;
+          if (p < tot) {
+            int lo = 0, hi = kBlock;
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (s_pref[mid] <= p) lo = mid; else hi = mid;
+            }
+            const long long off = rbase + (long long)(cb + lo) * CH + (p - s_pref[lo]);
+            idx[u] = sa.surv_idx[off];
+            wv[u] = sa.surv_val[off];
+          }
+        }
+        uint4 vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) vr[u] = (idx[u] >= 0) ? ld16(vbase + (size_t)idx[u] * D) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (idx[u] >= 0) {
+            const float w = expf(wv[u] - m);
+            float x[RG::EPL];
+            Unpack<T>::run(vr[u], x);
+#pragma unroll
+            for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
+            z += w;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  reduce_groups<T, D>(acc, z, s_red_big, s_out);
+
+  float* part = a.part + ((long long)row * S + s) * (D + 4);
+  for (int d = tid; d < D; d += kBlock) part[4 + d] = s_out[d];
+  if (tid == 0) {
+    part[0] = m;
+    part[1] = s_out[D];
+    part[2] = __int_as_float(cnt_all);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&a.row_done[row], 1u) == (unsigned)(S - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // merge the S partials of the row
+  const float* rp = a.part + (long long)row * S * (D + 4);
+  float mm = -INFINITY;
+  int total = 0;
+  if (tid < S) {
+    const int n = __float_as_int(rp[(long long)tid * (D + 4) + 2]);
+    total = n;
+    if (n > 0) mm = rp[(long long)tid * (D + 4)];
+  }
+  const float M = block_max(mm, s_ftmp);
+  total = block_sum_i(total, s_itmp);
+  if (tid == 0) a.row_done[row] = 0u;
+
+  if (total == 0) {
+    forced_refresh_row<T, D>(a, b, j, L, s_red_big, s_out);
+    return;
+  }
+  float zz = 0.f;
+  if (tid < S) {
+    const int n = __float_as_int(rp[(long long)tid * (D + 4) + 2]);
+    const float w = (n > 0) ? expf(rp[(long long)tid * (D + 4)] - M) : 0.f;
+    s_w[tid] = w;
+    zz = w * rp[(long long)tid * (D + 4) + 1];
+  }
+  const float Z = block_sum(zz, s_ftmp);  // also orders s_w before use
+  for (int d = tid; d < D; d += kBlock) {
+    float o = 0.f;
+    for (int q = 0; q < S; ++q) {
+      const float w = s_w[q];
+      if (w != 0.f) o += w * rp[(long long)q * (D + 4) + 4 + d];
+    }
+    store_out<D>(a, row, d, o / Z);
+  }
+  if (tid == 0) {
+    if (a.sel_count) a.sel_count[row] = total;
+    if (a.flags) a.flags[row] = a.refreshed ? 1 : 0;
+  }
+  // optional export of the kept indices (list order: chunk order)
+  if (a.sel_idx) {
+    int written = 0;
+    for (int cb = 0; cb < nch_b && written < a.sel_cap; cb += kBlock) {
+      const int c = cb + tid;
+      const int n = (c < nch_b) ? sa.chunk_cnt[cbase + c] : 0;
+      int tot;
+      const int ex = block_excl_scan(n, s_itmp, tot);
+      for (int t = 0; t < n; ++t) {
+        const int pos = written + ex + t;
+        if (pos < a.sel_cap) a.sel_idx[(long long)row * a.sel_cap + pos] = sa.surv_idx[rbase + (long long)c * CH + t];
+      }
+      written += tot;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Dense grouped-query attention (eq. (2)-(4)), split over the cached keys.
+
+struct DenseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* l_kv;
+  float* part;     // [B*h_q, nchd, D+4] per-chunk (m, Z, -, -, o[D])
+  void* out;
+  int h_q, h_kv, g, l_max, nchd, out_bf16;
+  int max_l_kv;
+  float scale;
+};
+
+// grid = (nchd, h_kv, B), block = 256. Each block: logits of CHD keys for the g query
+// heads of one key/value head (MFMA), the chunk's softmax numerator relative to the
+// chunk maximum, and its product with the chunk's value rows (VALU).
+template <typename T, int D, int GH>
+__global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
+  constexpr int TPW = StreamCfg<T, D>::kTPW;
+  constexpr int CHD = StreamCfg<T, D>::kChunk;
+  constexpr int EPL = Unpack<T>::kN;
+  constexpr int G = D / EPL;                         // lanes per value row
+  constexpr int VL = (16 * D) / (EPL * kWave);       // 16-byte value loads per lane per tile
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int base = c * CHD;
+  if (base >= L) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int hh = lane & 15, kq = lane >> 4;
+  const int j0 = g * a.g;
+  const int row0 = b * a.h_q + j0;
+
+  __shared__ float s_p[kWaves][TPW][16][GH];
+  __shared__ float s_m[kWaves][GH], s_z[kWaves][GH];
+  __shared__ float s_o[kWaves][GH][D];
+
+  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_kv + g) * a.l_max * D;
+  const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_kv + g) * a.l_max * D;
+  const int wbase = base + wv * 16 * TPW;
+
+  // value tiles: load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
+  uint4 vb[TPW][VL];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < VL; ++r) {
+      const int e = r * kWave + lane;
+      const int key = min(wbase + 16 * t + e / G, L - 1);
+      vb[t][r] = ld16(vh + (size_t)key * D + (e % G) * EPL);
+    }
+
+  QK<T, D> qk;
+  qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, a.g, lane);
+  floatx4 sc[TPW];
+  score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+
+  float mh = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = wbase + 16 * t + 4 * kq + r;
+      if (key >= L) sc[t][r] = -INFINITY;
+      mh = fmaxf(mh, sc[t][r]);
+    }
+  mh = fmaxf(mh, __shfl_xor(mh, 16));
+  mh = fmaxf(mh, __shfl_xor(mh, 32));
+  float zh = 0.f;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = (mh == -INFINITY) ? 0.f : expf(sc[t][r] - mh);
+      zh += p;
+      if (hh < GH) s_p[wv][t][4 * kq + r][hh] = p;
+    }
+  zh += __shfl_xor(zh, 16);
+  zh += __shfl_xor(zh, 32);
+  if (lane < GH) {
+    s_m[wv][lane] = mh;
+    s_z[wv][lane] = zh;
+  }
+  __syncthreads();
+
+  float o[GH][EPL];
+#pragma unroll
+  for (int h = 0; h < GH; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < VL; ++r) {
+      const int e = r * kWave + lane;
+      const int k16 = e / G;
+      float x[EPL];
+      Unpack<T>::run(vb[t][r], x);
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        const float p = s_p[wv][t][k16][h];
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) o[h][q] += p * x[q];
+      }
+    }
+  // lanes with the same column group (lane % G) hold partial sums over different keys
+#pragma unroll
+  for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < GH; ++h)
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) o[h][q] += __shfl_xor(o[h][q], off);
+  if (lane < G) {
+#pragma unroll
+    for (int h = 0; h < GH; ++h)
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) s_o[wv][h][lane * EPL + q] = o[h][q];
+  }
+  __syncthreads();
+
+  // merge the 4 waves (each relative to its own maximum) and write the chunk partial
+  for (int idx = tid; idx < a.g * (D + 1); idx += kBlock) {
+    const int h = idx / (D + 1), d = idx - h * (D + 1);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w][h];
+      const float sw = (mw == -INFINITY) ? 0.f : expf(mw - M);
+      acc += sw * (d < D ? s_o[w][h][d] : s_z[w][h]);
+    }
+    float* pp = a.part + ((long long)(row0 + h) * a.nchd + c) * (D + 4);
+    if (d < D) pp[4 + d] = acc;
+    else {
+      pp[0] = M;
+      pp[1] = acc;
+    }
+  }
+}
+
+// Log-sum-exp merge of the chunk partials of each row (b, j).
+// grid = (D / 32, h_q, B), block = 256 = 32 columns x 8 chunk subsets.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_dense_combine(const DenseArgs a, int chd) {
+  const int cg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int row = b * a.h_q + j;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int tid = threadIdx.x;
+  const int col = cg * 32 + (tid & 31), sub = tid >> 5;
+  __shared__ float s_ftmp[kWaves];
+  __shared__ float s_acc[8][33];
+  if (L <= 0) {
+    if (tid < 32) {
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(long long)row * D + col] = 0;
+      else reinterpret_cast<float*>(a.out)[(long long)row * D + col] = 0.f;
+    }
+    return;
+  }
+  const int nch_b = (L + chd - 1) / chd;
+  const float* rp = a.part + (long long)row * a.nchd * (D + 4);
+  float m = -INFINITY;
+  for (int c = tid; c < nch_b; c += kBlock) m = fmaxf(m, rp[(long long)c * (D + 4)]);
+  const float M = block_max(m, s_ftmp);
+  float o = 0.f, z = 0.f;
+#pragma unroll 8
+  for (int c = sub; c < nch_b; c += 8) {
+    const float* pc = rp + (long long)c * (D + 4);
+    const float w = expf(pc[0] - M);
+    o += w * pc[4 + col];
+    z += w * pc[1];
+  }
+  s_acc[sub][tid & 31] = o;
+  if ((tid & 31) == 0) s_acc[sub][32] = z;
+  __syncthreads();
+  if (tid < 32) {
+    float oo = 0.f, zz = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      oo += s_acc[q][tid];
+      zz += s_acc[q][32];
+    }
+    const float x = oo / zz;
+    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(long long)row * D + col] = f32_to_bf16(x);
+    else reinterpret_cast<float*>(a.out)[(long long)row * D + col] = x;
+  }
+}
+
+// Zero fill (workspace initialisation) with 16-byte stores plus a byte tail.
+__global__ void k_zero_fill(uint8_t* p, size_t n) {
+  const size_t n16 = n / 16;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < (n & 15)) p[n16 * 16 + threadIdx.x] = 0;
+}
+
+}  // namespace saga

@@ -1,0 +1,278 @@
+"""HIP path vs the CPU oracle on identical seeded inputs (needs an MI355X).
+
+Sizes: small cases span several chunks and a ragged tail; the named workloads run
+at full size in the launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import saga_oracle as orc
+from sparse_decode_attention_saga_amd import api
+from sparse_decode_attention_saga_amd import workloads as wl
+from tests.parity import GpuCase, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def oracle_step(x, N, n, step, tau_in=None):
+    q64, k64, v64 = x.f64()
+    return orc.saga_decode_step(q64, k64, v64, x.l_kv, N, n, step, tau_in=tau_in)
+
+
+def small(B, h_q, h_k, h_v, d, lens, dtype, seed, plant=0.01, l_max=None):
+    w = wl.Workload("small", 90 + seed, batch=B, h_q=h_q, h_k=h_k, h_v=h_v, d=d, l_kv=max(lens), N=1,
+                    refresh_period=1, dtype=dtype, plant_frac=plant)
+    return w, wl.generate(w, seed=seed, lengths=lens, l_max=l_max or max(max(lens), 1))
+
+
+# --- the tiny fp32 workload: refresh every step == exact top-N ------------------
+
+def test_tiny_fp32_exact_topn():
+    w = wl.TINY
+    x = wl.generate(w, seed=0)
+    say(f"{w.name} N={w.N}")
+    g = GpuCase(x, w.N)
+    got = g.step(w.refresh_period, 0)
+    ref = oracle_step(x, w.N, w.refresh_period, 0)
+    compare(got, ref, x, "f32", check_tau=True)
+    assert np.all(got["count"] == w.N)          # fp32 logits, no ties: exactly N kept
+    assert np.all(got["flags"] == 1)
+    # next step (refresh again) gives the same answer
+    got2 = g.step(w.refresh_period, 1)
+    assert np.array_equal(np.sort(got2["idx"], axis=-1), np.sort(got["idx"], axis=-1))
+
+
+# --- small shapes: several chunks, ragged tails, head groupings ----------------
+
+SMALL = [
+    # B, h_q, h_k, h_v, d, lens, dtype, N
+    (2, 8, 2, 4, 64, [1000, 37], "bf16", 16),
+    (3, 12, 1, 4, 128, [513, 1, 2000], "bf16", 32),
+    (1, 32, 2, 8, 64, [4097], "bf16", 64),
+    (2, 4, 1, 4, 64, [300, 65], "f32", 8),
+    (1, 16, 1, 16, 128, [777], "f32", 20),
+    (1, 40, 1, 8, 64, [1500], "bf16", 10),
+    (2, 6, 6, 6, 64, [100, 64], "bf16", 100),
+    (2, 8, 4, 2, 128, [3000, 2999], "bf16", 7),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_shapes_refresh_and_stale(case):
+    B, h_q, h_k, h_v, d, lens, dtype, N = SMALL[case]
+    say(f"small case {case}: {SMALL[case]}")
+    w, x = small(B, h_q, h_k, h_v, d, lens, dtype, seed=case)
+    g = GpuCase(x, N)
+    got = g.step(4, 0)                            # refresh step
+    ref = oracle_step(x, N, 4, 0)
+    compare(got, ref, x, dtype, check_tau=True)
+    assert np.all(got["flags"][np.array(lens) > 0] == 1)
+    # stale step on the same inputs with each side's own threshold: same selection
+    got1 = g.step(4, 1)
+    ref1 = oracle_step(x, N, 4, 1, tau_in=ref.tau)
+    compare(got1, ref1, x, dtype, check_tau=False)
+    assert np.all(got1["flags"][np.array(lens) > 0] == 0)
+    assert np.array_equal(got1["count"], got["count"])
+
+
+def test_bf16_output_rounding():
+    w, x = small(1, 12, 1, 4, 128, [5000], "bf16", seed=20)
+    g = GpuCase(x, 64, out_dtype=torch.bfloat16)
+    got = g.step(1, 0)
+    compare(got, oracle_step(x, 64, 1, 0), x, "bf16", check_tau=True, out_bf16=True)
+
+
+# --- named workloads at full size ------------------------------------------------
+
+@pytest.mark.parametrize("name", ["llama3.2-1b-shape-l32k", "qwen2.5-1.5b-shape-l128k"])
+def test_workload_full_size(name):
+    w = wl.WORKLOADS[name]
+    x = wl.generate(w, seed=0)
+    say(f"{name}: refresh step then stale steps")
+    g = GpuCase(x, w.N)
+    got = g.step(w.refresh_period, 0)
+    ref = oracle_step(x, w.N, w.refresh_period, 0)
+    bands = compare(got, ref, x, w.dtype, check_tau=True)
+    assert bands <= max(1, w.h_q // 8)
+    got1 = g.step(w.refresh_period, 5)
+    ref1 = oracle_step(x, w.N, w.refresh_period, 5, tau_in=ref.tau)
+    compare(got1, ref1, x, w.dtype, check_tau=False)
+
+
+def test_ragged_batch_full_size():
+    w = wl.RAGGED_B8
+    x = wl.generate(w, seed=0)
+    say(f"{w.name}: lengths {x.l_kv.tolist()}")
+    g = GpuCase(x, w.N)
+    got = g.step(w.refresh_period, 0)
+    ref = oracle_step(x, w.N, w.refresh_period, 0)
+    bands = compare(got, ref, x, w.dtype, check_tau=True)
+    assert bands <= 8
+    got1 = g.step(w.refresh_period, 3)
+    compare(got1, oracle_step(x, w.N, w.refresh_period, 3, tau_in=ref.tau), x, w.dtype, check_tau=False)
+
+
+# --- multi-step decode: appended rows, drifting query, periodic refresh ----------
+
+def test_multistep_append_and_drift():
+    w = wl.SWEEP.with_(N=128, refresh_period=8)
+    s = wl.DecodeStream(w, seed=0, l0=4096, l_max=4096 + 40)
+    g = GpuCase(s.inputs(), w.N, max_l_kv=4096 + 40)
+    tau_o = None
+    for t in range(24):
+        x = s.inputs()
+        g.refresh_inputs(x)
+        got = g.step(w.refresh_period, t)
+        ref = oracle_step(x, w.N, w.refresh_period, t, tau_in=tau_o)
+        compare(got, ref, x, w.dtype, check_tau=(t % w.refresh_period == 0))
+        assert np.all((got["flags"] & 1) == (1 if t % w.refresh_period == 0 else 0)) or ref.fallback.any()
+        tau_o = ref.tau
+        s.append(1)
+        s.drift()
+
+
+# --- forced paths ------------------------------------------------------------------
+
+def test_empty_stale_selection_forces_refresh():
+    w, x = small(2, 8, 2, 4, 128, [2500, 700], "bf16", seed=30)
+    N = 24
+    g = GpuCase(x, N, sel_cap=700)
+    tau_in = np.full((2, 8), np.inf, np.float32)
+    tau_in[1, 5] = -np.inf                        # this row keeps everything instead
+    got = g.step(10, 3, tau_in=tau_in)
+    ref = oracle_step(x, N, 10, 3, tau_in=tau_in.astype(np.float64))
+    compare(got, ref, x, "bf16", check_tau=True)
+    forced = ref.fallback
+    assert forced.sum() == 15 and not forced[1, 5]
+    assert np.all((got["flags"] == 3) == forced)
+    assert got["count"][1, 5] == 700
+
+
+def test_minus_inf_threshold_equals_dense():
+    w, x = small(1, 4, 1, 4, 64, [900], "f32", seed=31)
+    g = GpuCase(x, 8, sel_cap=900)
+    got = g.step(5, 2, tau_in=np.full((1, 4), -np.inf, np.float32))
+    q64, k64, v64 = x.f64()
+    dense = orc.saga_decode_step(q64, k64, v64, x.l_kv, N=10 ** 6, refresh_period=1, step=0)
+    assert np.all(got["count"] == 900)
+    np.testing.assert_allclose(got["O"], dense.O, rtol=0, atol=1e-5 * np.abs(dense.O).max())
+
+
+def test_n_at_least_length_is_dense():
+    w, x = small(2, 8, 2, 8, 64, [50, 300], "bf16", seed=32)
+    g = GpuCase(x, 64, sel_cap=300)
+    got = g.step(1, 0)
+    ref = oracle_step(x, 64, 1, 0)
+    compare(got, ref, x, "bf16", check_tau=True)
+    assert np.all(np.isneginf(got["tau"][0])) and np.all(got["count"][0] == 50)
+
+
+def test_empty_sequences():
+    w, x = small(3, 4, 1, 2, 64, [0, 333, 0], "bf16", seed=33, l_max=400)
+    g = GpuCase(x, 16)
+    g.tau.fill_(0.75)
+    got = g.step(2, 0)
+    ref = oracle_step(x, 16, 2, 0, tau_in=np.full((3, 4), 0.75))
+    compare(got, ref, x, "bf16", check_tau=True)
+    assert np.all(got["tau"][[0, 2]] == 0.75)
+    # every sequence empty: nothing to stream, zero outputs
+    x0 = wl.Inputs(x.q, x.k, x.v, np.zeros(3, np.int32))
+    g2 = GpuCase(x0, 16, max_l_kv=0)
+    got0 = g2.step(1, 0)
+    assert np.all(got0["O"] == 0) and np.all(got0["count"] == 0)
+
+
+def test_ties_keep_every_equal_logit():
+    # every key of the row identical: all logits tie at the threshold, all are kept
+    w, x = small(1, 4, 1, 2, 64, [600], "bf16", seed=34)
+    x.k[0, 0, :600] = x.k[0, 0, 7]
+    g = GpuCase(x, 10, sel_cap=600)
+    got = g.step(1, 0)
+    assert np.all(got["count"] == 600)
+    v = x.v.double().numpy()
+    for j in range(4):
+        mean = v[0, j // 2, :600].mean(axis=0)
+        assert np.abs(got["O"][0, j] - mean).max() <= 2e-3 * np.abs(mean).max()
+
+
+# --- the other entry points --------------------------------------------------------
+
+def test_refresh_threshold_entry_point():
+    w, x = small(2, 12, 1, 4, 128, [3000, 1200], "bf16", seed=35)
+    g = GpuCase(x, 1)
+    q64, k64, _ = x.f64()
+    for N in (1, 7, 100, 1199, 1200, 5000):
+        api.refresh_threshold(g.q, g.k, g.l_kv, g.tau, N=N, max_l_kv=g.max_l_kv, workspace=g.ws)
+        torch.cuda.synchronize()
+        got = g.tau.double().cpu().numpy()
+        want = orc.refresh_threshold(q64, k64, x.l_kv, N)
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(got), fin), N
+        assert np.all(got[~fin] == want[~fin])
+        assert np.all(np.abs(got[fin] - want[fin]) <= 1e-5 * np.abs(want[fin])), N
+
+
+def test_stages_equal_decode_step():
+    w, x = small(1, 12, 1, 4, 128, [6000], "bf16", seed=36)
+    g = GpuCase(x, 64)
+    g.step(8, 0)
+    ref = g.step(8, 1)
+    tau = g.tau.clone()
+    out = torch.empty_like(g.out)
+    api.qk_select(g.q, g.k, g.l_kv, tau, max_l_kv=g.max_l_kv, workspace=g.ws)
+    api.sparse_gather(g.q, g.k, g.v, g.l_kv, tau, N=64, max_l_kv=g.max_l_kv, out=out, workspace=g.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.double().cpu().numpy(), ref["O"], rtol=0, atol=1e-6)
+
+
+DENSE = [
+    # B, h_q, h_kv, d, lens, dtype
+    (1, 12, 2, 128, [5000], "bf16"),
+    (2, 32, 8, 64, [3000, 17], "bf16"),
+    (3, 4, 1, 64, [1, 0, 700], "f32"),
+    (1, 16, 1, 128, [2049], "f32"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DENSE)))
+def test_dense_gqa(case):
+    B, h_q, h_kv, d, lens, dtype = DENSE[case]
+    say(f"dense case {case}: {DENSE[case]}")
+    w, x = small(B, h_q, h_kv, h_kv, d, lens, dtype, seed=40 + case)
+    dev = torch.device("cuda:0")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    l_kv = torch.from_numpy(x.l_kv).to(dev)
+    out = api.dense_gqa_attn(q, k, v, l_kv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q64, k64, v64 = x.f64()
+    ref = orc.dense_gqa(q64, k64, v64, x.l_kv)
+    got = out.double().cpu().numpy()
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    for b in range(B):
+        if x.l_kv[b] == 0:
+            assert np.all(got[b] == 0)
+            continue
+        for j in range(h_q):
+            s = np.abs(ref[b, j]).max()
+            assert np.abs(got[b, j] - ref[b, j]).max() <= tol * s, (b, j)
+
+
+@pytest.mark.parametrize("name", ["llama3.2-1b-shape-l32k", "qwen2.5-1.5b-shape-l128k"])
+def test_dense_gqa_full_size(name):
+    w0 = wl.WORKLOADS[name]
+    w = w0.with_(h_k=w0.dense_h_kv, h_v=w0.dense_h_kv, workload_id=w0.workload_id + 100)
+    x = wl.generate(w, seed=0)
+    dev = torch.device("cuda:0")
+    out = api.dense_gqa_attn(x.q.to(dev), x.k.to(dev), x.v.to(dev), torch.from_numpy(x.l_kv).to(dev),
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q64, k64, v64 = x.f64()
+    ref = orc.dense_gqa(q64, k64, v64, x.l_kv)
+    got = out.double().cpu().numpy()
+    err = np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)
+    assert err.max() <= 2e-3, err.max()

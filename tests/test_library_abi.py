@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every function include/saga.h declares, and
+rejects bad arguments on the host before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_decode_attention_saga_amd import api
+from sparse_decode_attention_saga_amd import build as build_mod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saga.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build_mod.LIB_PATH):
+        build_mod.build()
+    return api.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(saga_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(api.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["SAGA_OK", "SAGA_ERR_NULL", "SAGA_ERR_SHAPE", "SAGA_ERR_UNSUPPORTED",
+                                 "SAGA_ERR_WORKSPACE", "SAGA_ERR_HIP"]):
+        assert api.status_str(code) == name
+    assert api.status_str(77) == "SAGA_ERR_UNKNOWN"
+
+
+def shape(**kw):
+    d = dict(batch=1, h_q=12, h_k=1, h_v=4, d=128, l_max=131072, dtype=api.BF16, out_dtype=api.BF16, scale=0.0)
+    d.update(kw)
+    return api.SagaShape(**d)
+
+
+def test_workspace_bytes(lib):
+    s = shape()
+    n = lib.saga_workspace_bytes(ctypes.byref(s), 512, 131072)
+    # at least the fp32 logits, kept indices and kept logits of every row
+    assert n >= 3 * 12 * 131072 * 4
+    assert lib.saga_workspace_bytes(ctypes.byref(s), 512, 4096) < n
+    assert lib.saga_workspace_bytes(ctypes.byref(shape(h_k=5)), 512, 1024) == 0
+    assert lib.saga_workspace_bytes(ctypes.byref(shape(d=96)), 512, 1024) == 0
+    assert lib.saga_workspace_bytes(ctypes.byref(s), 0, 1024) == 0
+    assert lib.saga_workspace_bytes(ctypes.byref(s), 8, 131073) == 0
+    assert lib.saga_workspace_bytes(None, 8, 16) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def decode(lib, s, N=8, period=4, step=1, ws_bytes=1 << 40, max_l=1024, tau=FAKE, sel_idx=None, cap=0):
+    return lib.saga_decode_attn(None if s is None else ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, max_l, N,
+                                period, step, tau, FAKE, None, sel_idx, cap, None, FAKE, ws_bytes, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert decode(lib, None) == api.ERR_NULL
+    assert decode(lib, shape(), tau=None) == api.ERR_NULL
+    assert decode(lib, shape(h_k=5)) == api.ERR_SHAPE
+    assert decode(lib, shape(h_v=7)) == api.ERR_SHAPE
+    assert decode(lib, shape(batch=0)) == api.ERR_SHAPE
+    assert decode(lib, shape(scale=-1.0)) == api.ERR_SHAPE
+    assert decode(lib, shape(), N=0) == api.ERR_SHAPE
+    assert decode(lib, shape(), period=0) == api.ERR_SHAPE
+    assert decode(lib, shape(), step=-1) == api.ERR_SHAPE
+    assert decode(lib, shape(), max_l=131073) == api.ERR_SHAPE
+    assert decode(lib, shape(), max_l=-1) == api.ERR_SHAPE
+    assert decode(lib, shape(), sel_idx=FAKE, cap=0) == api.ERR_SHAPE
+    assert decode(lib, shape(d=96)) == api.ERR_UNSUPPORTED
+    assert decode(lib, shape(dtype=7)) == api.ERR_UNSUPPORTED
+    assert decode(lib, shape(out_dtype=2)) == api.ERR_UNSUPPORTED
+    assert decode(lib, shape(), ws_bytes=1024) == api.ERR_WORKSPACE
+
+
+def test_other_entry_points_reject_bad_arguments(lib):
+    s = shape()
+    big = 1 << 40
+    assert lib.saga_refresh_threshold(ctypes.byref(s), FAKE, FAKE, FAKE, 1024, 0, FAKE, FAKE, big, None) == api.ERR_SHAPE
+    assert lib.saga_refresh_threshold(ctypes.byref(s), FAKE, FAKE, FAKE, 1024, 4, FAKE, FAKE, 16, None) == api.ERR_WORKSPACE
+    assert lib.saga_qk_select(ctypes.byref(s), FAKE, None, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_NULL
+    assert lib.saga_sparse_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, None, None, None, 0,
+                                  None, FAKE, big, None) == api.ERR_NULL
+    # dense GQA needs as many value heads as key heads
+    assert lib.saga_dense_gqa_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_SHAPE
+    wide = shape(h_q=32, h_k=1, h_v=1)
+    assert lib.saga_dense_gqa_attn(ctypes.byref(wide), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_UNSUPPORTED
+    assert lib.saga_workspace_init(None, 16, None) == api.ERR_NULL
+
+
+def test_binding_requires_gpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 4, 64)
+    k = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        api.decode_attn(q, k, k, torch.zeros(1, dtype=torch.int32), torch.zeros(1, 4), N=4, refresh_period=1, step=0)
