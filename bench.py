@@ -100,6 +100,25 @@ def cpu_baseline(w, x, seconds: float):
                       f"float64 numpy, BLAS threads = cores"}
 
 
+def copy_probe(torch, reps: int) -> int:
+    """torch's device copy of 256 MiB, `reps` times: reads and writes 256 MiB each."""
+    n = 256 << 20
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "launches": reps + 1,
+                      "us_per_copy": us, "read_plus_write_gbs": 2 * n / us / 1e3}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +131,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "saga", "dense", "select"], default="all",
                     help="time only one part (for profiler runs)")
+    ap.add_argument("--probe", choices=["none", "copy"], default="none",
+                    help="copy: time a plain device copy of 256 MiB (counter calibration, streaming ceiling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -122,6 +143,9 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.probe == "copy":
+        return copy_probe(torch, max(args.steps, 8))
 
     from sparse_decode_attention_saga_amd import api
     from sparse_decode_attention_saga_amd import bytemodel

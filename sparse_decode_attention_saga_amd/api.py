@@ -147,6 +147,8 @@ def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale):
     if v is not None:
         _dev(v, "v")
     _dev(l_kv, "l_kv", torch.int32)
+    if out_dtype is None and out is not None:
+        out_dtype = out.dtype
     shape = make_shape(q, k, v, out_dtype, scale)
     if l_kv.numel() != shape.batch:
         raise ValueError("l_kv must have one entry per sequence")

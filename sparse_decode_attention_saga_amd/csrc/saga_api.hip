@@ -11,7 +11,6 @@ using namespace saga;
 
 namespace {
 
-constexpr int kMaxGatherSplits = 64;   // partial slots per row of the sparse gather
 constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
 
 #define SAGA_DISPATCH(DT, DIM, ...)                                   \
@@ -57,9 +56,9 @@ saga_status check_shape(const saga_shape* s) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  int rows, ch, nch, S, P;
+  int rows, ch, nch, P;
   long long lpad;
-  size_t hist, cand_cnt, done, row_done, scores, surv_idx, surv_val, chunk_cnt, chunk_max, part, dpart, total;
+  size_t hist, cand_cnt, scores, surv_idx, surv_val, chunk_cnt, chunk_max, dpart, total;
 };
 
 Layout layout(const saga_shape* s, int max_l_kv) {
@@ -68,8 +67,6 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   w.ch = chunk_keys(s->dtype, s->d);
   w.nch = max_l_kv > 0 ? (max_l_kv + w.ch - 1) / w.ch : 1;
   w.lpad = (long long)w.nch * w.ch;
-  int S = (w.nch + 7) / 8;
-  w.S = S < 1 ? 1 : (S > kMaxGatherSplits ? kMaxGatherSplits : S);
   w.P = max_l_kv > 0 ? (max_l_kv + kSelSlice - 1) / kSelSlice : 1;
   const size_t rows = (size_t)w.rows;
   size_t off = 0;
@@ -78,17 +75,14 @@ Layout layout(const saga_shape* s, int max_l_kv) {
     off = align_up(off + bytes);
     return at;
   };
-  // counters first: they must be zero before the first call
+  // counters first: they must be zero before the first call and every call leaves them at zero
   w.hist = take(rows * 256 * 4);
   w.cand_cnt = take(rows * 4);
-  w.done = take(rows * 4);
-  w.row_done = take(rows * 4);
   w.scores = take(rows * (size_t)w.lpad * 4);
   w.surv_idx = take(rows * (size_t)w.lpad * 4);
   w.surv_val = take(rows * (size_t)w.lpad * 4);
   w.chunk_cnt = take(rows * (size_t)w.nch * 4);
   w.chunk_max = take(rows * (size_t)w.nch * 4);
-  w.part = take(rows * (size_t)w.S * (s->d + 4) * 4);
   w.dpart = take(rows * (size_t)w.nch * (s->d + 4) * 4);
   w.total = off;
   return w;
@@ -113,7 +107,6 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.chunk_max = at<float>(ws, w.chunk_max);
   a.hist = at<unsigned>(ws, w.hist);
   a.cand_cnt = at<unsigned>(ws, w.cand_cnt);
-  a.done = at<unsigned>(ws, w.done);
   a.h_q = s->h_q;
   a.h_k = s->h_k;
   a.g_k = s->h_q / s->h_k;
@@ -148,7 +141,8 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
   SAGA_DISPATCH(s->dtype, s->d, {
     hipLaunchKernelGGL((k_scores_hist<T, D>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });
-  hipLaunchKernelGGL(k_threshold_select, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a, tau);
+  hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
+  hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);
 }
 
 void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, hipStream_t st) {
@@ -162,11 +156,11 @@ void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bo
 
 void launch_gather(const saga_shape* s, const Layout& w, const GatherArgs& g, hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, {
-    hipLaunchKernelGGL((k_sparse_gather<T, D>), dim3(w.S, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+    hipLaunchKernelGGL((k_row_gather<T, D>), dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, g);
   });
 }
 
-GatherArgs gather_args(const saga_shape* s, const Layout& w, void* ws, const StreamArgs& sa, const void* v,
+GatherArgs gather_args(const saga_shape* s, const StreamArgs& sa, const void* v,
                        float* tau, void* out, int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap,
                        int32_t* flags, bool refreshed) {
   GatherArgs g{};
@@ -177,8 +171,6 @@ GatherArgs gather_args(const saga_shape* s, const Layout& w, void* ws, const Str
   g.sel_count = sel_count;
   g.sel_idx = sel_idx;
   g.flags = flags;
-  g.part = at<float>(ws, w.part);
-  g.row_done = at<unsigned>(ws, w.row_done);
   g.h_v = s->h_v;
   g.sel_cap = sel_idx ? sel_cap : 0;
   g.out_bf16 = s->out_dtype == SAGA_BF16;
@@ -238,7 +230,7 @@ saga_status saga_decode_attn(const saga_shape* s, const void* q, const void* k, 
     if (refresh) launch_refresh(s, w, a, tau, hs);
     launch_select(s, w, a, refresh, hs);
   }
-  launch_gather(s, w, gather_args(s, w, workspace, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
+  launch_gather(s, w, gather_args(s, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
   return launched();
 }
 
@@ -278,7 +270,7 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
   const Layout w = layout(s, max_l_kv);
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N);
-  launch_gather(s, w, gather_args(s, w, workspace, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, false),
+  launch_gather(s, w, gather_args(s, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, false),
                 (hipStream_t)stream);
   return launched();
 }
@@ -317,7 +309,7 @@ saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* 
       else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, D, 8>), grid, dim3(kBlock), 0, hs, a);
       else hipLaunchKernelGGL((k_dense_partial<T, D, 16>), grid, dim3(kBlock), 0, hs, a);
     }
-    hipLaunchKernelGGL((k_dense_combine<D>), dim3(D / 32, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
+    hipLaunchKernelGGL((k_dense_combine<D>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
                        (int)StreamCfg<T, D>::kChunk);
   });
   return launched();

@@ -167,7 +167,8 @@ __device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& 
 }
 
 // ----------------------------------------------------------------------------
-// Block-wide helpers for 256-thread blocks. Every thread of the block must call them.
+// Block-wide helpers for blocks of NT threads (a multiple of 64, at most 1024).
+// Every thread of the block must call them. Scratch arrays are __shared__.
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -178,16 +179,17 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-// Exclusive prefix sum over the block in thread order; `total` gets the block sum.
-// `tmp` is __shared__ int[kWaves].
+// Exclusive prefix sum in thread order; `total` gets the block sum. tmp: int[NT/64].
+template <int NT = kBlock>
 __device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int inc = wave_incl_scan(x, lane);
   if (lane == kWave - 1) tmp[w] = inc;
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int t = tmp[i];
     off += (i < w) ? t : 0;
     tot += t;
@@ -213,37 +215,43 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
-// `tmp` is __shared__ float[kWaves].
+// tmp: float[NT/64] (int[NT/64] for the integer sum).
+template <int NT = kBlock>
 __device__ __forceinline__ float block_max(float x, float* tmp) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   x = wave_max(x);
   if (lane == 0) tmp[w] = x;
   __syncthreads();
   float r = tmp[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, tmp[i]);
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, tmp[i]);
   __syncthreads();
   return r;
 }
+template <int NT = kBlock>
 __device__ __forceinline__ float block_sum(float x, float* tmp) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   x = wave_sum(x);
   if (lane == 0) tmp[w] = x;
   __syncthreads();
   float r = 0.f;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += tmp[i];
+  for (int i = 0; i < NW; ++i) r += tmp[i];
   __syncthreads();
   return r;
 }
+template <int NT = kBlock>
 __device__ __forceinline__ int block_sum_i(int x, int* tmp) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   x = wave_sum_i(x);
   if (lane == 0) tmp[w] = x;
   __syncthreads();
   int r = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += tmp[i];
+  for (int i = 0; i < NW; ++i) r += tmp[i];
   __syncthreads();
   return r;
 }
@@ -254,7 +262,8 @@ __device__ __forceinline__ int block_sum_i(int x, int* tmp) {
 // Given a 256-bin histogram `hist` (shared), find the digit whose bin holds the k-th
 // largest element counting from the top bin; res[0] = digit, res[1] = rank of the
 // element inside that bin. If the bins hold fewer than k elements res is left at
-// (0, 1). `itmp` is __shared__ int[kWaves].
+// (0, 1). itmp: int[NT/64].
+template <int NT = kBlock>
 __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsigned k, int* itmp,
                                                      unsigned* res) {
   const int t = threadIdx.x;
@@ -262,10 +271,10 @@ __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsig
     res[0] = 0u;
     res[1] = 1u;
   }
-  const int c = (int)hist[255 - t];
+  const int c = (t < 256) ? (int)hist[255 - t] : 0;
   int total;
-  const int above = block_excl_scan(c, itmp, total);  // elements in bins above 255-t
-  if ((unsigned)above < k && k <= (unsigned)(above + c)) {
+  const int above = block_excl_scan<NT>(c, itmp, total);  // elements in bins above 255-t
+  if (t < 256 && (unsigned)above < k && k <= (unsigned)(above + c)) {
     res[0] = (unsigned)(255 - t);
     res[1] = k - (unsigned)above;
   }
@@ -274,19 +283,31 @@ __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsig
 
 // The order key of the k-th largest of vals[0..n) among the values whose key
 // matches `prefix` on the bits of `mask`, resolving bits shift_start+7..0.
+// `vals` may point to global or shared memory.
+template <int NT = kBlock>
 __device__ __forceinline__ uint32_t radix_select_block(const float* vals, long long n, uint32_t prefix,
                                                        uint32_t mask, int shift_start, unsigned k,
                                                        unsigned* hist, int* itmp, unsigned* res) {
   const int tid = threadIdx.x;
   for (int shift = shift_start; shift >= 0; shift -= 8) {
-    hist[tid] = 0u;
+    for (int e = tid; e < 256; e += NT) hist[e] = 0u;
     __syncthreads();
-    for (long long i = tid; i < n; i += kBlock) {
-      const uint32_t u = order_key(vals[i]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    for (long long i0 = 0; i0 < n; i0 += 4LL * NT) {
+      float v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long i = i0 + (long long)u * NT + tid;
+        v4[u] = (i < n) ? vals[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long i = i0 + (long long)u * NT + tid;
+        const uint32_t key = order_key(v4[u]);
+        if (i < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
-    digit_of_kth_largest(hist, k, itmp, res);
+    digit_of_kth_largest<NT>(hist, k, itmp, res);
     prefix |= res[0] << shift;
     mask |= 255u << shift;
     k = res[1];

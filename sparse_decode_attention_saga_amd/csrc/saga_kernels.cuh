@@ -1,9 +1,13 @@
 // Kernels of the SAGA + Atop-N decode step and of the dense GQA baseline (gfx950).
 //
-// Steady step (threshold reused):  k_qk_select  ->  k_sparse_gather
-// Refresh step (exact threshold):  k_scores_hist -> k_threshold_select
-//                                   -> k_qk_select<from stored scores> -> k_sparse_gather
+// Steady step (threshold reused):  k_qk_select -> k_row_gather
+// Refresh step (exact threshold):  k_scores_hist -> k_cand_collect -> k_select_finish
+//                                   -> k_qk_select<from stored logits> -> k_row_gather
 // Dense GQA baseline:              k_dense_partial -> k_dense_combine
+//
+// Kernels never wait on each other inside a launch: every exchange between
+// workgroups goes through a kernel boundary (or a device-scope atomic counter that
+// only the next kernel reads).
 //
 // Paper: "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding"
 // (summary page picx.dev DRD92V): eq. (2) logits, section "Methodology > Atop-N
@@ -17,9 +21,13 @@
 namespace saga {
 
 // Keys per block of the key-streaming kernels: 4 waves x TPW tiles x 16 keys.
+#ifndef SAGA_KEY_BYTES_PER_WAVE
+#define SAGA_KEY_BYTES_PER_WAVE 16384  // K bytes one wave has in flight per chunk
+#endif
 template <typename T, int D> struct StreamCfg {
-  // ~16 KB of K per wave in flight: 4 x 16-byte loads per lane per tile at 256 B rows.
-  static constexpr int kTPW = (D * (int)sizeof(T) >= 512) ? 2 : (D * (int)sizeof(T) == 256 ? 4 : 8);
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kTPW = SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes);  // 16-key tiles per wave
+  static_assert(kTPW >= 1, "at least one tile per wave");
   static constexpr int kChunk = 16 * kTPW * kWaves;
 };
 
@@ -38,7 +46,6 @@ struct StreamArgs {
   float* chunk_max;        // [B*h_q, nch] largest kept logit per chunk
   unsigned* hist;          // [B*h_q, 256] top-digit histogram (zero between calls)
   unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
-  unsigned* done;          // [B*h_q] block counter of the threshold select (zero between calls)
   int h_q, h_k, g_k, htiles, l_max, nch, N;
   int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   long long lpad;
@@ -167,84 +174,122 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Refresh, pass 2: the exact threshold tau = N-th largest stored logit of each row
-// (counting repeats; -inf when N >= l_kv). Each block copies the logits of its slice
-// that fall in the top-digit bin holding the N-th largest into the row's candidate
-// list; the last block of the row resolves the remaining 24 bits on the candidates
-// and writes tau. It also returns the row's counters and histogram to zero.
+// Refresh, pass 2: candidates for the exact threshold. The top-digit histogram of a
+// row gives the 8-bit bin that holds its N-th largest logit; each block copies the
+// logits of its slice that fall in that bin to the row's candidate list (stored in
+// the row's kept-logit buffer, free at this point of a refresh step).
 // grid = (P, h_q, B) with P = ceil(max_l_kv / kSelSlice), block = 256.
-constexpr int kSelSlice = 4096;
+constexpr int kSelSlice = 4096;   // logits scanned per block
+constexpr int kCandLds = 8192;    // candidates the finishing block stages in LDS
+constexpr int kRowThreads = 1024; // threads of the one-block-per-row kernels
 
-__global__ __launch_bounds__(kBlock) void k_threshold_select(const StreamArgs a, float* tau_out) {
+__global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int row = b * a.h_q + j;
+  const long long row = (long long)b * a.h_q + j;
   const int L = min(a.l_kv[b], a.max_l_kv);
   const int N = a.N;
   const int tid = threadIdx.x;
-  const long long rbase = (long long)row * a.lpad;
+  const int lo = p * kSelSlice;
+  if (L <= 0 || N >= L || lo >= L) return;  // uniform over the block
+  const long long rbase = row * a.lpad;
 
   __shared__ unsigned s_hist[256];
   __shared__ int s_itmp[kWaves];
   __shared__ unsigned s_res[2];
   __shared__ float s_cand[kSelSlice];
-  __shared__ int s_cc, s_base, s_last;
+  __shared__ int s_cc, s_base;
 
-  const bool active = L > 0 && N < L;
-  unsigned d1 = 0u, k1 = 1u;
-  if (active) {
-    s_hist[tid] = a.hist[(long long)row * 256 + tid];
-    if (tid == 0) s_cc = 0;
-    __syncthreads();
-    digit_of_kth_largest(s_hist, (unsigned)N, s_itmp, s_res);
-    d1 = s_res[0];
-    k1 = s_res[1];
-    const int lo = p * kSelSlice, hi = min(lo + kSelSlice, L);
-    for (int i = lo + tid; i < hi; i += kBlock) {
-      const float v = a.scores[rbase + i];
-      if ((order_key(v) >> 24) == d1) s_cand[atomicAdd(&s_cc, 1)] = v;
+  s_hist[tid] = a.hist[row * 256 + tid];
+  if (tid == 0) s_cc = 0;
+  __syncthreads();
+  digit_of_kth_largest(s_hist, (unsigned)N, s_itmp, s_res);
+  const unsigned d1 = s_res[0];
+  const int hi = min(lo + kSelSlice, L);
+  constexpr int PER = kSelSlice / kBlock;
+  float vals[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = lo + u * kBlock + tid;
+    vals[u] = (i < hi) ? a.scores[rbase + i] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = lo + u * kBlock + tid;
+    if (i < hi && (order_key(vals[u]) >> 24) == d1) s_cand[atomicAdd(&s_cc, 1)] = vals[u];
+  }
+  __syncthreads();
+  const int cnt = s_cc;
+  if (tid == 0 && cnt > 0) s_base = (int)atomicAdd(&a.cand_cnt[row], (unsigned)cnt);
+  __syncthreads();
+  for (int i = tid; i < cnt; i += kBlock) a.surv_val[rbase + s_base + i] = s_cand[i];
+}
+
+// Refresh, pass 3: the remaining 24 bits of the N-th largest logit resolved on the
+// candidates (counting repeats); writes tau (-inf when N >= l_kv, unchanged when
+// l_kv == 0) and returns the row's histogram and candidate count to zero.
+// grid = (h_q, B), block = 1024.
+__global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs a, float* tau_out) {
+  constexpr int NT = kRowThreads;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const long long row = (long long)b * a.h_q + j;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int N = a.N;
+  const int tid = threadIdx.x;
+  if (L <= 0) return;
+
+  __shared__ unsigned s_hist[256];
+  __shared__ int s_itmp[NT / kWave];
+  __shared__ unsigned s_res[2];
+  __shared__ float s_cand[kCandLds];
+
+  if (N >= L) {
+    if (tid == 0) tau_out[row] = -INFINITY;
+    if (tid < 256) a.hist[row * 256 + tid] = 0u;
+    return;
+  }
+  if (tid < 256) s_hist[tid] = a.hist[row * 256 + tid];
+  __syncthreads();
+  digit_of_kth_largest<NT>(s_hist, (unsigned)N, s_itmp, s_res);
+  const unsigned d1 = s_res[0], k1 = s_res[1];
+  const unsigned C = a.cand_cnt[row];
+  const float* cand = a.surv_val + row * a.lpad;
+  if (C <= (unsigned)kCandLds) {
+    for (int i0 = 0; i0 < (int)C; i0 += 4 * NT) {
+      float t4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        t4[u] = (i < (int)C) ? cand[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        if (i < (int)C) s_cand[i] = t4[u];
+      }
     }
     __syncthreads();
-    const int cnt = s_cc;
-    if (tid == 0 && cnt > 0) s_base = (int)atomicAdd(&a.cand_cnt[row], (unsigned)cnt);
-    __syncthreads();
-    for (int i = tid; i < cnt; i += kBlock) a.surv_val[rbase + s_base + i] = s_cand[i];
+    cand = s_cand;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.done[row], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (L > 0) {
-    float tau = -INFINITY;
-    if (active) {
-      const unsigned C = __hip_atomic_load(&a.cand_cnt[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t u = radix_select_block(a.surv_val + rbase, (long long)C, d1 << 24, 0xff000000u, 16, k1,
-                                            s_hist, s_itmp, s_res);
-      tau = order_key_to_f32(u);
-    }
-    if (tid == 0) tau_out[row] = tau;
-  }
-  a.hist[(long long)row * 256 + tid] = 0u;
+  const uint32_t key = radix_select_block<NT>(cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist,
+                                              s_itmp, s_res);
   if (tid == 0) {
+    tau_out[row] = order_key_to_f32(key);
     a.cand_cnt[row] = 0u;
-    a.done[row] = 0u;
   }
+  if (tid < 256) a.hist[row * 256 + tid] = 0u;
 }
 
 // ----------------------------------------------------------------------------
 // Sparse softmax and value gather (eq. (7)) over the kept entries of one row.
 
 struct GatherArgs {
-  StreamArgs s;           // q, k, l_kv, scores, survivor lists, counts
+  StreamArgs s;           // q, k, l_kv, logit buffer, kept lists and counts
   const void* v;          // [B, h_v, l_max, D]
   float* tau;             // [B*h_q] (written only by a forced refresh)
   void* out;              // [B*h_q, D]
   int32_t* sel_count;     // [B*h_q] or null
   int32_t* sel_idx;       // [B*h_q, sel_cap] or null
   int32_t* flags;         // [B*h_q] or null
-  float* part;            // [B*h_q, S, D+4] per-block partials
-  unsigned* row_done;     // [B*h_q] block counter (zero between calls)
   int h_v, sel_cap, out_bf16, refreshed;
 };
 
@@ -254,57 +299,75 @@ __device__ __forceinline__ void store_out(const GatherArgs& a, long long row, in
   else reinterpret_cast<float*>(a.out)[row * D + d] = x;
 }
 
-// Accumulate w * V[i] over a list of (index, logit) pairs handed out to groups of G
-// lanes (one value row per group). acc gets this lane's EPL columns.
+// Work split of a value-row gather: groups of G lanes read one 16-byte slice each of
+// a D-wide row; NG groups per 1024-thread block.
 template <typename T, int D>
 struct RowGather {
-  static constexpr int EPL = Unpack<T>::kN;  // columns per lane (16 bytes)
+  static constexpr int EPL = Unpack<T>::kN;  // columns per lane
   static constexpr int G = D / EPL;          // lanes per value row
-  static constexpr int NG = kBlock / G;      // rows in flight per block pass
+  static constexpr int NG = kRowThreads / G; // rows in flight per block pass (x U)
+  static constexpr int U = 8;                // rows per group per pass
 };
 
-// Reduce the per-group accumulators of a block into s_red[0..D) (+ Z in s_red[D]).
+// Sum the per-lane accumulators of a 1024-thread block into s_red[0][0..D) and the
+// weight sums into s_z[0] (shuffles inside each wave, then one LDS pass).
 template <typename T, int D>
-__device__ __forceinline__ void reduce_groups(const float* acc, float z, float* s_red_big, float* s_out /*[D+1]*/) {
+__device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[D], float* s_z) {
   using RG = RowGather<T, D>;
-  const int tid = threadIdx.x, grp = tid / RG::G, gl = tid - grp * RG::G;
+  constexpr int NW = kRowThreads / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 #pragma unroll
-  for (int e = 0; e < RG::EPL; ++e) s_red_big[grp * (D + 1) + gl * RG::EPL + e] = acc[e];
-  if (gl == 0) s_red_big[grp * (D + 1) + D] = z;
+  for (int off = RG::G; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < RG::EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
+    z += __shfl_xor(z, off);
+  }
+  if (lane < RG::G) {
+#pragma unroll
+    for (int e = 0; e < RG::EPL; ++e) s_red[wv][lane * RG::EPL + e] = acc[e];
+  }
+  if (lane == 0) s_z[wv] = z;
   __syncthreads();
-  for (int col = tid; col <= D; col += kBlock) {
+  if (tid < D) {
     float x = 0.f;
-    for (int q = 0; q < RG::NG; ++q) x += s_red_big[q * (D + 1) + col];
-    s_out[col] = x;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x += s_red[w][tid];
+    s_red[0][tid] = x;  // each column is read and written by one thread only
+  }
+  if (tid == 0) {
+    float zz = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) zz += s_z[w];
+    s_z[0] = zz;
   }
   __syncthreads();
 }
 
-// Forced refresh of one row by a single block (a stale threshold kept nothing):
-// logits of every key of the row with the same tiles as the streaming kernels, the
-// exact N-th largest, then the sparse softmax-PV over the new selection.
+// Forced refresh of one row by its block (a stale threshold kept nothing): logits of
+// every key with the same tiles as the streaming kernels, the exact N-th largest,
+// then the sparse softmax-PV over the new selection.
 template <typename T, int D>
-__device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, float* s_red_big, float* s_out) {
+__device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, float (*s_red)[D], float* s_z) {
+  constexpr int NT = kRowThreads;
+  constexpr int NW = NT / kWave;
   constexpr int TPW = StreamCfg<T, D>::kTPW;
-  constexpr int CH = StreamCfg<T, D>::kChunk;
   using RG = RowGather<T, D>;
   const StreamArgs& s = a.s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const int row = b * s.h_q + j;
-  const long long rbase = (long long)row * s.lpad;
+  const long long row = (long long)b * s.h_q + j;
+  const long long rbase = row * s.lpad;
   const int g = j / s.g_k;
   const int jt = (j - g * s.g_k) / 16;
   const int j0 = g * s.g_k + jt * 16;
   const int nh = min(16, s.g_k - jt * 16);
   const int jj = j - j0;
 
-  // 1) logits of head j for all keys, into the row's score buffer
   {
     QK<T, D> qk;
     qk.load_q(reinterpret_cast<const T*>(s.q) + (size_t)(b * s.h_q + j0) * D, nh, lane);
     const T* kh = reinterpret_cast<const T*>(s.k) + (size_t)(b * s.h_k + g) * s.l_max * D;
     const int kq = lane >> 4;
-    for (int base = 0; base < L; base += CH) {
+    for (int base = 0; base < L; base += NW * 16 * TPW) {
       const int wbase = base + wv * 16 * TPW;
       if (wbase < L) {
         floatx4 sc[TPW];
@@ -324,23 +387,21 @@ __device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, flo
   __syncthreads();
 
   __shared__ unsigned s_hist[256];
-  __shared__ int s_itmp[kWaves];
+  __shared__ int s_itmp[NW];
   __shared__ unsigned s_res[2];
-  __shared__ float s_ftmp[kWaves];
-  __shared__ int s_list_i[kBlock];
-  __shared__ float s_list_v[kBlock];
+  __shared__ float s_ftmp[NW];
+  __shared__ int s_list_i[NT];
+  __shared__ float s_list_v[NT];
   __shared__ int s_n;
 
-  // 2) exact threshold and the row maximum
   const float* srow = s.scores + rbase;
   float tau = -INFINITY;
   if (s.N < L)
-    tau = order_key_to_f32(radix_select_block(srow, L, 0u, 0u, 24, (unsigned)s.N, s_hist, s_itmp, s_res));
+    tau = order_key_to_f32(radix_select_block<NT>(srow, L, 0u, 0u, 24, (unsigned)s.N, s_hist, s_itmp, s_res));
   float m = -INFINITY;
-  for (int i = tid; i < L; i += kBlock) m = fmaxf(m, srow[i]);
-  m = block_max(m, s_ftmp);
+  for (int i = tid; i < L; i += NT) m = fmaxf(m, srow[i]);
+  m = block_max<NT>(m, s_ftmp);
 
-  // 3) compare, compact 256 keys at a time, gather their value rows
   const int vh = (int)(((long long)j * a.h_v) / s.h_q);
   const int grp = tid / RG::G, gl = tid - grp * RG::G;
   const T* vbase = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_v + vh) * s.l_max * D + gl * RG::EPL;
@@ -349,7 +410,7 @@ __device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, flo
   for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
   float z = 0.f;
   int kept = 0;
-  for (int base = 0; base < L; base += kBlock) {
+  for (int base = 0; base < L; base += NT) {
     if (tid == 0) s_n = 0;
     __syncthreads();
     const int i = base + tid;
@@ -371,14 +432,13 @@ __device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, flo
 #pragma unroll
       for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
       z += w;
-      if (gl == 0 && a.sel_idx && kept + p < a.sel_cap) a.sel_idx[(long long)row * a.sel_cap + kept + p] = idx;
+      if (gl == 0 && a.sel_idx && kept + p < a.sel_cap) a.sel_idx[row * a.sel_cap + kept + p] = idx;
     }
     kept += n;
     __syncthreads();
   }
-  reduce_groups<T, D>(acc, z, s_red_big, s_out);
-  const float Z = s_out[D];
-  for (int d = tid; d < D; d += kBlock) store_out<D>(a, row, d, s_out[d] / Z);
+  reduce_rows<T, D>(acc, z, s_red, s_z);
+  if (tid < D) store_out<D>(a, row, tid, s_red[0][tid] / s_z[0]);
   if (tid == 0) {
     a.tau[row] = tau;
     if (a.sel_count) a.sel_count[row] = kept;
@@ -386,59 +446,60 @@ __device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, flo
   }
 }
 
-// grid = (S, h_q, B), block = 256. Block s of row (b, j) takes the kept entries of
-// chunks [s*nch_b/S, (s+1)*nch_b/S), computes their softmax numerator and value sum
-// relative to its own maximum, and writes a partial (m, Z, count, o[D]). The last
-// block of the row merges the S partials (log-sum-exp), writes the output row and
-// the optional index export, and runs the forced refresh if the row kept nothing.
+// One 1024-thread block per row (b, j): the kept entries of all its chunks (counts
+// and maxima from k_qk_select), softmax relative to the row maximum, and the gather
+// of the kept value rows of value head v(j) (U rows in flight per lane group).
+// grid = (h_q, B), block = 1024.
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock) void k_sparse_gather(const GatherArgs a) {
+__global__ __launch_bounds__(kRowThreads) void k_row_gather(const GatherArgs a) {
+  constexpr int NT = kRowThreads;
+  constexpr int NW = NT / kWave;
   constexpr int CH = StreamCfg<T, D>::kChunk;
   using RG = RowGather<T, D>;
+  constexpr int U = RG::U;
   const StreamArgs& sa = a.s;
-  const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int S = gridDim.x;
-  const int row = b * sa.h_q + j;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const long long row = (long long)b * sa.h_q + j;
   const int L = min(sa.l_kv[b], sa.max_l_kv);
   const int tid = threadIdx.x;
 
+  __shared__ int s_pref[NT + 1];
+  __shared__ int s_itmp[NW];
+  __shared__ float s_ftmp[NW];
+  __shared__ float s_red[NW][D];
+  __shared__ float s_z[NW];
+
   if (L <= 0) {
-    if (s == 0) {
-      for (int d = tid; d < D; d += kBlock) store_out<D>(a, row, d, 0.f);
-      if (tid == 0) {
-        if (a.sel_count) a.sel_count[row] = 0;
-        if (a.flags) a.flags[row] = 0;
-      }
+    if (tid < D) store_out<D>(a, row, tid, 0.f);
+    if (tid == 0) {
+      if (a.sel_count) a.sel_count[row] = 0;
+      if (a.flags) a.flags[row] = 0;
     }
     return;
   }
-
-  __shared__ int s_pref[kBlock + 1];
-  __shared__ int s_itmp[kWaves];
-  __shared__ float s_ftmp[kWaves];
-  __shared__ float s_red_big[RG::NG * (D + 1)];
-  __shared__ float s_out[D + 1];
-  __shared__ float s_w[64];
-  __shared__ int s_last;
-
-  const long long rbase = (long long)row * sa.lpad;
-  const long long cbase = (long long)row * sa.nch;
+  const long long rbase = row * sa.lpad;
+  const long long cbase = row * sa.nch;
   const int nch_b = (L + CH - 1) / CH;
-  const int c0 = (int)(((long long)nch_b * s) / S), c1 = (int)(((long long)nch_b * (s + 1)) / S);
+  const bool one_pass = nch_b <= NT;
 
-  // this block's maximum kept logit and count
   float m = -INFINITY;
-  int cnt_all = 0;
-  for (int cb = c0; cb < c1; cb += kBlock) {
+  int total = 0, n_keep = 0;
+  for (int cb = 0; cb < nch_b; cb += NT) {
     const int c = cb + tid;
-    if (c < c1) {
+    if (c < nch_b) {
       const int n = sa.chunk_cnt[cbase + c];
-      cnt_all += n;
-      if (n > 0) m = fmaxf(m, sa.chunk_max[cbase + c]);
+      const float mx = sa.chunk_max[cbase + c];
+      n_keep = n;
+      total += n;
+      m = fmaxf(m, n > 0 ? mx : -INFINITY);
     }
   }
-  m = block_max(m, s_ftmp);
-  cnt_all = block_sum_i(cnt_all, s_itmp);
+  m = block_max<NT>(m, s_ftmp);
+  total = block_sum_i<NT>(total, s_itmp);
+  if (total == 0) {
+    forced_refresh_row<T, D>(a, b, j, L, s_red, s_z);
+    return;
+  }
 
   const int vh = (int)(((long long)j * a.h_v) / sa.h_q);
   const int grp = tid / RG::G, gl = tid - grp * RG::G;
@@ -447,121 +508,59 @@ __global__ __launch_bounds__(kBlock) void k_sparse_gather(const GatherArgs a) {
 #pragma unroll
   for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
   float z = 0.f;
-
-  if (cnt_all > 0) {
-    for (int cb = c0; cb < c1; cb += kBlock) {
-      const int c = cb + tid;
-      const int n = (c < c1) ? sa.chunk_cnt[cbase + c] : 0;
-      int tot;
-      const int ex = block_excl_scan(n, s_itmp, tot);
-      s_pref[tid] = ex;
-      if (tid == kBlock - 1) s_pref[kBlock] = tot;
-      __syncthreads();
-      constexpr int U = 4;  // value rows in flight per group
-      for (int p0 = 0; p0 < tot; p0 += RG::NG * U) {
-        int idx[U];
-        float wv[U];
+  int done = 0;  // list positions of earlier chunk passes (index export order)
+  for (int cb = 0; cb < nch_b; cb += NT) {
+    const int c = cb + tid;
+    const int n = one_pass ? n_keep : ((c < nch_b) ? sa.chunk_cnt[cbase + c] : 0);
+    int tot;
+    const int ex = block_excl_scan<NT>(n, s_itmp, tot);
+    s_pref[tid] = ex;
+    if (tid == NT - 1) s_pref[NT] = tot;
+    __syncthreads();
+    for (int p0 = 0; p0 < tot; p0 += RG::NG * U) {
+      int idx[U];
+      float lv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int p = p0 + u * RG::NG + grp;
-          idx[u] = -1;
-          wv[u] = 0.f;
-          if (p < tot) {
-            int lo = 0, hi = kBlock;
-            while (hi - lo > 1) {
-              const int mid = (lo + hi) >> 1;
-              if (s_pref[mid] <= p) lo = mid; else hi = mid;
-            }
-            const long long off = rbase + (long long)(cb + lo) * CH + (p - s_pref[lo]);
-            idx[u] = sa.surv_idx[off];
-            wv[u] = sa.surv_val[off];
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * RG::NG + grp;
+        idx[u] = -1;
+        lv[u] = 0.f;
+        if (p < tot) {
+          int lo = 0, hi = NT;  // largest lo with s_pref[lo] <= p: the chunk holding p
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= p) lo = mid; else hi = mid;
           }
-        }
-        uint4 vr[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) vr[u] = (idx[u] >= 0) ? ld16(vbase + (size_t)idx[u] * D) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (idx[u] >= 0) {
-            const float w = expf(wv[u] - m);
-            float x[RG::EPL];
-            Unpack<T>::run(vr[u], x);
-#pragma unroll
-            for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
-            z += w;
-          }
+          const long long off = rbase + (long long)(cb + lo) * CH + (p - s_pref[lo]);
+          idx[u] = sa.surv_idx[off];
+          lv[u] = sa.surv_val[off];
         }
       }
-      __syncthreads();
+      uint4 vr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) vr[u] = (idx[u] >= 0) ? ld16(vbase + (size_t)idx[u] * D) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (idx[u] >= 0) {
+          const float w = expf(lv[u] - m);
+          float x[RG::EPL];
+          Unpack<T>::run(vr[u], x);
+#pragma unroll
+          for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
+          z += w;
+          const int pos = done + p0 + u * RG::NG + grp;
+          if (gl == 0 && a.sel_idx && pos < a.sel_cap) a.sel_idx[row * a.sel_cap + pos] = idx[u];
+        }
+      }
     }
+    done += tot;
+    __syncthreads();
   }
-  reduce_groups<T, D>(acc, z, s_red_big, s_out);
-
-  float* part = a.part + ((long long)row * S + s) * (D + 4);
-  for (int d = tid; d < D; d += kBlock) part[4 + d] = s_out[d];
-  if (tid == 0) {
-    part[0] = m;
-    part[1] = s_out[D];
-    part[2] = __int_as_float(cnt_all);
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.row_done[row], 1u) == (unsigned)(S - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // merge the S partials of the row
-  const float* rp = a.part + (long long)row * S * (D + 4);
-  float mm = -INFINITY;
-  int total = 0;
-  if (tid < S) {
-    const int n = __float_as_int(rp[(long long)tid * (D + 4) + 2]);
-    total = n;
-    if (n > 0) mm = rp[(long long)tid * (D + 4)];
-  }
-  const float M = block_max(mm, s_ftmp);
-  total = block_sum_i(total, s_itmp);
-  if (tid == 0) a.row_done[row] = 0u;
-
-  if (total == 0) {
-    forced_refresh_row<T, D>(a, b, j, L, s_red_big, s_out);
-    return;
-  }
-  float zz = 0.f;
-  if (tid < S) {
-    const int n = __float_as_int(rp[(long long)tid * (D + 4) + 2]);
-    const float w = (n > 0) ? expf(rp[(long long)tid * (D + 4)] - M) : 0.f;
-    s_w[tid] = w;
-    zz = w * rp[(long long)tid * (D + 4) + 1];
-  }
-  const float Z = block_sum(zz, s_ftmp);  // also orders s_w before use
-  for (int d = tid; d < D; d += kBlock) {
-    float o = 0.f;
-    for (int q = 0; q < S; ++q) {
-      const float w = s_w[q];
-      if (w != 0.f) o += w * rp[(long long)q * (D + 4) + 4 + d];
-    }
-    store_out<D>(a, row, d, o / Z);
-  }
+  reduce_rows<T, D>(acc, z, s_red, s_z);
+  if (tid < D) store_out<D>(a, row, tid, s_red[0][tid] / s_z[0]);
   if (tid == 0) {
     if (a.sel_count) a.sel_count[row] = total;
     if (a.flags) a.flags[row] = a.refreshed ? 1 : 0;
-  }
-  // optional export of the kept indices (list order: chunk order)
-  if (a.sel_idx) {
-    int written = 0;
-    for (int cb = 0; cb < nch_b && written < a.sel_cap; cb += kBlock) {
-      const int c = cb + tid;
-      const int n = (c < nch_b) ? sa.chunk_cnt[cbase + c] : 0;
-      int tot;
-      const int ex = block_excl_scan(n, s_itmp, tot);
-      for (int t = 0; t < n; ++t) {
-        const int pos = written + ex + t;
-        if (pos < a.sel_cap) a.sel_idx[(long long)row * a.sel_cap + pos] = sa.surv_idx[rbase + (long long)c * CH + t];
-      }
-      written += tot;
-    }
   }
 }
 
@@ -708,50 +707,66 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   }
 }
 
-// Log-sum-exp merge of the chunk partials of each row (b, j).
-// grid = (D / 32, h_q, B), block = 256 = 32 columns x 8 chunk subsets.
+// Log-sum-exp merge of the chunk partials of each row (b, j). Thread t takes chunks
+// t, t+256, ... and 16 columns (four 16-byte loads per chunk).
+// grid = (D / 16, h_q, B), block = 256.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_dense_combine(const DenseArgs a, int chd) {
   const int cg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int row = b * a.h_q + j;
+  const long long row = (long long)b * a.h_q + j;
   const int L = min(a.l_kv[b], a.max_l_kv);
-  const int tid = threadIdx.x;
-  const int col = cg * 32 + (tid & 31), sub = tid >> 5;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   __shared__ float s_ftmp[kWaves];
-  __shared__ float s_acc[8][33];
+  __shared__ float s_acc[kWaves][17];
   if (L <= 0) {
-    if (tid < 32) {
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(long long)row * D + col] = 0;
-      else reinterpret_cast<float*>(a.out)[(long long)row * D + col] = 0.f;
+    if (tid < 16) {
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[row * D + cg * 16 + tid] = 0;
+      else reinterpret_cast<float*>(a.out)[row * D + cg * 16 + tid] = 0.f;
     }
     return;
   }
   const int nch_b = (L + chd - 1) / chd;
-  const float* rp = a.part + (long long)row * a.nchd * (D + 4);
+  const float* rp = a.part + row * a.nchd * (D + 4);
   float m = -INFINITY;
   for (int c = tid; c < nch_b; c += kBlock) m = fmaxf(m, rp[(long long)c * (D + 4)]);
   const float M = block_max(m, s_ftmp);
-  float o = 0.f, z = 0.f;
-#pragma unroll 8
-  for (int c = sub; c < nch_b; c += 8) {
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  float z = 0.f;
+  for (int c = tid; c < nch_b; c += kBlock) {
     const float* pc = rp + (long long)c * (D + 4);
     const float w = expf(pc[0] - M);
-    o += w * pc[4 + col];
     z += w * pc[1];
+    const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + cg * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = p4[q];
+      o[4 * q] += w * x.x;
+      o[4 * q + 1] += w * x.y;
+      o[4 * q + 2] += w * x.z;
+      o[4 * q + 3] += w * x.w;
+    }
   }
-  s_acc[sub][tid & 31] = o;
-  if ((tid & 31) == 0) s_acc[sub][32] = z;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = wave_sum(o[e]);
+  z = wave_sum(z);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_acc[wv][e] = o[e];
+    s_acc[wv][16] = z;
+  }
   __syncthreads();
-  if (tid < 32) {
+  if (tid < 16) {
     float oo = 0.f, zz = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      oo += s_acc[q][tid];
-      zz += s_acc[q][32];
+    for (int w = 0; w < kWaves; ++w) {
+      oo += s_acc[w][tid];
+      zz += s_acc[w][16];
     }
     const float x = oo / zz;
-    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(long long)row * D + col] = f32_to_bf16(x);
-    else reinterpret_cast<float*>(a.out)[(long long)row * D + col] = x;
+    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[row * D + cg * 16 + tid] = f32_to_bf16(x);
+    else reinterpret_cast<float*>(a.out)[row * D + cg * 16 + tid] = x;
   }
 }
 
