@@ -12,8 +12,9 @@ serving repeated reads, as a model's per-layer caches would. The K timed steps a
 replayed from a HIP graph and timed with HIP events on the launch stream.
 
 Prints one JSON line. `value` = SAGA decode steps/s; `roofline` is for the dominant
-kernel (the K-streaming select kernel, timed alone the same way); `cpu_baseline` is
-the CPU oracle timed on this host on the same workload.
+kernel (the fused steady-step kernel, timed alone the same way: a step that reuses
+the threshold is exactly one launch of it); `cpu_baseline` is the CPU oracle timed on
+this host on the same workload.
 """
 from __future__ import annotations
 
@@ -129,7 +130,7 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: >= 1 GiB of K)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "saga", "dense", "select"], default="all",
+    ap.add_argument("--only", choices=["all", "saga", "dense", "steady"], default="all",
                     help="time only one part (for profiler runs)")
     ap.add_argument("--probe", choices=["none", "copy"], default="none",
                     help="copy: time a plain device copy of 256 MiB (counter calibration, streaming ceiling)")
@@ -182,9 +183,11 @@ def main() -> int:
         api.decode_attn(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, refresh_period=w.refresh_period,
                         step=t, max_l_kv=L, out=out, workspace=ws)
 
-    def select_step(t):
+    def steady_step(t):
+        # a step that reuses the threshold: exactly one launch of the fused kernel
         r = t % R
-        api.qk_select(qs[r], ks[r], l_kv, taus[r], max_l_kv=L, workspace=ws)
+        api.decode_attn(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, refresh_period=1 << 30,
+                        step=1 + t, max_l_kv=L, out=out, workspace=ws)
 
     K, W = args.steps, args.warmup
     res = {}
@@ -197,10 +200,10 @@ def main() -> int:
         res["saga_ms_all"] = ms
         res["refresh_steps"] = sum(1 for t in range(W, W + K) if t % w.refresh_period == 0)
         log(f"saga: {1e3 * res['saga_ms'] / K:.2f} us/step over {K} steps ({res['refresh_steps']} refresh)")
-    if args.only in ("all", "select"):
-        ms = time_graph(torch, lambda: [select_step(t) for t in range(W, W + K)], args.reps)
-        res["select_ms"] = median(ms)
-        log(f"select kernel: {1e3 * res['select_ms'] / K:.2f} us/launch")
+    if args.only in ("all", "steady"):
+        ms = time_graph(torch, lambda: [steady_step(t) for t in range(W, W + K)], args.reps)
+        res["steady_ms"] = median(ms)
+        log(f"fused steady-step kernel: {1e3 * res['steady_ms'] / K:.2f} us/launch")
 
     # survivor statistics at a stale step of set 0 (union of kept rows per value head)
     cap = 8 * w.N
@@ -249,15 +252,15 @@ def main() -> int:
         del kd, vd
 
     if "saga_ms" not in res:
-        print(json.dumps({"metric": METRIC, "partial": args.only, "select_ms": res.get("select_ms"),
+        print(json.dumps({"metric": METRIC, "partial": args.only, "steady_ms": res.get("steady_ms"),
                           "dense": dense}))
         return 0
 
     t_step = res["saga_ms"] / K * 1e-3
     bytes_step = bytes_k + bytes_v
     step_gbs = bytes_step / t_step / 1e9
-    sel_s = res["select_ms"] / K * 1e-3 if "select_ms" in res else None
-    achieved = bytes_k / sel_s / 1e9 if sel_s else None
+    st_s = res["steady_ms"] / K * 1e-3 if "steady_ms" in res else None
+    achieved = bytes_step / st_s / 1e9 if st_s else None
     line = {
         "metric": METRIC,
         "value": 1.0 / t_step,
@@ -285,10 +288,10 @@ def main() -> int:
         "survivors_mean": float(counts.mean()),
         "survivors_max": int(counts.max()),
         "saga_ms_replays": res["saga_ms_all"],
-        "roofline": {"kernel": "k_qk_select (K stream, a1+a2)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"kernel": "k_decode_fused (steady step: K stream, compare, V gather, merge)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
-                     "kernel_us": sel_s * 1e6 if sel_s else None, "bytes_per_launch": bytes_k},
+                     "kernel_us": st_s * 1e6 if st_s else None, "bytes_per_launch": bytes_step},
     }
     if dense:
         td = dense["ms"] / K * 1e-3

@@ -1,13 +1,13 @@
 // Kernels of the SAGA + Atop-N decode step and of the dense GQA baseline (gfx950).
 //
-// Steady step (threshold reused):  k_qk_select -> k_row_gather
-// Refresh step (exact threshold):  k_scores_hist -> k_cand_collect -> k_select_finish
-//                                   -> k_qk_select<from stored logits> -> k_row_gather
-// Dense GQA baseline:              k_dense_partial -> k_dense_combine
+// Stale-threshold step:  k_qk_select -> k_gather_split
+// Refresh step:          k_scores_hist -> k_cand_collect -> k_select_finish
+//                        -> k_qk_select<from stored logits> -> k_gather_split
+// Dense GQA baseline:    k_dense_partial -> k_dense_combine
 //
-// Kernels never wait on each other inside a launch: every exchange between
-// workgroups goes through a kernel boundary (or a device-scope atomic counter that
-// only the next kernel reads).
+// No kernel waits on another workgroup: exchanges go through kernel boundaries, or
+// through device-scope atomics whose last arrival finishes the work (device-scope
+// fences are avoided: on this GPU they write back and invalidate the whole L2).
 //
 // Paper: "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding"
 // (summary page picx.dev DRD92V): eq. (2) logits, section "Methodology > Atop-N
@@ -26,10 +26,13 @@ namespace saga {
 #endif
 template <typename T, int D> struct StreamCfg {
   static constexpr int kRowBytes = D * (int)sizeof(T);
-  static constexpr int kTPW = SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes);  // 16-key tiles per wave
+  static constexpr int kTPW = SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) > 0 ? SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) : 1;  // 16-key tiles per wave
   static_assert(kTPW >= 1, "at least one tile per wave");
   static constexpr int kChunk = 16 * kTPW * kWaves;
 };
+
+constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 for raw gfx9 buffers
+constexpr int kCoherent = 16;           // sc1 cache policy: coherent across the device's L2s
 
 // ----------------------------------------------------------------------------
 // Shared argument blocks (passed by value).
@@ -50,30 +53,52 @@ struct StreamArgs {
   int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   long long lpad;
   float scale;
+  float* zero_f;           // k_qk_select clears [zero_n] floats here (the gather's accumulators)
+  long long zero_n;
 };
+
+// Source of the logits of k_qk_select.
+enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 
 // ----------------------------------------------------------------------------
 // Logits of one chunk of keys for the (up to) 16 query heads of one head tile, then
 // the Atop-N comparison against each head's threshold. Kept (index, logit) pairs go
-// to the chunk's segment of the row's survivor list; the chunk's count and largest
-// kept logit are recorded. FROM_SCORES reads the logits stored by k_scores_hist
-// instead of recomputing them from K (refresh steps: the same fp32 values the
-// threshold was selected from).
+// to the chunk's segment of the row's kept list; the chunk's count and largest kept
+// logit are recorded. MODE kFromScores reads the logits stored by k_scores_hist (a
+// refresh step: the fp32 values the threshold was selected from); MODE
+// kFromKeysSpeculative (one sequence) issues the key loads before l_kv arrives.
+// Every block also clears its share of the gather's accumulators.
 // grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D, bool FROM_SCORES>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
   constexpr int CH = StreamCfg<T, D>::kChunk;
   const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
-  const int L = min(a.l_kv[b], a.max_l_kv);
-  const int base = c * CH;
-  if (base >= L) return;
   const int g = gy / a.htiles, ht = gy - g * a.htiles;
   const int j0 = g * a.g_k + ht * 16;
   const int nh = min(16, a.g_k - ht * 16);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int hh = lane & 15, kq = lane >> 4;
   const int row0 = b * a.h_q + j0;
+  const int base = c * CH;
+  const int wbase = base + wv * 16 * TPW;
+  const bool live = hh < nh;
+
+  floatx4 sc[TPW];
+  QK<T, D> qk;
+  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_k + g) * a.l_max * D;
+  if constexpr (MODE == kFromKeysSpeculative) {
+    qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
+    score_tiles<T, D, TPW>(sc, qk, kh, wbase, a.max_l_kv, lane, a.scale);
+  }
+  {
+    const long long nblk = (long long)gridDim.x * gridDim.y * gridDim.z;
+    const long long id = blockIdx.x + (long long)gridDim.x * (blockIdx.y + (long long)gridDim.y * blockIdx.z);
+    const long long per = (a.zero_n + nblk - 1) / nblk;
+    for (long long i = id * per + tid; i < min(a.zero_n, (id + 1) * per); i += kBlock) a.zero_f[i] = 0.f;
+  }
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  if (base >= L) return;
 
   __shared__ int s_cnt[16];
   __shared__ unsigned s_max[16];
@@ -81,19 +106,13 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     s_cnt[tid] = 0;
     s_max[tid] = 0u;
   }
-  const bool live = hh < nh;
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
-  const int wbase = base + wv * 16 * TPW;
-
-  floatx4 sc[TPW];
-  if constexpr (FROM_SCORES) {
+  if constexpr (MODE == kFromScores) {
     const float* srow = a.scores + (long long)(row0 + (live ? hh : 0)) * a.lpad;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) sc[t] = *reinterpret_cast<const floatx4*>(srow + wbase + 16 * t + 4 * kq);
-  } else {
-    QK<T, D> qk;
+  } else if constexpr (MODE == kFromKeys) {
     qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
-    const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_k + g) * a.l_max * D;
     score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
   }
   __syncthreads();
@@ -104,12 +123,12 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = wbase + 16 * t + 4 * kq + r;
-      const float s = sc[t][r];
-      if (live && key < L && s >= tau_l) {
+      const float v = sc[t][r];
+      if (live && key < L && v >= tau_l) {
         const int slot = atomicAdd(&s_cnt[hh], 1);
         a.surv_idx[seg + slot] = key;
-        a.surv_val[seg + slot] = s;
-        atomicMax(&s_max[hh], order_key(s));
+        a.surv_val[seg + slot] = v;
+        atomicMax(&s_max[hh], order_key(v));
       }
     }
   }
@@ -285,12 +304,14 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
 struct GatherArgs {
   StreamArgs s;           // q, k, l_kv, logit buffer, kept lists and counts
   const void* v;          // [B, h_v, l_max, D]
-  float* tau;             // [B*h_q] (written only by a forced refresh)
+  float* tau;             // [B*h_q] (written only where a row is refreshed)
   void* out;              // [B*h_q, D]
   int32_t* sel_count;     // [B*h_q] or null
   int32_t* sel_idx;       // [B*h_q, sel_cap] or null
   int32_t* flags;         // [B*h_q] or null
   int h_v, sel_cap, out_bf16, refreshed;
+  float* acc;             // [B*h_q][D+4] sum of w*v (D), sum of w; cleared by k_qk_select
+  unsigned* row_done;     // [B*h_q] finished blocks per row; cleared by k_qk_select
 };
 
 template <int D>
@@ -300,21 +321,21 @@ __device__ __forceinline__ void store_out(const GatherArgs& a, long long row, in
 }
 
 // Work split of a value-row gather: groups of G lanes read one 16-byte slice each of
-// a D-wide row; NG groups per 1024-thread block.
-template <typename T, int D>
+// a D-wide row; NG groups per block of NT threads.
+template <typename T, int D, int NT>
 struct RowGather {
   static constexpr int EPL = Unpack<T>::kN;  // columns per lane
   static constexpr int G = D / EPL;          // lanes per value row
-  static constexpr int NG = kRowThreads / G; // rows in flight per block pass (x U)
+  static constexpr int NG = NT / G;          // rows in flight per block pass (x U)
   static constexpr int U = 8;                // rows per group per pass
 };
 
-// Sum the per-lane accumulators of a 1024-thread block into s_red[0][0..D) and the
-// weight sums into s_z[0] (shuffles inside each wave, then one LDS pass).
-template <typename T, int D>
+// Sum the per-lane accumulators of a block into s_red[0][0..D) and the weight sums
+// into s_z[0] (shuffles inside each wave, then one LDS pass). s_red: [NT/64][D].
+template <typename T, int D, int NT>
 __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[D], float* s_z) {
-  using RG = RowGather<T, D>;
-  constexpr int NW = kRowThreads / kWave;
+  using RG = RowGather<T, D, NT>;
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 #pragma unroll
   for (int off = RG::G; off < kWave; off <<= 1) {
@@ -328,11 +349,11 @@ __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[
   }
   if (lane == 0) s_z[wv] = z;
   __syncthreads();
-  if (tid < D) {
+  for (int col = tid; col < D; col += NT) {
     float x = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) x += s_red[w][tid];
-    s_red[0][tid] = x;  // each column is read and written by one thread only
+    for (int w = 0; w < NW; ++w) x += s_red[w][col];
+    s_red[0][col] = x;  // each column is read and written by one thread only
   }
   if (tid == 0) {
     float zz = 0.f;
@@ -343,15 +364,18 @@ __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[
   __syncthreads();
 }
 
-// Forced refresh of one row by its block (a stale threshold kept nothing): logits of
-// every key with the same tiles as the streaming kernels, the exact N-th largest,
-// then the sparse softmax-PV over the new selection.
-template <typename T, int D>
-__device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, float (*s_red)[D], float* s_z) {
-  constexpr int NT = kRowThreads;
+// One row (b, j) computed exactly by one block: the logits of every key with the same
+// tiles as the streaming kernels (into the row's logit buffer), optionally the exact
+// N-th largest as a new threshold (a forced refresh), then the kept set, its maximum
+// and the sparse softmax-PV. Used where the fast paths cannot answer: a stale
+// threshold that keeps nothing, or a logit range too wide for the fixed-reference
+// accumulation. Writes out, tau (refresh only), sel_count, sel_idx and flags.
+template <typename T, int D, int NT>
+__device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh_tau, float (*s_red)[D],
+                          float* s_z) {
   constexpr int NW = NT / kWave;
   constexpr int TPW = StreamCfg<T, D>::kTPW;
-  using RG = RowGather<T, D>;
+  using RG = RowGather<T, D, NT>;
   const StreamArgs& s = a.s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const long long row = (long long)b * s.h_q + j;
@@ -395,11 +419,17 @@ __device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, flo
   __shared__ int s_n;
 
   const float* srow = s.scores + rbase;
-  float tau = -INFINITY;
-  if (s.N < L)
-    tau = order_key_to_f32(radix_select_block<NT>(srow, L, 0u, 0u, 24, (unsigned)s.N, s_hist, s_itmp, s_res));
+  float tau = a.tau[row];
+  if (refresh_tau) {
+    tau = -INFINITY;
+    if (s.N < L)
+      tau = order_key_to_f32(radix_select_block<NT>(srow, L, 0u, 0u, 24, (unsigned)s.N, s_hist, s_itmp, s_res));
+  }
   float m = -INFINITY;
-  for (int i = tid; i < L; i += NT) m = fmaxf(m, srow[i]);
+  for (int i = tid; i < L; i += NT) {
+    const float v = srow[i];
+    if (v >= tau) m = fmaxf(m, v);
+  }
   m = block_max<NT>(m, s_ftmp);
 
   const int vh = (int)(((long long)j * a.h_v) / s.h_q);
@@ -437,69 +467,95 @@ __device__ void forced_refresh_row(const GatherArgs& a, int b, int j, int L, flo
     kept += n;
     __syncthreads();
   }
-  reduce_rows<T, D>(acc, z, s_red, s_z);
-  if (tid < D) store_out<D>(a, row, tid, s_red[0][tid] / s_z[0]);
+  reduce_rows<T, D, NT>(acc, z, s_red, s_z);
+  for (int d = tid; d < D; d += NT) store_out<D>(a, row, d, kept > 0 ? s_red[0][d] / s_z[0] : 0.f);
   if (tid == 0) {
-    a.tau[row] = tau;
+    if (refresh_tau) a.tau[row] = tau;
     if (a.sel_count) a.sel_count[row] = kept;
-    if (a.flags) a.flags[row] = 3;
+    if (a.flags) a.flags[row] = refresh_tau ? 3 : (a.refreshed ? 1 : 0);
   }
+  __syncthreads();
 }
 
-// One 1024-thread block per row (b, j): the kept entries of all its chunks (counts
-// and maxima from k_qk_select), softmax relative to the row maximum, and the gather
-// of the kept value rows of value head v(j) (U rows in flight per lane group).
-// grid = (h_q, B), block = 1024.
+// Split gather: P blocks per row (b, j). Every block reads the row's chunk counts
+// and maxima (so all use the row maximum m as the softmax reference and their sums
+// add directly), takes list positions [T*s/P, T*(s+1)/P) of the row's kept list
+// (chunk order), gathers those value rows of value head v(j) and adds its sum of
+// w*v and of w, w = exp(A - m), to the row's accumulator (device-scope atomics,
+// fan-in P). The last of the P blocks to finish divides and writes the row. A row
+// that kept nothing is recomputed exactly by block 0 (forced refresh).
+// grid = (P, h_q, B), block = 256.
+constexpr int kSplitWindow = 1024;  // list positions a block stages in LDS per pass
+constexpr int kChunkRegs = 8;       // chunk counts a thread keeps in registers
+
 template <typename T, int D>
-__global__ __launch_bounds__(kRowThreads) void k_row_gather(const GatherArgs a) {
-  constexpr int NT = kRowThreads;
+__global__ __launch_bounds__(kBlock) void k_gather_split(const GatherArgs a) {
+  constexpr int NT = kBlock;
   constexpr int NW = NT / kWave;
   constexpr int CH = StreamCfg<T, D>::kChunk;
-  using RG = RowGather<T, D>;
-  constexpr int U = RG::U;
+  constexpr int AS = D + 4;
+  using RG = RowGather<T, D, NT>;
+  constexpr int U = 4;
   const StreamArgs& sa = a.s;
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int P = gridDim.x;
   const long long row = (long long)b * sa.h_q + j;
   const int L = min(sa.l_kv[b], sa.max_l_kv);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 
-  __shared__ int s_pref[NT + 1];
   __shared__ int s_itmp[NW];
   __shared__ float s_ftmp[NW];
+  __shared__ int s_li[kSplitWindow];
+  __shared__ float s_lv[kSplitWindow];
   __shared__ float s_red[NW][D];
   __shared__ float s_z[NW];
+  __shared__ int s_last;
 
   if (L <= 0) {
-    if (tid < D) store_out<D>(a, row, tid, 0.f);
-    if (tid == 0) {
-      if (a.sel_count) a.sel_count[row] = 0;
-      if (a.flags) a.flags[row] = 0;
+    if (s == 0) {
+      for (int d = tid; d < D; d += NT) store_out<D>(a, row, d, 0.f);
+      if (tid == 0) {
+        if (a.sel_count) a.sel_count[row] = 0;
+        if (a.flags) a.flags[row] = 0;
+      }
     }
     return;
   }
   const long long rbase = row * sa.lpad;
   const long long cbase = row * sa.nch;
   const int nch_b = (L + CH - 1) / CH;
-  const bool one_pass = nch_b <= NT;
+  const int cpt = (nch_b + NT - 1) / NT;  // consecutive chunks per thread
+  const int c0 = tid * cpt, c1 = min(nch_b, c0 + cpt);
 
+  // counts and maxima of this thread's chunks (kept in registers when few)
+  int nreg[kChunkRegs];
   float m = -INFINITY;
-  int total = 0, n_keep = 0;
-  for (int cb = 0; cb < nch_b; cb += NT) {
-    const int c = cb + tid;
-    if (c < nch_b) {
+  int tsum = 0;
+#pragma unroll
+  for (int k = 0; k < kChunkRegs; ++k) {
+    const int c = c0 + k;
+    nreg[k] = 0;
+    if (c < c1) {
       const int n = sa.chunk_cnt[cbase + c];
       const float mx = sa.chunk_max[cbase + c];
-      n_keep = n;
-      total += n;
+      nreg[k] = n;
+      tsum += n;
       m = fmaxf(m, n > 0 ? mx : -INFINITY);
     }
   }
+  for (int c = c0 + kChunkRegs; c < c1; ++c) {
+    const int n = sa.chunk_cnt[cbase + c];
+    tsum += n;
+    if (n > 0) m = fmaxf(m, sa.chunk_max[cbase + c]);
+  }
   m = block_max<NT>(m, s_ftmp);
-  total = block_sum_i<NT>(total, s_itmp);
+  int total;
+  const int tpre = block_excl_scan<NT>(tsum, s_itmp, total);
   if (total == 0) {
-    forced_refresh_row<T, D>(a, b, j, L, s_red, s_z);
+    if (s == 0) exact_row<T, D, NT>(a, b, j, L, true, s_red, s_z);
     return;
   }
+  const int lo = (int)(((long long)total * s) / P), hi = (int)(((long long)total * (s + 1)) / P);
 
   const int vh = (int)(((long long)j * a.h_v) / sa.h_q);
   const int grp = tid / RG::G, gl = tid - grp * RG::G;
@@ -508,56 +564,85 @@ __global__ __launch_bounds__(kRowThreads) void k_row_gather(const GatherArgs a) 
 #pragma unroll
   for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
   float z = 0.f;
-  int done = 0;  // list positions of earlier chunk passes (index export order)
-  for (int cb = 0; cb < nch_b; cb += NT) {
-    const int c = cb + tid;
-    const int n = one_pass ? n_keep : ((c < nch_b) ? sa.chunk_cnt[cbase + c] : 0);
-    int tot;
-    const int ex = block_excl_scan<NT>(n, s_itmp, tot);
-    s_pref[tid] = ex;
-    if (tid == NT - 1) s_pref[NT] = tot;
+  for (int w0 = lo; w0 < hi; w0 += kSplitWindow) {
+    const int w1 = min(hi, w0 + kSplitWindow);
+    // each thread stages its own chunks' kept entries that fall in [w0, w1)
+    int pos = tpre;
+#pragma unroll
+    for (int k = 0; k < kChunkRegs; ++k) {
+      const int c = c0 + k;
+      if (c < c1 && pos < w1) {
+        const int n = nreg[k];
+        const int q0 = max(pos, w0), q1 = min(pos + n, w1);
+        for (int q = q0; q < q1; ++q) {
+          const long long off = rbase + (long long)c * CH + (q - pos);
+          s_li[q - w0] = sa.surv_idx[off];
+          s_lv[q - w0] = sa.surv_val[off];
+        }
+        pos += n;
+      }
+    }
+    for (int c = c0 + kChunkRegs; c < c1 && pos < w1; ++c) {
+      const int n = sa.chunk_cnt[cbase + c];
+      const int q0 = max(pos, w0), q1 = min(pos + n, w1);
+      for (int q = q0; q < q1; ++q) {
+        const long long off = rbase + (long long)c * CH + (q - pos);
+        s_li[q - w0] = sa.surv_idx[off];
+        s_lv[q - w0] = sa.surv_val[off];
+      }
+      pos += n;
+    }
     __syncthreads();
-    for (int p0 = 0; p0 < tot; p0 += RG::NG * U) {
+    const int wn = w1 - w0;
+    for (int p0 = 0; p0 < wn; p0 += RG::NG * U) {
       int idx[U];
-      float lv[U];
+      uint4 vr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int p = p0 + u * RG::NG + grp;
-        idx[u] = -1;
-        lv[u] = 0.f;
-        if (p < tot) {
-          int lo = 0, hi = NT;  // largest lo with s_pref[lo] <= p: the chunk holding p
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_pref[mid] <= p) lo = mid; else hi = mid;
-          }
-          const long long off = rbase + (long long)(cb + lo) * CH + (p - s_pref[lo]);
-          idx[u] = sa.surv_idx[off];
-          lv[u] = sa.surv_val[off];
-        }
+        idx[u] = (p < wn) ? s_li[p] : -1;
       }
-      uint4 vr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) vr[u] = (idx[u] >= 0) ? ld16(vbase + (size_t)idx[u] * D) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (idx[u] >= 0) {
-          const float w = expf(lv[u] - m);
+          const int p = p0 + u * RG::NG + grp;
+          const float w = expf(s_lv[p] - m);
           float x[RG::EPL];
           Unpack<T>::run(vr[u], x);
 #pragma unroll
           for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
           z += w;
-          const int pos = done + p0 + u * RG::NG + grp;
-          if (gl == 0 && a.sel_idx && pos < a.sel_cap) a.sel_idx[row * a.sel_cap + pos] = idx[u];
+          if (gl == 0 && a.sel_idx && w0 + p < a.sel_cap) a.sel_idx[row * a.sel_cap + w0 + p] = idx[u];
         }
       }
     }
-    done += tot;
     __syncthreads();
   }
-  reduce_rows<T, D>(acc, z, s_red, s_z);
-  if (tid < D) store_out<D>(a, row, tid, s_red[0][tid] / s_z[0]);
+  if (lo < hi) {
+    reduce_rows<T, D, NT>(acc, z, s_red, s_z);
+    float* ar = a.acc + row * AS;
+    for (int d = tid; d < D; d += NT) atomicAdd(&ar[d], s_red[0][d]);
+    if (tid == 0) atomicAdd(&ar[D], s_z[0]);
+  }
+  // every thread's atomics have completed before the block is counted
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&a.row_done[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(P - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // last block of the row: coherent (sc1) loads of the accumulated sums
+  __shared__ float s_fin[AS];
+  if (tid < AS / 4) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(a.acc + row * AS, (short)0, AS * 4, kBufDword3);
+    const floatx4 q = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, 0, kCoherent);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_fin[tid * 4 + e] = q[e];
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += NT) store_out<D>(a, row, d, s_fin[d] / s_fin[D]);
   if (tid == 0) {
     if (a.sel_count) a.sel_count[row] = total;
     if (a.flags) a.flags[row] = a.refreshed ? 1 : 0;

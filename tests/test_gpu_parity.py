@@ -227,7 +227,7 @@ def test_stages_equal_decode_step():
     api.qk_select(g.q, g.k, g.l_kv, tau, max_l_kv=g.max_l_kv, workspace=g.ws)
     api.sparse_gather(g.q, g.k, g.v, g.l_kv, tau, N=64, max_l_kv=g.max_l_kv, out=out, workspace=g.ws)
     torch.cuda.synchronize()
-    np.testing.assert_allclose(out.double().cpu().numpy(), ref["O"], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(out.double().cpu().numpy(), ref["O"], rtol=0, atol=1e-5 * np.abs(ref["O"]).max())
 
 
 DENSE = [
