@@ -55,30 +55,20 @@ saga_status check_shape(const saga_shape* s) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Gather blocks per row: about 16 kept entries each at N (value rows gathered from
-// scattered addresses go fastest spread over many CUs), at most 128.
-int gather_blocks(int N, int max_l_kv) {
-  long long k = N < max_l_kv ? N : (max_l_kv > 0 ? max_l_kv : 1);
-  long long P = (k + 15) / 16;
-  if (P > 128) P = 128;
-  return P < 1 ? 1 : (int)P;
-}
-
 struct Layout {
-  int rows, ch, nch, P, G;  // P: threshold-select blocks per row, G: gather blocks per row
+  int rows, ch, nch, P;  // P: threshold-candidate blocks per row
   long long lpad;
-  size_t hist, cand_cnt, acc, row_done;
-  size_t scores, surv_idx, surv_val, chunk_cnt, chunk_max, dpart, total;
+  size_t hist, cand_cnt;
+  size_t scores, surv_idx, surv_val, chunk_cnt, chunk_max, part, total;
 };
 
-Layout layout(const saga_shape* s, int max_l_kv, int N = 1) {
+Layout layout(const saga_shape* s, int max_l_kv) {
   Layout w{};
   w.rows = s->batch * s->h_q;
   w.ch = chunk_keys(s->dtype, s->d);
   w.nch = max_l_kv > 0 ? (max_l_kv + w.ch - 1) / w.ch : 1;
   w.lpad = (long long)w.nch * w.ch;
   w.P = max_l_kv > 0 ? (max_l_kv + kSelSlice - 1) / kSelSlice : 1;
-  w.G = gather_blocks(N, max_l_kv);
   const size_t rows = (size_t)w.rows;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -89,14 +79,12 @@ Layout layout(const saga_shape* s, int max_l_kv, int N = 1) {
   // counters first: they must be zero before the first call and every call leaves them at zero
   w.hist = take(rows * 256 * 4);
   w.cand_cnt = take(rows * 4);
-  w.acc = take(rows * (size_t)(s->d + 4) * 4 + rows * 4);  // accumulators then row counters
-  w.row_done = w.acc + rows * (size_t)(s->d + 4) * 4;
   w.scores = take(rows * (size_t)w.lpad * 4);
   w.surv_idx = take(rows * (size_t)w.lpad * 4);
   w.surv_val = take(rows * (size_t)w.lpad * 4);
   w.chunk_cnt = take(rows * (size_t)w.nch * 4);
   w.chunk_max = take(rows * (size_t)w.nch * 4);
-  w.dpart = take(rows * (size_t)w.nch * (s->d + 4) * 4);
+  w.part = take(rows * (size_t)w.nch * (s->d + 4) * 4);  // chunk records (sparse and dense)
   w.total = off;
   return w;
 }
@@ -107,10 +95,13 @@ P* at(void* ws, size_t off) {
 }
 
 StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const void* q, const void* k,
-                       const int32_t* l_kv, int32_t max_l_kv, const float* tau, int N) {
+                       const void* v, const int32_t* l_kv, int32_t max_l_kv, const float* tau, int N) {
   StreamArgs a{};
   a.q = q;
   a.k = k;
+  a.v = v;
+  a.part = at<float>(ws, w.part);
+  a.h_v = s->h_v;
   a.l_kv = l_kv;
   a.tau = tau;
   a.scores = at<float>(ws, w.scores);
@@ -130,8 +121,6 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.max_l_kv = max_l_kv;
   a.lpad = w.lpad;
   a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
-  a.zero_f = at<float>(ws, w.acc);
-  a.zero_n = (long long)(w.row_done - w.acc) / 4 + w.rows;
   return a;
 }
 
@@ -141,7 +130,7 @@ saga_status check_common(const saga_shape* s, int32_t max_l_kv, void* ws, size_t
   if (max_l_kv < 0 || max_l_kv > s->l_max) return SAGA_ERR_SHAPE;
   if (N < 1) return SAGA_ERR_SHAPE;
   if (!ws) return SAGA_ERR_NULL;
-  if (ws_bytes < layout(s, max_l_kv, N).total) return SAGA_ERR_WORKSPACE;
+  if (ws_bytes < layout(s, max_l_kv).total) return SAGA_ERR_WORKSPACE;
   return SAGA_OK;
 }
 
@@ -160,29 +149,40 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
   hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);
 }
 
-void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, hipStream_t st) {
+// Scores and Atop-N comparison; with `gather` also the chunk records of eq. (7).
+void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, bool gather,
+                   hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, {
-    if (from_scores)
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromScores>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+    const dim3 grid = stream_grid(s, w);
+    if (!gather)
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, false>), grid, dim3(kBlock), 0, st, a);
+    else if (from_scores)
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromScores, true>), grid, dim3(kBlock), 0, st, a);
     else if (s->batch == 1)  // one sequence: its chunks reach max_l_kv, key loads need not wait for l_kv
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeysSpeculative>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeysSpeculative, true>), grid, dim3(kBlock), 0, st, a);
     else
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, true>), grid, dim3(kBlock), 0, st, a);
   });
 }
 
-void launch_gather(const saga_shape* s, const Layout& w, const GatherArgs& g, hipStream_t st) {
+// Chunk records from the kept lists (only for the separate gather stage).
+void launch_chunk_gather(const saga_shape* s, const Layout& w, const StreamArgs& a, hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, {
-    hipLaunchKernelGGL((k_gather_split<T, D>), dim3(w.G, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+    hipLaunchKernelGGL((k_chunk_gather<T, D>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });
 }
 
-GatherArgs gather_args(const saga_shape* s, const Layout& w, void* ws, const StreamArgs& sa, const void* v,
-                       float* tau, void* out, int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap,
-                       int32_t* flags, bool refreshed) {
+void launch_combine(const saga_shape* s, const GatherArgs& g, hipStream_t st) {
+  SAGA_DISPATCH(s->dtype, s->d, {
+    hipLaunchKernelGGL((k_split_combine<T, D>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+  });
+}
+
+GatherArgs gather_args(const saga_shape* s, const StreamArgs& sa, float* tau, void* out, int32_t* sel_count,
+                       int32_t* sel_idx, int32_t sel_cap, int32_t* flags, bool refreshed) {
   GatherArgs g{};
   g.s = sa;
-  g.v = v;
+  g.v = sa.v;
   g.tau = tau;
   g.out = out;
   g.sel_count = sel_count;
@@ -192,8 +192,6 @@ GatherArgs gather_args(const saga_shape* s, const Layout& w, void* ws, const Str
   g.sel_cap = sel_idx ? sel_cap : 0;
   g.out_bf16 = s->out_dtype == SAGA_BF16;
   g.refreshed = refreshed ? 1 : 0;
-  g.acc = at<float>(ws, w.acc);
-  g.row_done = at<unsigned>(ws, w.row_done);
   return g;
 }
 
@@ -240,17 +238,16 @@ saga_status saga_decode_attn(const saga_shape* s, const void* q, const void* k, 
   saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
   if (st != SAGA_OK) return st;
   if (refresh_period < 1 || step < 0 || (sel_idx && sel_cap < 1)) return SAGA_ERR_SHAPE;
-  const Layout w = layout(s, max_l_kv, N);
+  const Layout w = layout(s, max_l_kv);
   const hipStream_t hs = (hipStream_t)stream;
   const bool refresh = (step % refresh_period) == 0;
   (void)hipGetLastError();
-  const StreamArgs a = stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N);
-  const GatherArgs g = gather_args(s, w, workspace, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, refresh);
+  const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
   if (max_l_kv > 0) {
     if (refresh) launch_refresh(s, w, a, tau, hs);
-    launch_select(s, w, a, refresh, hs);
+    launch_select(s, w, a, refresh, true, hs);
   }
-  launch_gather(s, w, g, hs);
+  launch_combine(s, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
   return launched();
 }
 
@@ -262,7 +259,8 @@ saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const voi
   if (st != SAGA_OK) return st;
   const Layout w = layout(s, max_l_kv);
   (void)hipGetLastError();
-  if (max_l_kv > 0) launch_refresh(s, w, stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N), tau, (hipStream_t)stream);
+  if (max_l_kv > 0)
+    launch_refresh(s, w, stream_args(s, w, workspace, q, k, nullptr, l_kv, max_l_kv, tau, N), tau, (hipStream_t)stream);
   return launched();
 }
 
@@ -275,7 +273,8 @@ saga_status saga_qk_select(const saga_shape* s, const void* q, const void* k, co
   const Layout w = layout(s, max_l_kv);
   (void)hipGetLastError();
   if (max_l_kv > 0)
-    launch_select(s, w, stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, 1), false, (hipStream_t)stream);
+    launch_select(s, w, stream_args(s, w, workspace, q, k, nullptr, l_kv, max_l_kv, tau, 1), false, false,
+                  (hipStream_t)stream);
   return launched();
 }
 
@@ -287,11 +286,12 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
   saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
   if (st != SAGA_OK) return st;
   if (sel_idx && sel_cap < 1) return SAGA_ERR_SHAPE;
-  const Layout w = layout(s, max_l_kv, N);
+  const Layout w = layout(s, max_l_kv);
+  const hipStream_t hs = (hipStream_t)stream;
   (void)hipGetLastError();
-  const StreamArgs a = stream_args(s, w, workspace, q, k, l_kv, max_l_kv, tau, N);
-  launch_gather(s, w, gather_args(s, w, workspace, a, v, tau, out, sel_count, sel_idx, sel_cap, flags, false),
-                (hipStream_t)stream);
+  const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
+  if (max_l_kv > 0) launch_chunk_gather(s, w, a, hs);
+  launch_combine(s, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false), hs);
   return launched();
 }
 
@@ -311,7 +311,7 @@ saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* 
   a.k = k;
   a.v = v;
   a.l_kv = l_kv;
-  a.part = at<float>(workspace, w.dpart);
+  a.part = at<float>(workspace, w.part);
   a.out = out;
   a.h_q = s->h_q;
   a.h_kv = s->h_k;

@@ -1,13 +1,14 @@
 // Kernels of the SAGA + Atop-N decode step and of the dense GQA baseline (gfx950).
 //
-// Stale-threshold step:  k_qk_select -> k_gather_split
+// Stale-threshold step:  k_qk_select<gather> -> k_split_combine
 // Refresh step:          k_scores_hist -> k_cand_collect -> k_select_finish
-//                        -> k_qk_select<from stored logits> -> k_gather_split
+//                        -> k_qk_select<from stored logits, gather> -> k_split_combine
+// Separate stages:       k_qk_select -> k_chunk_gather -> k_split_combine
 // Dense GQA baseline:    k_dense_partial -> k_dense_combine
 //
-// No kernel waits on another workgroup: exchanges go through kernel boundaries, or
-// through device-scope atomics whose last arrival finishes the work (device-scope
-// fences are avoided: on this GPU they write back and invalidate the whole L2).
+// No kernel waits on another workgroup and none needs a device-scope fence: every
+// exchange between workgroups goes through a kernel boundary (the threshold
+// candidates are appended with device atomics and read by the next kernel).
 //
 // Paper: "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding"
 // (summary page picx.dev DRD92V): eq. (2) logits, section "Methodology > Atop-N
@@ -53,9 +54,97 @@ struct StreamArgs {
   int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   long long lpad;
   float scale;
-  float* zero_f;           // k_qk_select clears [zero_n] floats here (the gather's accumulators)
-  long long zero_n;
+  const void* v;           // [B, h_v, l_max, D] (gathering kernels)
+  float* part;             // [B*h_q, nch, D+4] chunk records: [1] sum w, [4..4+D) sum w*v
+  int h_v;
 };
+
+// Kept entries of one chunk, per head of the tile, staged in LDS: offset of the key
+// inside the chunk and its logit; plus the count and the largest kept logit (as an
+// order key) per head.
+template <int CH> struct KeptLds {
+  uint16_t off[16][CH];
+  float val[16][CH];
+  int cnt[16];
+  unsigned mx[16];
+};
+
+// Eq. (7) split over chunks of keys: the 16-lane group h of the block takes head
+// j0+h of the tile, gathers the value rows of its kept entries from value head v(j)
+// and writes the chunk record of row (b, j): [1] = sum_i w_i and [4..4+D) =
+// sum_i w_i V[i,:], w_i = exp(A_i - m), m = the chunk's largest kept logit of the row
+// (so every w_i <= 1). Rows without kept entries in the chunk write nothing.
+template <typename T, int D, int CH>
+__device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const StreamArgs& a, int b, int j0, int nh,
+                                              int c) {
+  constexpr int EPL = Unpack<T>::kN;                    // columns per 16-byte piece
+  constexpr int PIECES = D / EPL;                       // pieces per value row
+  constexpr int RPG = PIECES >= 16 ? 1 : 16 / PIECES;  // rows one group load covers
+  constexpr int PPL = PIECES >= 16 ? PIECES / 16 : 1;   // pieces per lane per row
+  constexpr int U = 4;                                  // loads in flight per lane
+  const int tid = threadIdx.x, h = tid >> 4, gl = tid & 15;
+  if (h >= nh) return;
+  const int n = kl.cnt[h];
+  if (n == 0) return;
+  const int sub = RPG > 1 ? gl / PIECES : 0;
+  const int pc = RPG > 1 ? gl % PIECES : gl;
+  const int j = j0 + h;
+  const int vh = (int)(((long long)j * a.h_v) / a.h_q);
+  const int base = c * CH;
+  const T* vrow = reinterpret_cast<const T*>(a.v) + ((size_t)(b * a.h_v + vh) * a.l_max + base) * D + pc * EPL;
+  const float m = order_key_to_f32(kl.mx[h]);
+  float acc[PPL][EPL];
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[p][e] = 0.f;
+  float z = 0.f;
+  for (int e0 = sub; e0 < n; e0 += RPG * U) {
+    uint4 x[U][PPL];
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * RPG;
+      w[u] = 0.f;
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) x[u][p] = make_uint4(0, 0, 0, 0);
+      if (e < n) {
+        const T* r = vrow + (size_t)kl.off[h][e] * D;
+#pragma unroll
+        for (int p = 0; p < PPL; ++p) x[u][p] = ld16(r + 16 * p * EPL);
+        w[u] = expf(kl.val[h][e] - m);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        float f[EPL];
+        Unpack<T>::run(x[u][p], f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[p][e] += w[u] * f[e];
+      }
+      z += w[u];
+    }
+  }
+#pragma unroll
+  for (int o = PIECES; o < 16; o <<= 1) {
+#pragma unroll
+    for (int p = 0; p < PPL; ++p)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[p][e] += __shfl_xor(acc[p][e], o);
+    z += __shfl_xor(z, o);
+  }
+  if (sub != 0) return;
+  float* rec = a.part + ((long long)(b * a.h_q + j) * a.nch + c) * (D + 4);
+#pragma unroll
+  for (int p = 0; p < PPL; ++p)
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(rec + 4 + (pc + 16 * p) * EPL + e) =
+          make_float4(acc[p][e], acc[p][e + 1], acc[p][e + 2], acc[p][e + 3]);
+  if (gl == 0) rec[1] = z;
+}
 
 // Source of the logits of k_qk_select.
 enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
@@ -67,9 +156,9 @@ enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 // logit are recorded. MODE kFromScores reads the logits stored by k_scores_hist (a
 // refresh step: the fp32 values the threshold was selected from); MODE
 // kFromKeysSpeculative (one sequence) issues the key loads before l_kv arrives.
-// Every block also clears its share of the gather's accumulators.
+// With GATHER the block also writes the chunk records of eq. (7) (chunk_records).
 // grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool GATHER>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
   constexpr int CH = StreamCfg<T, D>::kChunk;
@@ -91,20 +180,13 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
     score_tiles<T, D, TPW>(sc, qk, kh, wbase, a.max_l_kv, lane, a.scale);
   }
-  {
-    const long long nblk = (long long)gridDim.x * gridDim.y * gridDim.z;
-    const long long id = blockIdx.x + (long long)gridDim.x * (blockIdx.y + (long long)gridDim.y * blockIdx.z);
-    const long long per = (a.zero_n + nblk - 1) / nblk;
-    for (long long i = id * per + tid; i < min(a.zero_n, (id + 1) * per); i += kBlock) a.zero_f[i] = 0.f;
-  }
   const int L = min(a.l_kv[b], a.max_l_kv);
   if (base >= L) return;
 
-  __shared__ int s_cnt[16];
-  __shared__ unsigned s_max[16];
+  __shared__ KeptLds<GATHER ? CH : 1> kl;
   if (tid < 16) {
-    s_cnt[tid] = 0;
-    s_max[tid] = 0u;
+    kl.cnt[tid] = 0;
+    kl.mx[tid] = 0u;
   }
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
   if constexpr (MODE == kFromScores) {
@@ -125,19 +207,58 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
       const int key = wbase + 16 * t + 4 * kq + r;
       const float v = sc[t][r];
       if (live && key < L && v >= tau_l) {
-        const int slot = atomicAdd(&s_cnt[hh], 1);
+        const int slot = atomicAdd(&kl.cnt[hh], 1);
         a.surv_idx[seg + slot] = key;
         a.surv_val[seg + slot] = v;
-        atomicMax(&s_max[hh], order_key(v));
+        atomicMax(&kl.mx[hh], order_key(v));
+        if constexpr (GATHER) {
+          kl.off[hh][slot] = (uint16_t)(key - base);
+          kl.val[hh][slot] = v;
+        }
       }
     }
   }
   __syncthreads();
   if (tid < nh) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
-    a.chunk_cnt[o] = s_cnt[tid];
-    a.chunk_max[o] = order_key_to_f32(s_max[tid]);
+    a.chunk_cnt[o] = kl.cnt[tid];
+    a.chunk_max[o] = order_key_to_f32(kl.mx[tid]);
   }
+  if constexpr (GATHER) chunk_records<T, D, CH>(kl, a, b, j0, nh, c);
+}
+
+// The chunk records of eq. (7) from kept lists already in the workspace (the
+// separately callable gather stage): stages each head's kept entries of the chunk
+// in LDS, then chunk_records. grid = (nch, h_k * htiles, B), block = 256.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
+  constexpr int CH = StreamCfg<T, D>::kChunk;
+  const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int base = c * CH;
+  if (base >= L) return;
+  const int g = gy / a.htiles, ht = gy - g * a.htiles;
+  const int j0 = g * a.g_k + ht * 16;
+  const int nh = min(16, a.g_k - ht * 16);
+  const int tid = threadIdx.x;
+  const int row0 = b * a.h_q + j0;
+  __shared__ KeptLds<CH> kl;
+  if (tid < nh) {
+    const long long o = (long long)(row0 + tid) * a.nch + c;
+    kl.cnt[tid] = a.chunk_cnt[o];
+    kl.mx[tid] = order_key(a.chunk_max[o]);
+  }
+  __syncthreads();
+  for (int e = tid; e < nh * CH; e += kBlock) {
+    const int h = e / CH, i = e - h * CH;
+    if (i < kl.cnt[h]) {
+      const long long at = (long long)(row0 + h) * a.lpad + base + i;
+      kl.off[h][i] = (uint16_t)(a.surv_idx[at] - base);
+      kl.val[h][i] = a.surv_val[at];
+    }
+  }
+  __syncthreads();
+  chunk_records<T, D, CH>(kl, a, b, j0, nh, c);
 }
 
 // ----------------------------------------------------------------------------
@@ -310,8 +431,6 @@ struct GatherArgs {
   int32_t* sel_idx;       // [B*h_q, sel_cap] or null
   int32_t* flags;         // [B*h_q] or null
   int h_v, sel_cap, out_bf16, refreshed;
-  float* acc;             // [B*h_q][D+4] sum of w*v (D), sum of w; cleared by k_qk_select
-  unsigned* row_done;     // [B*h_q] finished blocks per row; cleared by k_qk_select
 };
 
 template <int D>
@@ -367,9 +486,8 @@ __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[
 // One row (b, j) computed exactly by one block: the logits of every key with the same
 // tiles as the streaming kernels (into the row's logit buffer), optionally the exact
 // N-th largest as a new threshold (a forced refresh), then the kept set, its maximum
-// and the sparse softmax-PV. Used where the fast paths cannot answer: a stale
-// threshold that keeps nothing, or a logit range too wide for the fixed-reference
-// accumulation. Writes out, tau (refresh only), sel_count, sel_idx and flags.
+// and the sparse softmax-PV. Used for a stale threshold that keeps nothing (the
+// forced refresh). Writes out, tau (refresh only), sel_count, sel_idx and flags.
 template <typename T, int D, int NT>
 __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh_tau, float (*s_red)[D],
                           float* s_z) {
@@ -477,173 +595,154 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
   __syncthreads();
 }
 
-// Split gather: P blocks per row (b, j). Every block reads the row's chunk counts
-// and maxima (so all use the row maximum m as the softmax reference and their sums
-// add directly), takes list positions [T*s/P, T*(s+1)/P) of the row's kept list
-// (chunk order), gathers those value rows of value head v(j) and adds its sum of
-// w*v and of w, w = exp(A - m), to the row's accumulator (device-scope atomics,
-// fan-in P). The last of the P blocks to finish divides and writes the row. A row
-// that kept nothing is recomputed exactly by block 0 (forced refresh).
-// grid = (P, h_q, B), block = 256.
-constexpr int kSplitWindow = 1024;  // list positions a block stages in LDS per pass
-constexpr int kChunkRegs = 8;       // chunk counts a thread keeps in registers
+// Merge of the chunk records of each row (b, j) (eq. (7) reassembled from its
+// chunks): M = the row's largest kept logit (the maximum of the chunk maxima),
+// O = sum_c e_c o_c / sum_c e_c z_c with e_c = exp(m_c - M) over the chunks that kept
+// something. Block x takes output columns [16x, 16x+16); thread t takes chunks t,
+// t+256, ... . The kept indices are exported in the same pass (chunk c by block
+// c mod gridDim.x). A row that kept nothing is recomputed exactly by block 0
+// (forced refresh). The first kChunkRegs chunks of a thread are read in one round
+// of independent loads (count, maximum, record slice, first kept indices) whether
+// or not the chunk kept anything; the values of empty chunks are never used.
+// grid = (D / 16, h_q, B), block = 256.
+constexpr int kChunkRegs = 2;  // chunks per thread read speculatively
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock) void k_gather_split(const GatherArgs a) {
-  constexpr int NT = kBlock;
-  constexpr int NW = NT / kWave;
+__global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   constexpr int CH = StreamCfg<T, D>::kChunk;
   constexpr int AS = D + 4;
-  using RG = RowGather<T, D, NT>;
-  constexpr int U = 4;
   const StreamArgs& sa = a.s;
-  const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int P = gridDim.x;
+  const int cb = blockIdx.x, j = blockIdx.y, b = blockIdx.z, CB = gridDim.x;
   const long long row = (long long)b * sa.h_q + j;
   const int L = min(sa.l_kv[b], sa.max_l_kv);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int col = cb * 16;
 
-  __shared__ int s_itmp[NW];
-  __shared__ float s_ftmp[NW];
-  __shared__ int s_li[kSplitWindow];
-  __shared__ float s_lv[kSplitWindow];
-  __shared__ float s_red[NW][D];
-  __shared__ float s_z[NW];
-  __shared__ int s_last;
+  __shared__ int s_itmp[kWaves];
+  __shared__ float s_ftmp[kWaves];
+  __shared__ float s_acc[kWaves][17];
+  __shared__ float s_red[kWaves][D];
+  __shared__ float s_z[kWaves];
 
   if (L <= 0) {
-    if (s == 0) {
-      for (int d = tid; d < D; d += NT) store_out<D>(a, row, d, 0.f);
-      if (tid == 0) {
-        if (a.sel_count) a.sel_count[row] = 0;
-        if (a.flags) a.flags[row] = 0;
-      }
+    if (tid < 16) store_out<D>(a, row, col + tid, 0.f);
+    if (cb == 0 && tid == 0) {
+      if (a.sel_count) a.sel_count[row] = 0;
+      if (a.flags) a.flags[row] = 0;
     }
     return;
   }
-  const long long rbase = row * sa.lpad;
-  const long long cbase = row * sa.nch;
   const int nch_b = (L + CH - 1) / CH;
-  const int cpt = (nch_b + NT - 1) / NT;  // consecutive chunks per thread
-  const int c0 = tid * cpt, c1 = min(nch_b, c0 + cpt);
+  const int32_t* cnt = sa.chunk_cnt + row * sa.nch;
+  const float* cmax = sa.chunk_max + row * sa.nch;
+  const float* rp = sa.part + row * sa.nch * AS;
+  const int32_t* kept = sa.surv_idx + row * sa.lpad;
+  int32_t* exp_idx = a.sel_idx ? a.sel_idx + row * a.sel_cap : nullptr;
 
-  // counts and maxima of this thread's chunks (kept in registers when few)
   int nreg[kChunkRegs];
+  float mreg[kChunkRegs], zreg[kChunkRegs];
+  float4 xreg[kChunkRegs][4];
+  int4 ireg[kChunkRegs];
+#pragma unroll
+  for (int k = 0; k < kChunkRegs; ++k) {
+    const int c = tid + k * kBlock;
+    nreg[k] = 0;
+    if (c < nch_b) {
+      nreg[k] = cnt[c];
+      mreg[k] = cmax[c];
+      const float* pc = rp + (long long)c * AS;
+      const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + col);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xreg[k][q] = p4[q];
+      zreg[k] = pc[1];
+      if (exp_idx && c % CB == cb) ireg[k] = *reinterpret_cast<const int4*>(kept + (long long)c * CH);
+    }
+  }
   float m = -INFINITY;
   int tsum = 0;
 #pragma unroll
   for (int k = 0; k < kChunkRegs; ++k) {
-    const int c = c0 + k;
-    nreg[k] = 0;
-    if (c < c1) {
-      const int n = sa.chunk_cnt[cbase + c];
-      const float mx = sa.chunk_max[cbase + c];
-      nreg[k] = n;
-      tsum += n;
-      m = fmaxf(m, n > 0 ? mx : -INFINITY);
-    }
+    tsum += nreg[k];
+    if (nreg[k] > 0) m = fmaxf(m, mreg[k]);
   }
-  for (int c = c0 + kChunkRegs; c < c1; ++c) {
-    const int n = sa.chunk_cnt[cbase + c];
+  for (int c = tid + kChunkRegs * kBlock; c < nch_b; c += kBlock) {
+    const int n = cnt[c];
     tsum += n;
-    if (n > 0) m = fmaxf(m, sa.chunk_max[cbase + c]);
+    if (n > 0) m = fmaxf(m, cmax[c]);
   }
-  m = block_max<NT>(m, s_ftmp);
+  const float M = block_max(m, s_ftmp);
   int total;
-  const int tpre = block_excl_scan<NT>(tsum, s_itmp, total);
+  int pos = block_excl_scan(tsum, s_itmp, total);
   if (total == 0) {
-    if (s == 0) exact_row<T, D, NT>(a, b, j, L, true, s_red, s_z);
+    if (cb == 0) exact_row<T, D, kBlock>(a, b, j, L, true, s_red, s_z);
     return;
   }
-  const int lo = (int)(((long long)total * s) / P), hi = (int)(((long long)total * (s + 1)) / P);
 
-  const int vh = (int)(((long long)j * a.h_v) / sa.h_q);
-  const int grp = tid / RG::G, gl = tid - grp * RG::G;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_v + vh) * sa.l_max * D + gl * RG::EPL;
-  float acc[RG::EPL];
+  float o[16];
 #pragma unroll
-  for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
   float z = 0.f;
-  for (int w0 = lo; w0 < hi; w0 += kSplitWindow) {
-    const int w1 = min(hi, w0 + kSplitWindow);
-    // each thread stages its own chunks' kept entries that fall in [w0, w1)
-    int pos = tpre;
+  auto add = [&](const float4 (&x)[4], float zc, float mc) {
+    const float e = expf(mc - M);
 #pragma unroll
-    for (int k = 0; k < kChunkRegs; ++k) {
-      const int c = c0 + k;
-      if (c < c1 && pos < w1) {
-        const int n = nreg[k];
-        const int q0 = max(pos, w0), q1 = min(pos + n, w1);
-        for (int q = q0; q < q1; ++q) {
-          const long long off = rbase + (long long)c * CH + (q - pos);
-          s_li[q - w0] = sa.surv_idx[off];
-          s_lv[q - w0] = sa.surv_val[off];
-        }
-        pos += n;
-      }
+    for (int q = 0; q < 4; ++q) {
+      o[4 * q] += e * x[q].x;
+      o[4 * q + 1] += e * x[q].y;
+      o[4 * q + 2] += e * x[q].z;
+      o[4 * q + 3] += e * x[q].w;
     }
-    for (int c = c0 + kChunkRegs; c < c1 && pos < w1; ++c) {
-      const int n = sa.chunk_cnt[cbase + c];
-      const int q0 = max(pos, w0), q1 = min(pos + n, w1);
-      for (int q = q0; q < q1; ++q) {
-        const long long off = rbase + (long long)c * CH + (q - pos);
-        s_li[q - w0] = sa.surv_idx[off];
-        s_lv[q - w0] = sa.surv_val[off];
+    z += e * zc;
+  };
+  auto export_rest = [&](int c, int n, int from) {
+    for (int i = from; i < n && pos + i < a.sel_cap; ++i) exp_idx[pos + i] = kept[(long long)c * CH + i];
+  };
+#pragma unroll
+  for (int k = 0; k < kChunkRegs; ++k) {
+    const int c = tid + k * kBlock, n = nreg[k];
+    if (n > 0) {
+      add(xreg[k], zreg[k], mreg[k]);
+      if (exp_idx && c % CB == cb) {
+        const int first[4] = {ireg[k].x, ireg[k].y, ireg[k].z, ireg[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < n && pos + i < a.sel_cap) exp_idx[pos + i] = first[i];
+        export_rest(c, n, 4);
       }
       pos += n;
     }
-    __syncthreads();
-    const int wn = w1 - w0;
-    for (int p0 = 0; p0 < wn; p0 += RG::NG * U) {
-      int idx[U];
-      uint4 vr[U];
+  }
+  for (int c = tid + kChunkRegs * kBlock; c < nch_b; c += kBlock) {
+    const int n = cnt[c];
+    if (n > 0) {
+      const float* pc = rp + (long long)c * AS;
+      const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + col);
+      float4 x[4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + u * RG::NG + grp;
-        idx[u] = (p < wn) ? s_li[p] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) vr[u] = (idx[u] >= 0) ? ld16(vbase + (size_t)idx[u] * D) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (idx[u] >= 0) {
-          const int p = p0 + u * RG::NG + grp;
-          const float w = expf(s_lv[p] - m);
-          float x[RG::EPL];
-          Unpack<T>::run(vr[u], x);
-#pragma unroll
-          for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
-          z += w;
-          if (gl == 0 && a.sel_idx && w0 + p < a.sel_cap) a.sel_idx[row * a.sel_cap + w0 + p] = idx[u];
-        }
-      }
+      for (int q = 0; q < 4; ++q) x[q] = p4[q];
+      add(x, pc[1], cmax[c]);
+      if (exp_idx && c % CB == cb) export_rest(c, n, 0);
+      pos += n;
     }
-    __syncthreads();
   }
-  if (lo < hi) {
-    reduce_rows<T, D, NT>(acc, z, s_red, s_z);
-    float* ar = a.acc + row * AS;
-    for (int d = tid; d < D; d += NT) atomicAdd(&ar[d], s_red[0][d]);
-    if (tid == 0) atomicAdd(&ar[D], s_z[0]);
-  }
-  // every thread's atomics have completed before the block is counted
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&a.row_done[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(P - 1);
-  __syncthreads();
-  if (!s_last) return;
-  // last block of the row: coherent (sc1) loads of the accumulated sums
-  __shared__ float s_fin[AS];
-  if (tid < AS / 4) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(a.acc + row * AS, (short)0, AS * 4, kBufDword3);
-    const floatx4 q = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, 0, kCoherent);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_fin[tid * 4 + e] = q[e];
+  for (int e = 0; e < 16; ++e) o[e] = wave_sum(o[e]);
+  z = wave_sum(z);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_acc[wv][e] = o[e];
+    s_acc[wv][16] = z;
   }
   __syncthreads();
-  for (int d = tid; d < D; d += NT) store_out<D>(a, row, d, s_fin[d] / s_fin[D]);
-  if (tid == 0) {
+  if (tid < 16) {
+    float oo = 0.f, zz = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      oo += s_acc[w][tid];
+      zz += s_acc[w][16];
+    }
+    store_out<D>(a, row, col + tid, oo / zz);
+  }
+  if (cb == 0 && tid == 0) {
     if (a.sel_count) a.sel_count[row] = total;
     if (a.flags) a.flags[row] = a.refreshed ? 1 : 0;
   }
