@@ -8,17 +8,26 @@ steps occur at their natural rate (one in refresh_period) inside the timed regio
 
 Inputs are resident in HBM before timing. R rotating copies of q/K/V/tau (R*bytes(K)
 >= 1 GiB, R coprime with the refresh period) keep the 256 MB Infinity Cache from
-serving repeated reads, as a model's per-layer caches would. The K timed steps are
+serving repeated reads, as a model's per-layer caches would. Timed steps are
 replayed from a HIP graph and timed with HIP events on the launch stream.
 
-Prints one JSON line. `value` = SAGA decode steps/s; `roofline` is for the dominant
-kernel (the fused steady-step kernel, timed alone the same way: a step that reuses
-the threshold is exactly one launch of it); `cpu_baseline` is the CPU oracle timed on
-this host on the same workload.
+Prints one JSON line. `value` = SAGA decode steps/s (refresh steps included).
+`roofline` is for the dominant kernel, the select kernel of a step that reuses the
+threshold (saga_select_gather: K stream, comparison, value gather): a graph of K
+launches of it alone is timed with HIP events on its stream; its algorithmic bytes
+per launch are bytes(K) + bytes(selected V rows, union per value head). `traffic` is
+the HBM traffic of that kernel measured with rocprofv3 counters (recorded in
+profiles/ for one build of the kernels; null when the sources differ).
+`cpu_baseline` is the CPU oracle timed on this host on the same workload.
+
+Other modes: --probe copy|read (streaming ceilings and counter calibration),
+--only <part> (one part, for profiler runs), --rocprof-summary CSV... (per-kernel
+averages of a rocprofv3 csv output).
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import json
 import math
 import os
@@ -31,6 +40,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn steps/s + % HBM roofline at l_kv=128K, bs=1 (SAGA+Atop-N vs dense GQA)"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_qk_select_gather_qwen128k_traffic.txt")
+DOMINANT = "k_qk_select<bf16, d=128, speculative keys, gather> (saga_select_gather)"
 
 
 def log(msg: str) -> None:
@@ -48,7 +59,8 @@ def rotating_sets(bytes_k: int, period: int, want: int) -> int:
 
 def time_graph(torch, fn_steps, reps: int):
     """Capture fn_steps() into a HIP graph; replay once untimed, then `reps` timed
-    replays bracketed by device synchronisation. Returns the per-replay ms list."""
+    replays, each bracketed by device synchronisation and HIP events on the stream
+    the graph is launched on. Returns the per-replay ms list."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -70,35 +82,46 @@ def time_graph(torch, fn_steps, reps: int):
     return out
 
 
-def median(xs):
+def pct(xs, p):
     xs = sorted(xs)
-    n = len(xs)
-    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    if len(xs) == 1:
+        return xs[0]
+    k = (len(xs) - 1) * p / 100.0
+    lo, hi = int(math.floor(k)), int(math.ceil(k))
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
 
 def cpu_baseline(w, x, seconds: float):
-    """The oracle as it stands, on the same inputs, for about `seconds` of host time."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+    """The oracle as it stands, on the same inputs, for about `seconds` of host time
+    with every host core, then for a fifth of that on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import saga_oracle as orc
 
     q64, k64, v64 = x.f64()
-    tau = None
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        r = orc.saga_decode_step(q64, k64, v64, x.l_kv, w.N, w.refresh_period, steps, tau_in=tau,
-                                 keep_logits=False)
-        tau = r.tau
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def run(limit_s):
+        tau = None
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            r = orc.saga_decode_step(q64, k64, v64, x.l_kv, w.N, w.refresh_period, steps, tau_in=tau,
+                                     keep_logits=False)
+            tau = r.tau
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s:
+                return steps, el
+
+    steps, el = run(seconds)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    with threadpool_limits(limits=1):
+        steps1, el1 = run(seconds / 5)
     return {"value": steps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} consecutive oracle decode steps (steps 0..{steps - 1}, exact threshold at "
                       f"step % {w.refresh_period} == 0) of the full {w.name} workload, {el:.1f} s of host time; "
-                      f"float64 numpy, BLAS threads = cores"}
+                      f"float64 numpy, BLAS threads = cores",
+            "single_thread": {"value": steps1 / el1, "unit": "steps/s", "cores": 1,
+                              "sample": f"{steps1} steps, {el1:.1f} s, BLAS limited to one thread"}}
 
 
 def copy_probe(torch, reps: int) -> int:
@@ -120,21 +143,93 @@ def copy_probe(torch, reps: int) -> int:
     return 0
 
 
+def read_probe(torch, reps: int) -> dict:
+    """Streaming-read ceilings with torch's sum kernel: one 1 GiB read, and 32 MiB reads
+    (the size of the 128K key stream) from 32 different slices, each timed in a graph."""
+    n = 1 << 30
+    x = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+    acc = torch.zeros(32, dtype=torch.float32, device="cuda:0")
+    sl = x.view(32, -1)
+
+    def big():
+        torch.sum(x.view(1, -1), dim=1, dtype=torch.float32, out=acc[0:1])
+
+    def small():
+        for i in range(32):
+            torch.sum(sl[i:i + 1], dim=1, dtype=torch.float32, out=acc[i:i + 1])
+
+    big()
+    small()
+    torch.cuda.synchronize()
+    ms_big = min(time_graph(torch, lambda: [big() for _ in range(4)], reps)) / 4
+    ms_small = min(time_graph(torch, small, reps)) / 32
+    return {"kernel": "torch.sum (bf16 -> f32)", "gib_read_gbs": n / (ms_big * 1e-3) / 1e9,
+            "mib32_read_gbs": (n // 32) / (ms_small * 1e-3) / 1e9, "mib32_read_us": ms_small * 1e3}
+
+
+def recorded_traffic():
+    """Traffic per launch of the dominant kernel recorded in profiles/, if it was
+    measured on the current sources of the kernels; else None (with the reason)."""
+    from sparse_decode_attention_saga_amd import build
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter record"
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != build.source_digest():
+        return None, "kernel sources changed since the counters were taken"
+    return float(rec["traffic_bytes_per_launch"]), TRAFFIC_FILE
+
+
+def rocprof_summary(paths) -> int:
+    """Per-kernel averages of rocprofv3 csv files: kernel_stats (durations) or
+    counter_collection (one row per dispatch and counter)."""
+    for path in paths:
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        if not rows:
+            continue
+        if "AverageNs" in rows[0]:
+            print(f"# {os.path.basename(path)}: kernel, calls, average / min / max duration (us)")
+            for r in rows:
+                print(f"{r['Name'][:96]:96s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
+                      f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+        elif "Counter_Name" in rows[0]:
+            acc = {}
+            for r in rows:
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                s = acc.setdefault(key, [0.0, 0])
+                s[0] += float(r["Counter_Value"])
+                s[1] += 1
+            print(f"# {os.path.basename(path)}: kernel, counter, dispatches, average value per dispatch")
+            for (k, c), (tot, n) in sorted(acc.items()):
+                print(f"{k[:96]:96s} {c:12s} {n:7d} {tot / n:14.1f}")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--reps", type=int, default=5, help="timed graph replays (median reported)")
+    ap.add_argument("--reps", type=int, default=20, help="timed graph replays (median, p10, p90 reported)")
     ap.add_argument("--workload", default="qwen2.5-1.5b-shape-l128k")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: >= 1 GiB of K)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "saga", "dense", "steady"], default="all",
+    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady"], default="all",
                     help="time only one part (for profiler runs)")
-    ap.add_argument("--probe", choices=["none", "copy"], default="none",
-                    help="copy: time a plain device copy of 256 MiB (counter calibration, streaming ceiling)")
+    ap.add_argument("--probe", choices=["none", "copy", "read"], default="none",
+                    help="copy: a plain device copy of 256 MiB (counter calibration); read: read ceilings")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV",
+                    help="print per-kernel averages of rocprofv3 csv files and exit")
     args = ap.parse_args()
+
+    if args.rocprof_summary:
+        return rocprof_summary(args.rocprof_summary)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -142,11 +237,13 @@ def main() -> int:
               "multi-GPU runs are not part of this library.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     if args.probe == "copy":
         return copy_probe(torch, max(args.steps, 8))
+    if args.probe == "read":
+        print(json.dumps({"probe": "read", **read_probe(torch, max(args.reps, 3))}), flush=True)
+        return 0
 
     from sparse_decode_attention_saga_amd import api
     from sparse_decode_attention_saga_amd import bytemodel
@@ -184,10 +281,17 @@ def main() -> int:
                         step=t, max_l_kv=L, out=out, workspace=ws)
 
     def steady_step(t):
-        # a step that reuses the threshold: exactly one launch of the fused kernel
         r = t % R
         api.decode_attn(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, refresh_period=1 << 30,
                         step=1 + t, max_l_kv=L, out=out, workspace=ws)
+
+    def select_only(t):
+        r = t % R
+        api.select_gather(qs[r], ks[r], vs[r], l_kv, taus[r], max_l_kv=L, workspace=ws)
+
+    def combine_only(t):
+        r = t % R
+        api.split_combine(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, max_l_kv=L, out=out, workspace=ws)
 
     K, W = args.steps, args.warmup
     res = {}
@@ -196,24 +300,32 @@ def main() -> int:
             saga_step(t)
         torch.cuda.synchronize()
         ms = time_graph(torch, lambda: [saga_step(t) for t in range(W, W + K)], args.reps)
-        res["saga_ms"] = median(ms)
-        res["saga_ms_all"] = ms
+        res["saga_us"] = [1e3 * m / K for m in ms]
         res["refresh_steps"] = sum(1 for t in range(W, W + K) if t % w.refresh_period == 0)
-        log(f"saga: {1e3 * res['saga_ms'] / K:.2f} us/step over {K} steps ({res['refresh_steps']} refresh)")
+        log(f"saga: {pct(res['saga_us'], 50):.2f} us/step over {K} steps ({res['refresh_steps']} refresh)")
     if args.only in ("all", "steady"):
         ms = time_graph(torch, lambda: [steady_step(t) for t in range(W, W + K)], args.reps)
-        res["steady_ms"] = median(ms)
-        log(f"fused steady-step kernel: {1e3 * res['steady_ms'] / K:.2f} us/launch")
+        res["steady_us"] = pct([1e3 * m / K for m in ms], 50)
+        log(f"steady step (threshold reused): {res['steady_us']:.2f} us/step")
+    if args.only in ("all", "select"):
+        ms = time_graph(torch, lambda: [select_only(t) for t in range(W, W + K)], args.reps)
+        res["select_us"] = pct([1e3 * m / K for m in ms], 50)
+        log(f"select kernel alone: {res['select_us']:.2f} us/launch")
+        ms = time_graph(torch, lambda: [combine_only(t) for t in range(W, W + K)], args.reps)
+        res["combine_us"] = pct([1e3 * m / K for m in ms], 50)
+        log(f"combine kernel alone: {res['combine_us']:.2f} us/launch")
 
-    # survivor statistics at a stale step of set 0 (union of kept rows per value head)
+    # survivor statistics at a step that reuses the threshold of set 0
     cap = 8 * w.N
     sel_count = torch.zeros(w.batch, w.h_q, dtype=torch.int32, device=dev)
     sel_idx = torch.full((w.batch, w.h_q, cap), -1, dtype=torch.int32, device=dev)
+    flags = torch.zeros(w.batch, w.h_q, dtype=torch.int32, device=dev)
     api.decode_attn(qs[0], ks[0], vs[0], l_kv, taus[0], N=w.N, refresh_period=w.refresh_period,
-                    step=1, max_l_kv=L, out=out, sel_count=sel_count, sel_idx=sel_idx, workspace=ws)
+                    step=1, max_l_kv=L, out=out, sel_count=sel_count, sel_idx=sel_idx, flags=flags, workspace=ws)
     torch.cuda.synchronize()
     counts = sel_count.cpu().numpy()
     idx = sel_idx.cpu().numpy()
+    forced = int(((flags.cpu().numpy() & api.FLAG_FORCED) != 0).sum())
     union_rows = []
     for b in range(w.batch):
         for vh in range(w.h_v):
@@ -224,6 +336,7 @@ def main() -> int:
             union_rows.append(len(rows))
     bytes_v = bytemodel.selected_value_bytes(union_rows, w.d, es)
     bytes_v_per_head = int(counts.sum()) * w.d * es
+    bytes_step = bytes_k + bytes_v
 
     dense = {}
     if w.dense_h_kv and args.only in ("all", "dense"):
@@ -247,20 +360,29 @@ def main() -> int:
             dense_step(t)
         torch.cuda.synchronize()
         ms = time_graph(torch, lambda: [dense_step(t) for t in range(W, W + K)], args.reps)
-        dense = {"h_kv": wd.h_k, "ms": median(ms), "bytes": bytes_d, "sets": Rd}
-        log(f"dense GQA (h_kv={wd.h_k}): {1e3 * dense['ms'] / K:.2f} us/step")
+        dense = {"h_kv": wd.h_k, "us": pct([1e3 * m / K for m in ms], 50), "bytes": bytes_d, "sets": Rd}
+        log(f"dense GQA (h_kv={wd.h_k}): {dense['us']:.2f} us/step")
         del kd, vd
 
-    if "saga_ms" not in res:
-        print(json.dumps({"metric": METRIC, "partial": args.only, "steady_ms": res.get("steady_ms"),
-                          "dense": dense}))
+    if "saga_us" not in res:
+        print(json.dumps({"metric": METRIC, "partial": args.only, **res, "dense": dense}))
         return 0
 
-    t_step = res["saga_ms"] / K * 1e-3
-    bytes_step = bytes_k + bytes_v
+    ceil = read_probe(torch, 5) if args.only == "all" else None
+    if ceil:
+        log(f"read ceilings (torch.sum): 1 GiB {ceil['gib_read_gbs']:.0f} GB/s, "
+            f"32 MiB {ceil['mib32_read_gbs']:.0f} GB/s")
+    us = pct(res["saga_us"], 50)
+    t_step = us * 1e-6
     step_gbs = bytes_step / t_step / 1e9
-    st_s = res["steady_ms"] / K * 1e-3 if "steady_ms" in res else None
-    achieved = bytes_step / st_s / 1e9 if st_s else None
+    traffic, traffic_src = recorded_traffic()
+    roof = None
+    if "select_us" in res:
+        achieved = bytes_step / (res["select_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": DOMINANT,
+                "kernel_us": res["select_us"], "bytes_per_launch": bytes_step,
+                "traffic_source": traffic_src}
     line = {
         "metric": METRIC,
         "value": 1.0 / t_step,
@@ -277,7 +399,12 @@ def main() -> int:
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_k": w.h_k, "h_v": w.h_v,
                    "d": w.d, "l_kv": L, "N": w.N, "refresh_period": w.refresh_period,
                    "accumulate": "f32", "rotating_sets": R, "dense_h_kv": w.dense_h_kv},
-        "us_per_step": t_step * 1e6,
+        "us_per_step": us,
+        "us_per_step_p10": pct(res["saga_us"], 10),
+        "us_per_step_p90": pct(res["saga_us"], 90),
+        "us_steady_step": res.get("steady_us"),
+        "us_select_kernel": res.get("select_us"),
+        "us_combine_kernel": res.get("combine_us"),
         "bytes_per_step": bytes_step,
         "bytes_k": bytes_k,
         "bytes_selected_v_union": bytes_v,
@@ -287,15 +414,13 @@ def main() -> int:
         "refresh_steps_timed": res["refresh_steps"],
         "survivors_mean": float(counts.mean()),
         "survivors_max": int(counts.max()),
-        "saga_ms_replays": res["saga_ms_all"],
-        "roofline": {"kernel": "k_decode_fused (steady step: K stream, compare, V gather, merge)",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
-                     "kernel_us": st_s * 1e6 if st_s else None, "bytes_per_launch": bytes_step},
+        "forced_refresh_rows": forced,
+        "read_ceiling": ceil,
+        "roofline": roof,
     }
     if dense:
-        td = dense["ms"] / K * 1e-3
-        line["dense_gqa"] = {"h_kv": dense["h_kv"], "us_per_step": td * 1e6, "steps_per_s": 1.0 / td,
+        td = dense["us"] * 1e-6
+        line["dense_gqa"] = {"h_kv": dense["h_kv"], "us_per_step": dense["us"], "steps_per_s": 1.0 / td,
                              "bytes_per_step": dense["bytes"], "gbs": dense["bytes"] / td / 1e9,
                              "roofline_frac": dense["bytes"] / td / 1e9 / HBM_PEAK_GBS,
                              "rotating_sets": dense["sets"]}

@@ -130,6 +130,27 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
                                int32_t* sel_idx, int32_t sel_cap, int32_t* flags,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two kernels of a step that reuses the threshold, callable separately on one
+ * stream with one workspace (saga_decode_attn with step % refresh_period != 0 is
+ * exactly saga_select_gather followed by saga_split_combine).
+ * saga_select_gather: eq. (2) logits of every cached key, the comparison with tau,
+ *   and for each run of cached keys (the kernel's chunk) and query head the part of
+ *   eq. (7) over the chunk's kept entries, relative to the chunk's largest kept logit
+ *   m_c: sum exp(A_i - m_c) V[i,:] and sum exp(A_i - m_c), into the workspace.
+ * saga_split_combine: the log-sum-exp merge of those chunk parts into out
+ *   (O = sum_c e_c o_c / sum_c e_c z_c, e_c = exp(m_c - max_c m_c)); outputs as in
+ *   saga_decode_attn (flags bit 0 is never set here). q, k, N and tau are needed for
+ *   the forced refresh of a row that kept nothing. */
+saga_status saga_select_gather(const saga_shape* s, const void* q, const void* k,
+                               const void* v, const int32_t* l_kv, int32_t max_l_kv,
+                               const float* tau, void* workspace, size_t workspace_bytes,
+                               void* stream);
+saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k,
+                               const void* v, const int32_t* l_kv, int32_t max_l_kv,
+                               int32_t N, float* tau, void* out, int32_t* sel_count,
+                               int32_t* sel_idx, int32_t sel_cap, int32_t* flags,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,8 @@ from .build import LIB_PATH
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, BF16 = 0, 1
 EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "saga_decode_attn",
-           "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather")
+           "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather",
+           "saga_select_gather", "saga_split_combine")
 FLAG_REFRESHED, FLAG_FORCED = 1, 2
 
 
@@ -46,6 +47,8 @@ _SIGS = {
     "saga_dense_gqa_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_qk_select": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_sparse_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_select_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_split_combine": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
 }
 
 
@@ -225,6 +228,31 @@ def sparse_gather(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
                                   _ptr(tau), _ptr(out), _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags),
                                   _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
     _check(st, "saga_sparse_gather")
+    return out
+
+
+def select_gather(q, k, v, l_kv, tau, *, max_l_kv: Optional[int] = None, workspace: Optional[Workspace] = None,
+                  scale: float = 0.0, stream=None):
+    """saga_select_gather: scoring, threshold comparison and the per-chunk parts of the
+    softmax-weighted value sum (into the workspace)."""
+    shape, max_l_kv, _ = _prep(q, k, v, l_kv, tau, q, None, max_l_kv, scale)
+    ws = _ws(workspace, shape, 1, max_l_kv, q.device)
+    st = lib().saga_select_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv,
+                                  _ptr(tau), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_select_gather")
+
+
+def split_combine(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None, out=None, out_dtype=None,
+                  sel_count=None, sel_idx=None, flags=None, workspace: Optional[Workspace] = None,
+                  scale: float = 0.0, stream=None):
+    """saga_split_combine: merges the chunk parts left by saga_select_gather into `out`."""
+    shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
+    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    ws = _ws(workspace, shape, N, max_l_kv, q.device)
+    st = lib().saga_split_combine(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
+                                  _ptr(tau), _ptr(out), _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags),
+                                  _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_split_combine")
     return out
 
 

@@ -14,6 +14,18 @@ SOURCES = [os.path.join(HERE, "csrc", "saga_api.hip")]
 ARCH = "gfx950"
 
 
+def source_digest() -> str:
+    """sha256 over the library's sources (csrc/ and include/), in name order: names a
+    build of the kernels, e.g. for measurements that are valid for one kernel only."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(HERE, "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

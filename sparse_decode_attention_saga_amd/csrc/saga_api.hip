@@ -59,7 +59,7 @@ struct Layout {
   int rows, ch, nch, P;  // P: threshold-candidate blocks per row
   long long lpad;
   size_t hist, cand_cnt;
-  size_t scores, surv_idx, surv_val, chunk_cnt, chunk_max, part, total;
+  size_t scores, surv_idx, surv_val, chunk_hdr, part, total;
 };
 
 Layout layout(const saga_shape* s, int max_l_kv) {
@@ -82,9 +82,8 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   w.scores = take(rows * (size_t)w.lpad * 4);
   w.surv_idx = take(rows * (size_t)w.lpad * 4);
   w.surv_val = take(rows * (size_t)w.lpad * 4);
-  w.chunk_cnt = take(rows * (size_t)w.nch * 4);
-  w.chunk_max = take(rows * (size_t)w.nch * 4);
-  w.part = take(rows * (size_t)w.nch * (s->d + 4) * 4);  // chunk records (sparse and dense)
+  w.chunk_hdr = take(rows * (size_t)w.nch * sizeof(ChunkHdr));
+  w.part = take(rows * (size_t)w.nch * (s->d + 4) * 4);  // chunk records (sparse: D floats, dense: D+4)
   w.total = off;
   return w;
 }
@@ -107,8 +106,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.scores = at<float>(ws, w.scores);
   a.surv_idx = at<int32_t>(ws, w.surv_idx);
   a.surv_val = at<float>(ws, w.surv_val);
-  a.chunk_cnt = at<int32_t>(ws, w.chunk_cnt);
-  a.chunk_max = at<float>(ws, w.chunk_max);
+  a.chunk_hdr = at<ChunkHdr>(ws, w.chunk_hdr);
   a.hist = at<unsigned>(ws, w.hist);
   a.cand_cnt = at<unsigned>(ws, w.cand_cnt);
   a.h_q = s->h_q;
@@ -292,6 +290,35 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
   if (max_l_kv > 0) launch_chunk_gather(s, w, a, hs);
   launch_combine(s, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false), hs);
+  return launched();
+}
+
+saga_status saga_select_gather(const saga_shape* s, const void* q, const void* k, const void* v,
+                               const int32_t* l_kv, int32_t max_l_kv, const float* tau, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !tau) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
+  if (st != SAGA_OK) return st;
+  const Layout w = layout(s, max_l_kv);
+  (void)hipGetLastError();
+  if (max_l_kv > 0)
+    launch_select(s, w, stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, 1), false, true,
+                  (hipStream_t)stream);
+  return launched();
+}
+
+saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k, const void* v,
+                               const int32_t* l_kv, int32_t max_l_kv, int32_t N, float* tau, void* out,
+                               int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap, int32_t* flags,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !tau || !out) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
+  if (st != SAGA_OK) return st;
+  if (sel_idx && sel_cap < 1) return SAGA_ERR_SHAPE;
+  const Layout w = layout(s, max_l_kv);
+  (void)hipGetLastError();
+  const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
+  launch_combine(s, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false), (hipStream_t)stream);
   return launched();
 }
 

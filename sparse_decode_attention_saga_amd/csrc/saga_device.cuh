@@ -149,7 +149,8 @@ template <int D> struct QK<float, D> {
 
 // Scaled logits of TPW consecutive 16-key tiles starting at key `wbase` of the key
 // head whose rows start at `kh`. Rows past the valid length L are clamped to L-1 for
-// the load (always in bounds); callers mask them. Requires L >= 1.
+// the load (always in bounds); callers mask them. Requires L >= 1. All TPW*kLoads
+// loads of a lane are in flight together (the K stream is latency-bound per wave).
 template <typename T, int D, int TPW>
 __device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& qk, const T* kh,
                                             int wbase, int L, int lane, float scale) {
@@ -159,6 +160,8 @@ __device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& 
     const int key = min(wbase + 16 * t + (lane & 15), L - 1);
     QK<T, D>::load_k(kb[t], kh + (size_t)key * D, lane);
   }
+  // every key load of the wave is issued before the first MFMA waits on one
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const floatx4 a = qk.mma(kb[t]);
@@ -199,20 +202,52 @@ __device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {
   return off + inc - x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+// Wave reductions with DPP row operations (gfx9): sums and maxima within quads, then
+// half-rows, rows of 16, and across the four rows with the row broadcasts of lanes
+// 15 and 31; the total ends in lane 63 and is read back as a wave-uniform value.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROWS, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+constexpr int kDppRor4 = 0x124;       // row_ror:4
+constexpr int kDppRor8 = 0x128;       // row_ror:8
+
+// Sum of lanes i, i+4, i+8, i+12 (mod 16) within each row of 16 lanes, in every lane.
+__device__ __forceinline__ float row_stride4_sum(float x) {
+  x += __int_as_float(dpp_i<kDppRor4>(0, __float_as_int(x)));
+  x += __int_as_float(dpp_i<kDppRor8>(0, __float_as_int(x)));
   return x;
+}
+
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int x, int neutral, Op op) {
+  x = op(x, dpp_i<kDppXor1>(neutral, x));
+  x = op(x, dpp_i<kDppXor2>(neutral, x));
+  x = op(x, dpp_i<kDppHalfMirror>(neutral, x));
+  x = op(x, dpp_i<kDppMirror>(neutral, x));
+  x = op(x, dpp_i<kDppBcast15, 0xA>(neutral, x));
+  x = op(x, dpp_i<kDppBcast31, 0xC>(neutral, x));
+  return __builtin_amdgcn_readlane(x, kWave - 1);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return __int_as_float(wave_reduce_i(__float_as_int(x), __float_as_int(-INFINITY), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return __int_as_float(wave_reduce_i(__float_as_int(x), 0, [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_reduce_i(x, 0, [](int a, int b) { return a + b; });
 }
 
 // tmp: float[NT/64] (int[NT/64] for the integer sum).

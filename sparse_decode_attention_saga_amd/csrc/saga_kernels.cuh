@@ -35,6 +35,15 @@ template <typename T, int D> struct StreamCfg {
 constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 for raw gfx9 buffers
 constexpr int kCoherent = 16;           // sc1 cache policy: coherent across the device's L2s
 
+// Summary of one chunk of one row (b, j), written by the select kernels: the number
+// of kept entries, the largest kept logit m and, once gathered, sum_i exp(A_i - m).
+struct __align__(16) ChunkHdr {
+  int32_t cnt;
+  float mx;
+  float z;
+  int32_t unused;
+};
+
 // ----------------------------------------------------------------------------
 // Shared argument blocks (passed by value).
 
@@ -46,8 +55,7 @@ struct StreamArgs {
   float* scores;           // [B*h_q, lpad] fp32 logits (refresh steps and forced refresh)
   int32_t* surv_idx;       // [B*h_q, lpad] kept indices, one CH-segment per chunk
   float* surv_val;         // [B*h_q, lpad] kept logits; also the threshold candidates
-  int32_t* chunk_cnt;      // [B*h_q, nch] kept entries per chunk
-  float* chunk_max;        // [B*h_q, nch] largest kept logit per chunk
+  ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
   unsigned* hist;          // [B*h_q, 256] top-digit histogram (zero between calls)
   unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
   int h_q, h_k, g_k, htiles, l_max, nch, N;
@@ -55,7 +63,7 @@ struct StreamArgs {
   long long lpad;
   float scale;
   const void* v;           // [B, h_v, l_max, D] (gathering kernels)
-  float* part;             // [B*h_q, nch, D+4] chunk records: [1] sum w, [4..4+D) sum w*v
+  float* part;             // [B*h_q, D/16, nch, 16] chunk records: sum w*v, 16 columns per slice
   int h_v;
 };
 
@@ -71,9 +79,10 @@ template <int CH> struct KeptLds {
 
 // Eq. (7) split over chunks of keys: the 16-lane group h of the block takes head
 // j0+h of the tile, gathers the value rows of its kept entries from value head v(j)
-// and writes the chunk record of row (b, j): [1] = sum_i w_i and [4..4+D) =
-// sum_i w_i V[i,:], w_i = exp(A_i - m), m = the chunk's largest kept logit of the row
-// (so every w_i <= 1). Rows without kept entries in the chunk write nothing.
+// and writes the chunk record of row (b, j): sum_i w_i V[i,:] into the D/16 column
+// slices and sum_i w_i into the chunk header, w_i = exp(A_i - m), m = the chunk's
+// largest kept logit of the row (so every w_i <= 1). Rows without kept entries in
+// the chunk write nothing.
 template <typename T, int D, int CH>
 __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const StreamArgs& a, int b, int j0, int nh,
                                               int c) {
@@ -136,14 +145,17 @@ __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const Strea
     z += __shfl_xor(z, o);
   }
   if (sub != 0) return;
-  float* rec = a.part + ((long long)(b * a.h_q + j) * a.nch + c) * (D + 4);
+  const long long row = (long long)b * a.h_q + j;
+  float* rec = a.part + row * (D / 16) * a.nch * 16 + (long long)c * 16;
 #pragma unroll
   for (int p = 0; p < PPL; ++p)
 #pragma unroll
-    for (int e = 0; e < EPL; e += 4)
-      *reinterpret_cast<float4*>(rec + 4 + (pc + 16 * p) * EPL + e) =
+    for (int e = 0; e < EPL; e += 4) {
+      const int col = (pc + 16 * p) * EPL + e;
+      *reinterpret_cast<float4*>(rec + (long long)(col >> 4) * a.nch * 16 + (col & 15)) =
           make_float4(acc[p][e], acc[p][e + 1], acc[p][e + 2], acc[p][e + 3]);
-  if (gl == 0) rec[1] = z;
+    }
+  if (gl == 0) a.chunk_hdr[row * a.nch + c].z = z;
 }
 
 // Source of the logits of k_qk_select.
@@ -199,30 +211,43 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   }
   __syncthreads();
 
-  const long long seg = (long long)(row0 + hh) * a.lpad + base;
+  // this lane's kept entries as a bit mask (bit 4t+r: key wbase+16t+4kq+r), one LDS
+  // atomic per lane for their slots, then one short loop over the set bits
+  static_assert(TPW * 4 <= 32, "kept mask holds 32 entries");
+  unsigned pm = 0u;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = wbase + 16 * t + 4 * kq + r;
-      const float v = sc[t][r];
-      if (live && key < L && v >= tau_l) {
-        const int slot = atomicAdd(&kl.cnt[hh], 1);
-        a.surv_idx[seg + slot] = key;
-        a.surv_val[seg + slot] = v;
-        atomicMax(&kl.mx[hh], order_key(v));
-        if constexpr (GATHER) {
-          kl.off[hh][slot] = (uint16_t)(key - base);
-          kl.val[hh][slot] = v;
-        }
-      }
+      if (live && key < L && sc[t][r] >= tau_l) pm |= 1u << (4 * t + r);
     }
+  if (pm) {
+    const long long seg = (long long)(row0 + hh) * a.lpad + base;
+    int slot = atomicAdd(&kl.cnt[hh], __popc(pm));
+    float vmax = -INFINITY;
+    do {
+      const int bit = __builtin_ctz(pm);
+      pm &= pm - 1u;
+      float v = sc[0][0];
+#pragma unroll
+      for (int e = 1; e < TPW * 4; ++e) v = (bit == e) ? sc[e >> 2][e & 3] : v;
+      const int key = wbase + 16 * (bit >> 2) + 4 * kq + (bit & 3);
+      a.surv_idx[seg + slot] = key;
+      a.surv_val[seg + slot] = v;
+      if constexpr (GATHER) {
+        kl.off[hh][slot] = (uint16_t)(key - base);
+        kl.val[hh][slot] = v;
+      }
+      vmax = fmaxf(vmax, v);
+      ++slot;
+    } while (pm);
+    atomicMax(&kl.mx[hh], order_key(vmax));
   }
   __syncthreads();
   if (tid < nh) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
-    a.chunk_cnt[o] = kl.cnt[tid];
-    a.chunk_max[o] = order_key_to_f32(kl.mx[tid]);
+    *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
   }
   if constexpr (GATHER) chunk_records<T, D, CH>(kl, a, b, j0, nh, c);
 }
@@ -244,9 +269,9 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
   const int row0 = b * a.h_q + j0;
   __shared__ KeptLds<CH> kl;
   if (tid < nh) {
-    const long long o = (long long)(row0 + tid) * a.nch + c;
-    kl.cnt[tid] = a.chunk_cnt[o];
-    kl.mx[tid] = order_key(a.chunk_max[o]);
+    const ChunkHdr h = a.chunk_hdr[(long long)(row0 + tid) * a.nch + c];
+    kl.cnt[tid] = h.cnt;
+    kl.mx[tid] = order_key(h.mx);
   }
   __syncthreads();
   for (int e = tid; e < nh * CH; e += kBlock) {
@@ -598,32 +623,53 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
 // Merge of the chunk records of each row (b, j) (eq. (7) reassembled from its
 // chunks): M = the row's largest kept logit (the maximum of the chunk maxima),
 // O = sum_c e_c o_c / sum_c e_c z_c with e_c = exp(m_c - M) over the chunks that kept
-// something. Block x takes output columns [16x, 16x+16); thread t takes chunks t,
-// t+256, ... . The kept indices are exported in the same pass (chunk c by block
-// c mod gridDim.x). A row that kept nothing is recomputed exactly by block 0
-// (forced refresh). The first kChunkRegs chunks of a thread are read in one round
-// of independent loads (count, maximum, record slice, first kept indices) whether
-// or not the chunk kept anything; the values of empty chunks are never used.
-// grid = (D / 16, h_q, B), block = 256.
-constexpr int kChunkRegs = 2;  // chunks per thread read speculatively
+// something. Block x takes output columns [16x, 16x+16) (column slice x of the
+// records, contiguous over chunks); lane quarter q = t mod 4 of thread t takes
+// columns 16x+4q..16x+4q+3 of chunks t/4, t/4+64, ..., so each wave load reads 1 KB
+// of consecutive records. Headers, slices and the first kept indices of the first
+// kCombRegs*64 chunks are read in one round of independent loads, issued with l_kv
+// and whether or not a chunk kept anything; values of chunks past l_kv or without
+// kept entries are never used. The kept indices are exported in the same pass
+// (chunk c by block c mod gridDim.x). A row that kept nothing is recomputed exactly
+// by block 0 (forced refresh). grid = (D / 16, h_q, B), block = 256.
+constexpr int kCombRegs = 8;  // chunk slots per thread read speculatively
 
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   constexpr int CH = StreamCfg<T, D>::kChunk;
-  constexpr int AS = D + 4;
+  constexpr int CB = D / 16;
+  constexpr int kSlots = kBlock / 4;  // chunks per pass of the block
   const StreamArgs& sa = a.s;
-  const int cb = blockIdx.x, j = blockIdx.y, b = blockIdx.z, CB = gridDim.x;
+  const int cb = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const long long row = (long long)b * sa.h_q + j;
-  const int L = min(sa.l_kv[b], sa.max_l_kv);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int qd = tid & 3, r0 = tid >> 2;
   const int col = cb * 16;
 
   __shared__ int s_itmp[kWaves];
   __shared__ float s_ftmp[kWaves];
-  __shared__ float s_acc[kWaves][17];
+  __shared__ float s_acc[kWaves][4][17];
   __shared__ float s_red[kWaves][D];
   __shared__ float s_z[kWaves];
 
+  const ChunkHdr* hdr = sa.chunk_hdr + row * sa.nch;
+  const float4* sl = reinterpret_cast<const float4*>(sa.part + (row * CB + cb) * (long long)sa.nch * 16) + qd;
+  const int32_t* kept = sa.surv_idx + row * sa.lpad;
+  int32_t* exp_idx = a.sel_idx ? a.sel_idx + row * a.sel_cap : nullptr;
+  const bool exporter = exp_idx != nullptr && qd == 0;
+
+  float4 hreg[kCombRegs], xreg[kCombRegs];
+  int4 ireg[kCombRegs];
+#pragma unroll
+  for (int k = 0; k < kCombRegs; ++k) {
+    const int c = k * kSlots + r0;
+    if (c < sa.nch) {
+      hreg[k] = *reinterpret_cast<const float4*>(hdr + c);
+      xreg[k] = sl[(long long)c * 4];
+      if (exporter && c % CB == cb) ireg[k] = *reinterpret_cast<const int4*>(kept + (long long)c * CH);
+    }
+  }
+  const int L = min(sa.l_kv[b], sa.max_l_kv);
   if (L <= 0) {
     if (tid < 16) store_out<D>(a, row, col + tid, 0.f);
     if (cb == 0 && tid == 0) {
@@ -633,75 +679,47 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
     return;
   }
   const int nch_b = (L + CH - 1) / CH;
-  const int32_t* cnt = sa.chunk_cnt + row * sa.nch;
-  const float* cmax = sa.chunk_max + row * sa.nch;
-  const float* rp = sa.part + row * sa.nch * AS;
-  const int32_t* kept = sa.surv_idx + row * sa.lpad;
-  int32_t* exp_idx = a.sel_idx ? a.sel_idx + row * a.sel_cap : nullptr;
-
-  int nreg[kChunkRegs];
-  float mreg[kChunkRegs], zreg[kChunkRegs];
-  float4 xreg[kChunkRegs][4];
-  int4 ireg[kChunkRegs];
-#pragma unroll
-  for (int k = 0; k < kChunkRegs; ++k) {
-    const int c = tid + k * kBlock;
-    nreg[k] = 0;
-    if (c < nch_b) {
-      nreg[k] = cnt[c];
-      mreg[k] = cmax[c];
-      const float* pc = rp + (long long)c * AS;
-      const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + col);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xreg[k][q] = p4[q];
-      zreg[k] = pc[1];
-      if (exp_idx && c % CB == cb) ireg[k] = *reinterpret_cast<const int4*>(kept + (long long)c * CH);
-    }
-  }
+  int nreg[kCombRegs];
   float m = -INFINITY;
   int tsum = 0;
 #pragma unroll
-  for (int k = 0; k < kChunkRegs; ++k) {
+  for (int k = 0; k < kCombRegs; ++k) {
+    nreg[k] = (k * kSlots + r0 < nch_b) ? __float_as_int(hreg[k].x) : 0;
+    if (nreg[k] > 0) m = fmaxf(m, hreg[k].y);
     tsum += nreg[k];
-    if (nreg[k] > 0) m = fmaxf(m, mreg[k]);
   }
-  for (int c = tid + kChunkRegs * kBlock; c < nch_b; c += kBlock) {
-    const int n = cnt[c];
-    tsum += n;
-    if (n > 0) m = fmaxf(m, cmax[c]);
+  for (int c = kCombRegs * kSlots + r0; c < nch_b; c += kSlots) {
+    const ChunkHdr h = hdr[c];
+    if (h.cnt > 0) m = fmaxf(m, h.mx);
+    tsum += h.cnt;
   }
   const float M = block_max(m, s_ftmp);
   int total;
-  int pos = block_excl_scan(tsum, s_itmp, total);
+  int pos = block_excl_scan(qd == 0 ? tsum : 0, s_itmp, total);
   if (total == 0) {
     if (cb == 0) exact_row<T, D, kBlock>(a, b, j, L, true, s_red, s_z);
     return;
   }
 
-  float o[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
-  auto add = [&](const float4 (&x)[4], float zc, float mc) {
+  auto add = [&](const float4& x, float mc, float zc) {
     const float e = expf(mc - M);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o[4 * q] += e * x[q].x;
-      o[4 * q + 1] += e * x[q].y;
-      o[4 * q + 2] += e * x[q].z;
-      o[4 * q + 3] += e * x[q].w;
-    }
-    z += e * zc;
+    o[0] += e * x.x;
+    o[1] += e * x.y;
+    o[2] += e * x.z;
+    o[3] += e * x.w;
+    if (qd == 0) z += e * zc;
   };
   auto export_rest = [&](int c, int n, int from) {
     for (int i = from; i < n && pos + i < a.sel_cap; ++i) exp_idx[pos + i] = kept[(long long)c * CH + i];
   };
 #pragma unroll
-  for (int k = 0; k < kChunkRegs; ++k) {
-    const int c = tid + k * kBlock, n = nreg[k];
+  for (int k = 0; k < kCombRegs; ++k) {
+    const int c = k * kSlots + r0, n = nreg[k];
     if (n > 0) {
-      add(xreg[k], zreg[k], mreg[k]);
-      if (exp_idx && c % CB == cb) {
+      add(xreg[k], hreg[k].y, hreg[k].z);
+      if (exporter && c % CB == cb) {
         const int first[4] = {ireg[k].x, ireg[k].y, ireg[k].z, ireg[k].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -711,35 +729,33 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
       pos += n;
     }
   }
-  for (int c = tid + kChunkRegs * kBlock; c < nch_b; c += kBlock) {
-    const int n = cnt[c];
-    if (n > 0) {
-      const float* pc = rp + (long long)c * AS;
-      const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + col);
-      float4 x[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = p4[q];
-      add(x, pc[1], cmax[c]);
-      if (exp_idx && c % CB == cb) export_rest(c, n, 0);
-      pos += n;
+  for (int c = kCombRegs * kSlots + r0; c < nch_b; c += kSlots) {
+    const ChunkHdr h = hdr[c];
+    if (h.cnt > 0) {
+      add(sl[(long long)c * 4], h.mx, h.z);
+      if (exporter && c % CB == cb) export_rest(c, h.cnt, 0);
+      pos += h.cnt;
     }
   }
+  // lanes of one quarter within each row of 16 lanes, then rows and waves via LDS
 #pragma unroll
-  for (int e = 0; e < 16; ++e) o[e] = wave_sum(o[e]);
-  z = wave_sum(z);
-  if (lane == 0) {
+  for (int e = 0; e < 4; ++e) o[e] = row_stride4_sum(o[e]);
+  z = row_stride4_sum(z);
+  if ((lane & 15) < 4) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s_acc[wv][e] = o[e];
-    s_acc[wv][16] = z;
+    for (int e = 0; e < 4; ++e) s_acc[wv][lane >> 4][4 * qd + e] = o[e];
+    if (qd == 0) s_acc[wv][lane >> 4][16] = z;
   }
   __syncthreads();
   if (tid < 16) {
     float oo = 0.f, zz = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      oo += s_acc[w][tid];
-      zz += s_acc[w][16];
-    }
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        oo += s_acc[w][r][tid];
+        zz += s_acc[w][r][16];
+      }
     store_out<D>(a, row, col + tid, oo / zz);
   }
   if (cb == 0 && tid == 0) {

@@ -94,6 +94,12 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.saga_qk_select(ctypes.byref(s), FAKE, None, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_NULL
     assert lib.saga_sparse_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, None, None, None, 0,
                                   None, FAKE, big, None) == api.ERR_NULL
+    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, None, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_NULL
+    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 16, None) == api.ERR_WORKSPACE
+    assert lib.saga_split_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 0, FAKE, FAKE, None, None, 0,
+                                  None, FAKE, big, None) == api.ERR_SHAPE
+    assert lib.saga_split_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, FAKE, None, FAKE, 0,
+                                  None, FAKE, big, None) == api.ERR_SHAPE
     # dense GQA needs as many value heads as key heads
     assert lib.saga_dense_gqa_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_SHAPE
     wide = shape(h_q=32, h_k=1, h_v=1)
