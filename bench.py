@@ -144,27 +144,49 @@ def copy_probe(torch, reps: int) -> int:
 
 
 def read_probe(torch, reps: int) -> dict:
-    """Streaming-read ceilings with torch's sum kernel: one 1 GiB read, and 32 MiB reads
-    (the size of the 128K key stream) from 32 different slices, each timed in a graph."""
+    """Streaming-read ceilings with the probe kernel of libsaga_probe.so (16-byte loads,
+    each block one contiguous range, 8 loads in flight per thread), for 256..2048 blocks
+    of 256 threads: one 1 GiB read per launch, and 32 MiB reads (the size of the 128K
+    key stream) from 32 different slices, one per launch. Each is timed as a graph of
+    launches, like the decode steps; the best grid is reported with the whole table."""
+    import ctypes
+    from sparse_decode_attention_saga_amd import build
+    lib = ctypes.CDLL(build.PROBE_PATH)
+    fn = lib.saga_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     n = 1 << 30
-    x = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
-    acc = torch.zeros(32, dtype=torch.float32, device="cuda:0")
-    sl = x.view(32, -1)
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda:0")
 
-    def big():
-        torch.sum(x.view(1, -1), dim=1, dtype=torch.float32, out=acc[0:1])
+    def launch(off, nbytes, blocks):
+        st = fn(x.data_ptr() + off, nbytes, sink.data_ptr(), blocks, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"saga_probe_stream_read failed ({st})")
 
-    def small():
-        for i in range(32):
-            torch.sum(sl[i:i + 1], dim=1, dtype=torch.float32, out=acc[i:i + 1])
+    table = {}
+    for blocks in (256, 512, 1024, 2048):
+        def big():
+            for _ in range(4):
+                launch(0, n, blocks)
 
-    big()
-    small()
-    torch.cuda.synchronize()
-    ms_big = min(time_graph(torch, lambda: [big() for _ in range(4)], reps)) / 4
-    ms_small = min(time_graph(torch, small, reps)) / 32
-    return {"kernel": "torch.sum (bf16 -> f32)", "gib_read_gbs": n / (ms_big * 1e-3) / 1e9,
-            "mib32_read_gbs": (n // 32) / (ms_small * 1e-3) / 1e9, "mib32_read_us": ms_small * 1e3}
+        def small():
+            for i in range(32):
+                launch(i * (n // 32), n // 32, blocks)
+
+        big()
+        small()
+        torch.cuda.synchronize()
+        ms_big = min(time_graph(torch, big, reps)) / 4
+        ms_small = min(time_graph(torch, small, reps)) / 32
+        table[blocks] = (n / (ms_big * 1e-3) / 1e9, (n // 32) / (ms_small * 1e-3) / 1e9, ms_small * 1e3)
+    best_big = max(table, key=lambda b: table[b][0])
+    best_small = max(table, key=lambda b: table[b][1])
+    return {"kernel": "k_stream_read (libsaga_probe.so)",
+            "gib_read_gbs": table[best_big][0], "gib_blocks": best_big,
+            "mib32_read_gbs": table[best_small][1], "mib32_read_us": table[best_small][2], "mib32_blocks": best_small,
+            "by_blocks": {str(b): {"gib_gbs": round(v[0], 1), "mib32_gbs": round(v[1], 1), "mib32_us": round(v[2], 3)}
+                          for b, v in table.items()}}
 
 
 def recorded_traffic():
@@ -370,7 +392,7 @@ def main() -> int:
 
     ceil = read_probe(torch, 5) if args.only == "all" else None
     if ceil:
-        log(f"read ceilings (torch.sum): 1 GiB {ceil['gib_read_gbs']:.0f} GB/s, "
+        log(f"read ceilings (probe kernel): 1 GiB {ceil['gib_read_gbs']:.0f} GB/s, "
             f"32 MiB {ceil['mib32_read_gbs']:.0f} GB/s")
     us = pct(res["saga_us"], 50)
     t_step = us * 1e-6

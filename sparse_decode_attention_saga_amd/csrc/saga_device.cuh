@@ -173,13 +173,23 @@ __device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& 
 // Block-wide helpers for blocks of NT threads (a multiple of 64, at most 1024).
 // Every thread of the block must call them. Scratch arrays are __shared__.
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
+template <int CTRL, int ROWS = 0xf, int BANKS = 0xf>
+__device__ __forceinline__ int dpp_add_src(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROWS, BANKS, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (gfx9 DPP: shifts within rows of 16 lanes,
+// then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int x, int /*lane*/) {
+  int s = x;
+  s += dpp_add_src<0x111>(0, x);             // row_shr:1
+  s += dpp_add_src<0x112>(0, x);             // row_shr:2
+  s += dpp_add_src<0x113>(0, x);             // row_shr:3  (lane i: x[i-3..i] within its row)
+  s += dpp_add_src<0x114, 0xf, 0xe>(0, s);   // row_shr:4, lanes 4..15 of each row
+  s += dpp_add_src<0x118, 0xf, 0xc>(0, s);   // row_shr:8, lanes 8..15 of each row
+  s += dpp_add_src<0x142, 0xa>(0, s);        // row_bcast:15 into rows 1 and 3
+  s += dpp_add_src<0x143, 0xc>(0, s);        // row_bcast:31 into rows 2 and 3
+  return s;
 }
 
 // Exclusive prefix sum in thread order; `total` gets the block sum. tmp: int[NT/64].
@@ -248,6 +258,34 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
   return wave_reduce_i(x, 0, [](int a, int b) { return a + b; });
+}
+
+// Block maximum of `mx` and exclusive prefix sum of `x` in thread order, with one
+// barrier; `total` gets the block sum. fmp: float[NT/64], itmp: int[NT/64]; neither
+// may be written again before the caller's next barrier.
+template <int NT = kBlock>
+__device__ __forceinline__ int block_max_excl_scan(float mx, int x, float* fmp, int* itmp, float& M, int& total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const float wm = wave_max(mx);
+  const int inc = wave_incl_scan(x, lane);
+  if (lane == kWave - 1) {
+    itmp[w] = inc;
+    fmp[w] = wm;
+  }
+  __syncthreads();
+  int off = 0, tot = 0;
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int t = itmp[i];
+    off += (i < w) ? t : 0;
+    tot += t;
+    m = fmaxf(m, fmp[i]);
+  }
+  M = m;
+  total = tot;
+  return off + inc - x;
 }
 
 // tmp: float[NT/64] (int[NT/64] for the integer sum).

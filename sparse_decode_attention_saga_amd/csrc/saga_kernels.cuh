@@ -693,9 +693,9 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
     if (h.cnt > 0) m = fmaxf(m, h.mx);
     tsum += h.cnt;
   }
-  const float M = block_max(m, s_ftmp);
+  float M;
   int total;
-  int pos = block_excl_scan(qd == 0 ? tsum : 0, s_itmp, total);
+  int pos = block_max_excl_scan(m, qd == 0 ? tsum : 0, s_ftmp, s_itmp, M, total);
   if (total == 0) {
     if (cb == 0) exact_row<T, D, kBlock>(a, b, j, L, true, s_red, s_z);
     return;
