@@ -232,6 +232,76 @@ def rocprof_summary(paths) -> int:
     return 0
 
 
+def sweep(torch, args) -> int:
+    """Decode step time of SAGA + Atop-N and of the dense GQA kernel over the sweep grid
+    (Qwen2.5-1.5B-shaped heads, l_kv in 4K..128K, N in {128, 512, 2048}, refresh period
+    in {1, 8, 64}): where sparse selection stops paying off. Each point rotates enough
+    input sets that the touched bytes exceed the Infinity Cache."""
+    from sparse_decode_attention_saga_amd import api
+    from sparse_decode_attention_saga_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    api.lib()
+    base_w = wl.SWEEP
+    K, W = args.steps, args.warmup
+    rows = []
+    for L in wl.SWEEP_L:
+        x = wl.generate(base_w, seed=0, lengths=[L], l_max=L)
+        q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+        l_kv = torch.from_numpy(x.l_kv).to(dev)
+        touched = k0.numel() * 2 + base_w.h_q * max(wl.SWEEP_N) * base_w.d * 2
+        R = max(2, math.ceil((768 << 20) / touched))
+        while any(math.gcd(R, n) != 1 for n in wl.SWEEP_PERIOD):
+            R += 1
+        ks = k0.unsqueeze(0).repeat(R, 1, 1, 1, 1)
+        vs = v0.unsqueeze(0).repeat(R, 1, 1, 1, 1)
+        out = torch.empty_like(q0)
+        wsp = None
+        wd = base_w.with_(h_k=base_w.dense_h_kv, h_v=base_w.dense_h_kv, workload_id=base_w.workload_id + 100)
+        xd = wl.generate(wd, seed=0, lengths=[L], l_max=L)
+        qd = xd.q.to(dev)
+        Rd = max(2, math.ceil((768 << 20) / (2 * xd.k.numel() * 2)))
+        kd = xd.k.to(dev).unsqueeze(0).repeat(Rd, 1, 1, 1, 1)
+        vd = xd.v.to(dev).unsqueeze(0).repeat(Rd, 1, 1, 1, 1)
+        wsd = api.Workspace(api.make_shape(qd, kd[0], vd[0]), 1, L, dev)
+        outd = torch.empty_like(qd)
+
+        def dense_step(t):
+            api.dense_gqa_attn(qd, kd[t % Rd], vd[t % Rd], l_kv, max_l_kv=L, out=outd, workspace=wsd)
+
+        for t in range(W):
+            dense_step(t)
+        torch.cuda.synchronize()
+        dense_us = pct([1e3 * m / K for m in time_graph(torch, lambda: [dense_step(t) for t in range(K)],
+                                                        args.reps)], 50)
+        for N in wl.SWEEP_N:
+            wsp = api.Workspace(api.make_shape(q0, k0, v0), N, L, dev)
+            for n in wl.SWEEP_PERIOD:
+                taus = torch.zeros(R, 1, base_w.h_q, dtype=torch.float32, device=dev)
+                for r in range(R):
+                    api.refresh_threshold(q0, ks[r], l_kv, taus[r], N=N, max_l_kv=L, workspace=wsp)
+
+                def step(t):
+                    r = t % R
+                    api.decode_attn(q0, ks[r], vs[r], l_kv, taus[r], N=N, refresh_period=n, step=t,
+                                    max_l_kv=L, out=out, workspace=wsp)
+
+                for t in range(W):
+                    step(t)
+                torch.cuda.synchronize()
+                us = pct([1e3 * m / K for m in time_graph(torch, lambda: [step(t) for t in range(W, W + K)],
+                                                          args.reps)], 50)
+                rows.append({"l_kv": L, "N": N, "refresh_period": n, "saga_us": us, "dense_us": dense_us,
+                             "speedup": dense_us / us, "sets": R})
+                log(f"l_kv={L:6d} N={N:4d} n={n:2d}: saga {us:7.2f} us  dense {dense_us:7.2f} us  "
+                    f"speedup {dense_us / us:5.2f}")
+        del ks, vs, kd, vd
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": rows, "steps": K, "warmup": W, "workload": base_w.name,
+                      "dense_h_kv": base_w.dense_h_kv}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +318,8 @@ def main() -> int:
                     help="copy: a plain device copy of 256 MiB (counter calibration); read: read ceilings")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV",
                     help="print per-kernel averages of rocprofv3 csv files and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="SAGA vs dense step time over l_kv x N x refresh period (one JSON line)")
     args = ap.parse_args()
 
     if args.rocprof_summary:
@@ -266,6 +338,8 @@ def main() -> int:
     if args.probe == "read":
         print(json.dumps({"probe": "read", **read_probe(torch, max(args.reps, 3))}), flush=True)
         return 0
+    if args.sweep:
+        return sweep(torch, args)
 
     from sparse_decode_attention_saga_amd import api
     from sparse_decode_attention_saga_amd import bytemodel

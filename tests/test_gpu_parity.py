@@ -136,6 +136,33 @@ def test_multistep_append_and_drift():
         s.drift()
 
 
+# --- the multi-step sweep grid: every context length, top-N size and period ------
+
+SWEEP_GRID = [(L, N, n) for L in wl.SWEEP_L for N in wl.SWEEP_N for n in wl.SWEEP_PERIOD]
+
+
+@pytest.mark.parametrize("L,N,n", SWEEP_GRID)
+def test_sweep_grid_point(L, N, n):
+    # four decode steps ending at context L (rows appended and q drifting between
+    # steps), each side keeping its own threshold state
+    say(f"sweep point l_kv={L} N={N} n={n}")
+    w = wl.SWEEP.with_(N=N, refresh_period=n)
+    s = wl.DecodeStream(w, seed=1, l0=L - 3, l_max=L)
+    g = GpuCase(s.inputs(), N, max_l_kv=L)
+    tau_o = None
+    for t in range(4):
+        x = s.inputs()
+        if t:
+            g.refresh_inputs(x)
+        got = g.step(n, t)
+        ref = oracle_step(x, N, n, t, tau_in=tau_o)
+        compare(got, ref, x, w.dtype, check_tau=(t % n == 0))
+        tau_o = ref.tau
+        if t < 3:
+            s.append(1)
+            s.drift()
+
+
 # --- forced paths ------------------------------------------------------------------
 
 def test_empty_stale_selection_forces_refresh():
