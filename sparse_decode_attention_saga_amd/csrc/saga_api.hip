@@ -88,6 +88,26 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   return w;
 }
 
+// Blocks per chunk of the select kernel. Each kept entry costs one value-row load and
+// a block gathers with 16 groups of 16 lanes, 4 rows in flight per lane; a head with
+// about CH * N / l_kv kept entries per chunk is worth more than one group once that
+// exceeds two rounds of loads. The heads of a tile are then split over hsplit blocks
+// (each re-reads the chunk's keys, so no split where one group suffices).
+int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
+  if (max_l_kv <= 0) return 1;
+  const int g_k = s->h_q / s->h_k;
+  const int heads = g_k < 16 ? g_k : 16;
+  const int elem = s->dtype == SAGA_BF16 ? 2 : 4;
+  const int pieces = s->d * elem / 16;                 // 16-byte pieces per value row
+  const int rows_per_group_load = pieces >= 16 ? 1 : 16 / pieces;
+  const long long kept = (long long)w.ch * (N < max_l_kv ? N : max_l_kv) / max_l_kv;
+  const long long per_group = 2LL * rows_per_group_load * 4;  // two rounds of 4 loads
+  const long long groups = (kept + per_group - 1) / per_group;
+  const int owned = groups <= 1 ? 16 : (int)(16 / groups > 0 ? 16 / groups : 1);
+  int hsplit = (heads + owned - 1) / owned;
+  return hsplit < 1 ? 1 : hsplit;
+}
+
 template <typename P>
 P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
@@ -112,6 +132,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.h_q = s->h_q;
   a.h_k = s->h_k;
   a.g_k = s->h_q / s->h_k;
+  a.g_v = s->h_q / s->h_v;
   a.htiles = (a.g_k + 15) / 16;
   a.l_max = s->l_max;
   a.nch = w.nch;
@@ -119,6 +140,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.max_l_kv = max_l_kv;
   a.lpad = w.lpad;
   a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
+  a.hsplit = head_split(s, w, N, max_l_kv);
   return a;
 }
 
@@ -151,7 +173,8 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
 void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, bool gather,
                    hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, {
-    const dim3 grid = stream_grid(s, w);
+    dim3 grid = stream_grid(s, w);
+    grid.y *= a.hsplit;
     if (!gather)
       hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, false>), grid, dim3(kBlock), 0, st, a);
     else if (from_scores)
@@ -180,13 +203,11 @@ GatherArgs gather_args(const saga_shape* s, const StreamArgs& sa, float* tau, vo
                        int32_t* sel_idx, int32_t sel_cap, int32_t* flags, bool refreshed) {
   GatherArgs g{};
   g.s = sa;
-  g.v = sa.v;
   g.tau = tau;
   g.out = out;
   g.sel_count = sel_count;
   g.sel_idx = sel_idx;
   g.flags = flags;
-  g.h_v = s->h_v;
   g.sel_cap = sel_idx ? sel_cap : 0;
   g.out_bf16 = s->out_dtype == SAGA_BF16;
   g.refreshed = refreshed ? 1 : 0;

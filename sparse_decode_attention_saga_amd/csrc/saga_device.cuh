@@ -31,6 +31,7 @@ typedef uint16_t bf16_t;  // bf16 values are carried as their bit patterns
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
@@ -85,13 +86,15 @@ template <int D> struct QK<bf16_t, D> {
   static constexpr int kLoads = D / 32;  // 16-byte loads per lane per 16-key tile
   bf16x8 qf[kLoads];
 
-  // q of local heads 0..nh-1 starts at `qh` (rows of D values); heads >= nh read as 0.
+  // q of local heads 0..nh-1 starts at `qh` (rows of D values). Columns hh >= nh
+  // repeat head nh-1 (an unconditional load keeps every key load free to issue at
+  // once); callers never use those columns.
   __device__ __forceinline__ void load_q(const bf16_t* qh, int nh, int lane) {
-    const int hh = lane & 15, kq = lane >> 4;
+    const int hh = min(lane & 15, nh - 1), kq = lane >> 4;
 #pragma unroll
     for (int s = 0; s < kLoads; ++s) {
       V16 x;
-      x.u = (hh < nh) ? ld16(qh + (size_t)hh * D + 32 * s + 8 * kq) : make_uint4(0, 0, 0, 0);
+      x.u = ld16(qh + (size_t)hh * D + 32 * s + 8 * kq);
       qf[s] = x.h;
     }
   }
@@ -119,11 +122,11 @@ template <int D> struct QK<float, D> {
   float4 qf[kLoads];
 
   __device__ __forceinline__ void load_q(const float* qh, int nh, int lane) {
-    const int hh = lane & 15, kq = lane >> 4;
+    const int hh = min(lane & 15, nh - 1), kq = lane >> 4;
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
       V16 x;
-      x.u = (hh < nh) ? ld16(qh + (size_t)hh * D + 16 * u + 4 * kq) : make_uint4(0, 0, 0, 0);
+      x.u = ld16(qh + (size_t)hh * D + 16 * u + 4 * kq);
       qf[u] = make_float4(x.f[0], x.f[1], x.f[2], x.f[3]);
     }
   }

@@ -48,23 +48,26 @@ struct __align__(16) ChunkHdr {
 // Shared argument blocks (passed by value).
 
 struct StreamArgs {
+  // pointers first: the compiler may merge neighbouring field loads into one vector
+  // load, and a pointer rebuilt from a merged integer loses its global address space
+  // (its loads become flat loads, which the LDS waits of a thread also wait for)
   const void* q;           // [B, h_q, D]
   const void* k;           // [B, h_k, l_max, D]
+  const void* v;           // [B, h_v, l_max, D] (gathering kernels)
   const int32_t* l_kv;     // [B]
   const float* tau;        // [B*h_q] threshold (select kernels)
   float* scores;           // [B*h_q, lpad] fp32 logits (refresh steps and forced refresh)
   int32_t* surv_idx;       // [B*h_q, lpad] kept indices, one CH-segment per chunk
   float* surv_val;         // [B*h_q, lpad] kept logits; also the threshold candidates
   ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
+  float* part;             // [B*h_q, D/16, nch, 16] chunk records: sum w*v, 16 columns per slice
   unsigned* hist;          // [B*h_q, 256] top-digit histogram (zero between calls)
   unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
-  int h_q, h_k, g_k, htiles, l_max, nch, N;
-  int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   long long lpad;
+  int h_q, h_k, h_v, g_k, g_v, htiles, l_max, nch, N;  // g_k = h_q/h_k, g_v = h_q/h_v
+  int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
+  int hsplit;              // blocks sharing one chunk in k_qk_select (heads split among them)
   float scale;
-  const void* v;           // [B, h_v, l_max, D] (gathering kernels)
-  float* part;             // [B*h_q, D/16, nch, 16] chunk records: sum w*v, 16 columns per slice
-  int h_v;
 };
 
 // Kept entries of one chunk, per head of the tile, staged in LDS: offset of the key
@@ -77,43 +80,54 @@ template <int CH> struct KeptLds {
   unsigned mx[16];
 };
 
-// Eq. (7) split over chunks of keys: the 16-lane group h of the block takes head
-// j0+h of the tile, gathers the value rows of its kept entries from value head v(j)
-// and writes the chunk record of row (b, j): sum_i w_i V[i,:] into the D/16 column
-// slices and sum_i w_i into the chunk header, w_i = exp(A_i - m), m = the chunk's
-// largest kept logit of the row (so every w_i <= 1). Rows without kept entries in
-// the chunk write nothing.
+// Eq. (7) split over chunks of keys: the chunk record of row (b, j) for every head j
+// of the tile that this block owns (heads j0 + h with h mod hsplit == hs): the value
+// rows of its kept entries, gathered from value head v(j), summed as
+// sum_i w_i V[i,:] into the D/16 column slices and sum_i w_i into the chunk header,
+// w_i = exp(A_i - m), m = the chunk's largest kept logit of the row (every w_i <= 1).
+// The block's 16 groups of 16 lanes are spread over the owned heads (16 / owned
+// groups each, taking alternate kept entries); the groups of one head add their sums
+// in LDS. Rows without kept entries in the chunk write nothing. Called by every
+// thread of the block.
 template <typename T, int D, int CH>
 __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const StreamArgs& a, int b, int j0, int nh,
-                                              int c) {
+                                              int c, int hs, int hsplit) {
   constexpr int EPL = Unpack<T>::kN;                    // columns per 16-byte piece
   constexpr int PIECES = D / EPL;                       // pieces per value row
   constexpr int RPG = PIECES >= 16 ? 1 : 16 / PIECES;  // rows one group load covers
   constexpr int PPL = PIECES >= 16 ? PIECES / 16 : 1;   // pieces per lane per row
   constexpr int U = 4;                                  // loads in flight per lane
-  const int tid = threadIdx.x, h = tid >> 4, gl = tid & 15;
-  if (h >= nh) return;
-  const int n = kl.cnt[h];
-  if (n == 0) return;
+  constexpr int NG = kBlock / 16;                       // groups of 16 lanes
+  __shared__ float s_part[NG][D + 1];
+  const int nown = hsplit == 1 ? nh : (nh - hs + hsplit - 1) / hsplit;  // owned heads (uniform)
+  if (nown <= 0) return;
+  const int gph = NG / nown;                            // groups per owned head
+  const int tid = threadIdx.x, grp = tid >> 4, gl = tid & 15;
+  const int oh = gph == 1 ? grp : grp % nown, sg = gph == 1 ? 0 : grp / nown;
+  const bool act = gph == 1 ? grp < nown : sg < gph;
+  const int h = hs + (act ? oh : 0) * hsplit;
+  const int n = act ? kl.cnt[h] : 0;
+  if (gph == 1 && n == 0) return;                       // one group per head: no LDS merge follows
   const int sub = RPG > 1 ? gl / PIECES : 0;
   const int pc = RPG > 1 ? gl % PIECES : gl;
   const int j = j0 + h;
-  const int vh = (int)(((long long)j * a.h_v) / a.h_q);
+  const int vh = j / a.g_v;
   const int base = c * CH;
   const T* vrow = reinterpret_cast<const T*>(a.v) + ((size_t)(b * a.h_v + vh) * a.l_max + base) * D + pc * EPL;
-  const float m = order_key_to_f32(kl.mx[h]);
+  const float m = act ? order_key_to_f32(kl.mx[h]) : 0.f;
   float acc[PPL][EPL];
 #pragma unroll
   for (int p = 0; p < PPL; ++p)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[p][e] = 0.f;
   float z = 0.f;
-  for (int e0 = sub; e0 < n; e0 += RPG * U) {
+  // row slots k = sg, sg + gph, ... ; slot k holds entries k*RPG .. k*RPG + RPG-1
+  for (int k0 = sg; k0 * RPG < n; k0 += gph * U) {
     uint4 x[U][PPL];
     float w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = e0 + u * RPG;
+      const int e = (k0 + u * gph) * RPG + sub;
       w[u] = 0.f;
 #pragma unroll
       for (int p = 0; p < PPL; ++p) x[u][p] = make_uint4(0, 0, 0, 0);
@@ -144,18 +158,41 @@ __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const Strea
       for (int e = 0; e < EPL; ++e) acc[p][e] += __shfl_xor(acc[p][e], o);
     z += __shfl_xor(z, o);
   }
-  if (sub != 0) return;
-  const long long row = (long long)b * a.h_q + j;
-  float* rec = a.part + row * (D / 16) * a.nch * 16 + (long long)c * 16;
+  const long long nch16 = (long long)a.nch * 16;
+  if (gph == 1) {
+    // one group per head: it writes the record itself
+    if (sub != 0) return;
+    const long long row = (long long)b * a.h_q + j;
+    float* rec = a.part + row * (D / 16) * nch16 + (long long)c * 16;
 #pragma unroll
-  for (int p = 0; p < PPL; ++p)
+    for (int p = 0; p < PPL; ++p)
 #pragma unroll
-    for (int e = 0; e < EPL; e += 4) {
-      const int col = (pc + 16 * p) * EPL + e;
-      *reinterpret_cast<float4*>(rec + (long long)(col >> 4) * a.nch * 16 + (col & 15)) =
-          make_float4(acc[p][e], acc[p][e + 1], acc[p][e + 2], acc[p][e + 3]);
-    }
-  if (gl == 0) a.chunk_hdr[row * a.nch + c].z = z;
+      for (int e = 0; e < EPL; e += 4) {
+        const int col = (pc + 16 * p) * EPL + e;
+        *reinterpret_cast<float4*>(rec + (long long)(col >> 4) * nch16 + (col & 15)) =
+            make_float4(acc[p][e], acc[p][e + 1], acc[p][e + 2], acc[p][e + 3]);
+      }
+    if (gl == 0) a.chunk_hdr[row * a.nch + c].z = z;
+    return;
+  }
+  if (act && sub == 0) {
+#pragma unroll
+    for (int p = 0; p < PPL; ++p)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_part[grp][(pc + 16 * p) * EPL + e] = acc[p][e];
+    if (gl == 0) s_part[grp][D] = z;
+  }
+  __syncthreads();
+  for (int t = tid; t < nown * (D + 1); t += kBlock) {
+    const int o = t / (D + 1), col = t - o * (D + 1);
+    const int hh = hs + o * hsplit;
+    if (kl.cnt[hh] == 0) continue;
+    float sum = 0.f;
+    for (int q = 0; q < gph; ++q) sum += s_part[o + q * nown][col];
+    const long long row = (long long)b * a.h_q + j0 + hh;
+    if (col < D) a.part[row * (D / 16) * nch16 + (long long)(col >> 4) * nch16 + (long long)c * 16 + (col & 15)] = sum;
+    else a.chunk_hdr[row * a.nch + c].z = sum;
+  }
 }
 
 // Source of the logits of k_qk_select.
@@ -169,28 +206,41 @@ enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 // refresh step: the fp32 values the threshold was selected from); MODE
 // kFromKeysSpeculative (one sequence) issues the key loads before l_kv arrives.
 // With GATHER the block also writes the chunk records of eq. (7) (chunk_records).
-// grid = (nch, h_k * htiles, B), block = 256.
+// When hsplit > 1, hsplit blocks share each chunk: block hs compares and gathers only
+// the heads h of the tile with h mod hsplit == hs (every block computes all the
+// tile's logits; its duplicate key reads hit the cache).
+// grid = (nch, h_k * htiles * hsplit, B), block = 256.
 template <typename T, int D, int MODE, bool GATHER>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
   constexpr int CH = StreamCfg<T, D>::kChunk;
-  const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
-  const int g = gy / a.htiles, ht = gy - g * a.htiles;
-  const int j0 = g * a.g_k + ht * 16;
-  const int nh = min(16, a.g_k - ht * 16);
+  // every argument the key stream needs is read in one batch, before any arithmetic
+  // on them (otherwise the pointers' reads may wait behind the index arithmetic)
+  const T* const kbase = reinterpret_cast<const T*>(a.k);
+  const T* const qbase = reinterpret_cast<const T*>(a.q);
+  const int hsplit = a.hsplit, htiles = a.htiles, g_k = a.g_k, h_k = a.h_k, h_q = a.h_q;
+  const int l_max = a.l_max, max_l_kv = a.max_l_kv;
+  const float scale = a.scale;
+  __builtin_amdgcn_sched_barrier(0);
+  const int c = blockIdx.x, b = blockIdx.z;
+  const int gt = hsplit == 1 ? (int)blockIdx.y : (int)blockIdx.y / hsplit;
+  const int hs = blockIdx.y - gt * hsplit;
+  const int g = htiles == 1 ? gt : gt / htiles, ht = gt - g * htiles;
+  const int j0 = g * g_k + ht * 16;
+  const int nh = min(16, g_k - ht * 16);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int hh = lane & 15, kq = lane >> 4;
-  const int row0 = b * a.h_q + j0;
+  const int row0 = b * h_q + j0;
   const int base = c * CH;
   const int wbase = base + wv * 16 * TPW;
-  const bool live = hh < nh;
+  const bool live = hh < nh && (hsplit == 1 || hh % hsplit == hs);
 
   floatx4 sc[TPW];
   QK<T, D> qk;
-  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_k + g) * a.l_max * D;
+  const T* kh = kbase + (size_t)(b * h_k + g) * l_max * D;
   if constexpr (MODE == kFromKeysSpeculative) {
-    qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
-    score_tiles<T, D, TPW>(sc, qk, kh, wbase, a.max_l_kv, lane, a.scale);
+    qk.load_q(qbase + (size_t)row0 * D, nh, lane);
+    score_tiles<T, D, TPW>(sc, qk, kh, wbase, max_l_kv, lane, scale);
   }
   const int L = min(a.l_kv[b], a.max_l_kv);
   if (base >= L) return;
@@ -206,8 +256,8 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) sc[t] = *reinterpret_cast<const floatx4*>(srow + wbase + 16 * t + 4 * kq);
   } else if constexpr (MODE == kFromKeys) {
-    qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
-    score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+    qk.load_q(qbase + (size_t)row0 * D, nh, lane);
+    score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, scale);
   }
   __syncthreads();
 
@@ -245,11 +295,11 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     atomicMax(&kl.mx[hh], order_key(vmax));
   }
   __syncthreads();
-  if (tid < nh) {
+  if (tid < nh && (hsplit == 1 || tid % hsplit == hs)) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
     *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
   }
-  if constexpr (GATHER) chunk_records<T, D, CH>(kl, a, b, j0, nh, c);
+  if constexpr (GATHER) chunk_records<T, D, CH>(kl, a, b, j0, nh, c, hs, hsplit);
 }
 
 // The chunk records of eq. (7) from kept lists already in the workspace (the
@@ -283,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
     }
   }
   __syncthreads();
-  chunk_records<T, D, CH>(kl, a, b, j0, nh, c);
+  chunk_records<T, D, CH>(kl, a, b, j0, nh, c, 0, 1);
 }
 
 // ----------------------------------------------------------------------------
@@ -433,10 +483,12 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
       }
     }
     __syncthreads();
-    cand = s_cand;
   }
-  const uint32_t key = radix_select_block<NT>(cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist,
-                                              s_itmp, s_res);
+  // one call per source, so that each reads through a pointer of known kind (LDS or global)
+  const uint32_t key =
+      C <= (unsigned)kCandLds
+          ? radix_select_block<NT>(s_cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res)
+          : radix_select_block<NT>(cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
   if (tid == 0) {
     tau_out[row] = order_key_to_f32(key);
     a.cand_cnt[row] = 0u;
@@ -448,14 +500,15 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
 // Sparse softmax and value gather (eq. (7)) over the kept entries of one row.
 
 struct GatherArgs {
-  StreamArgs s;           // q, k, l_kv, logit buffer, kept lists and counts
-  const void* v;          // [B, h_v, l_max, D]
+  // own pointers before the embedded block (no pointer right after a scalar field:
+  // see StreamArgs)
   float* tau;             // [B*h_q] (written only where a row is refreshed)
   void* out;              // [B*h_q, D]
   int32_t* sel_count;     // [B*h_q] or null
   int32_t* sel_idx;       // [B*h_q, sel_cap] or null
   int32_t* flags;         // [B*h_q] or null
-  int h_v, sel_cap, out_bf16, refreshed;
+  StreamArgs s;           // q, k, v, l_kv, logit buffer, kept lists and counts
+  int sel_cap, out_bf16, refreshed;
 };
 
 template <int D>
@@ -575,9 +628,9 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
   }
   m = block_max<NT>(m, s_ftmp);
 
-  const int vh = (int)(((long long)j * a.h_v) / s.h_q);
+  const int vh = j / s.g_v;
   const int grp = tid / RG::G, gl = tid - grp * RG::G;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_v + vh) * s.l_max * D + gl * RG::EPL;
+  const T* vbase = reinterpret_cast<const T*>(s.v) + (size_t)(b * s.h_v + vh) * s.l_max * D + gl * RG::EPL;
   float acc[RG::EPL];
 #pragma unroll
   for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
