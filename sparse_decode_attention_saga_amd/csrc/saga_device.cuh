@@ -239,6 +239,37 @@ __device__ __forceinline__ float row_stride4_sum(float x) {
   return x;
 }
 
+// x[l] op x[l ^ m] for m = 8 (DPP rotate by 8 within rows of 16 lanes), 16 and 32
+// (gfx950 permlane swaps: the two returned halves hold x and its partner).
+template <int M, typename Op>
+__device__ __forceinline__ float xor_lanes(float x, Op op) {
+  static_assert(M == 8 || M == 16 || M == 32, "lane distance 8, 16 or 32");
+  if constexpr (M == 8) {
+    return op(x, __int_as_float(dpp_i<kDppRor8>(0, __float_as_int(x))));
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+// Sum (or maximum) over lanes l, l + G, l + 2G, ... of the wave (G = 8, 16 or 32).
+template <int G>
+__device__ __forceinline__ float strided_lane_sum(float x) {
+  auto add = [](float u, float v) { return u + v; };
+  if constexpr (G <= 8) x = xor_lanes<8>(x, add);
+  if constexpr (G <= 16) x = xor_lanes<16>(x, add);
+  return xor_lanes<32>(x, add);
+}
+template <int G>
+__device__ __forceinline__ float strided_lane_max(float x) {
+  auto mx = [](float u, float v) { return fmaxf(u, v); };
+  if constexpr (G <= 8) x = xor_lanes<8>(x, mx);
+  if constexpr (G <= 16) x = xor_lanes<16>(x, mx);
+  return xor_lanes<32>(x, mx);
+}
+
 template <typename Op>
 __device__ __forceinline__ int wave_reduce_i(int x, int neutral, Op op) {
   x = op(x, dpp_i<kDppXor1>(neutral, x));

@@ -150,14 +150,15 @@ __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const Strea
       z += w[u];
     }
   }
-#pragma unroll
-  for (int o = PIECES; o < 16; o <<= 1) {
+  if constexpr (RPG == 2) {  // the two rows of a group load: lanes l and l ^ 8
+    auto add = [](float u, float v) { return u + v; };
 #pragma unroll
     for (int p = 0; p < PPL; ++p)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[p][e] += __shfl_xor(acc[p][e], o);
-    z += __shfl_xor(z, o);
+      for (int e = 0; e < EPL; ++e) acc[p][e] = xor_lanes<8>(acc[p][e], add);
+    z = xor_lanes<8>(z, add);
   }
+  static_assert(RPG <= 2, "value rows of at least 8 pieces");
   const long long nch16 = (long long)a.nch * 16;
   if (gph == 1) {
     // one group per head: it writes the record itself
@@ -535,11 +536,8 @@ __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
 #pragma unroll
-  for (int off = RG::G; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < RG::EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
-    z += __shfl_xor(z, off);
-  }
+  for (int e = 0; e < RG::EPL; ++e) acc[e] = strided_lane_sum<RG::G>(acc[e]);
+  z = strided_lane_sum<RG::G>(z);
   if (lane < RG::G) {
 #pragma unroll
     for (int e = 0; e < RG::EPL; ++e) s_red[wv][lane * RG::EPL + e] = acc[e];
@@ -834,7 +832,8 @@ struct DenseArgs {
 
 // grid = (nchd, h_kv, B), block = 256. Each block: logits of CHD keys for the g query
 // heads of one key/value head (MFMA), the chunk's softmax numerator relative to the
-// chunk maximum, and its product with the chunk's value rows (VALU).
+// chunk maximum, and its product with the chunk's value rows (VALU). The value and
+// key loads of the chunk are all issued before the first MFMA.
 template <typename T, int D, int GH>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
@@ -842,21 +841,26 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   constexpr int EPL = Unpack<T>::kN;
   constexpr int G = D / EPL;                         // lanes per value row
   constexpr int VL = (16 * D) / (EPL * kWave);       // 16-byte value loads per lane per tile
+  const T* const kbase = reinterpret_cast<const T*>(a.k);
+  const T* const vbase = reinterpret_cast<const T*>(a.v);
+  const T* const qbase = reinterpret_cast<const T*>(a.q);
+  const int h_kv = a.h_kv, l_max = a.l_max, gq = a.g, h_q = a.h_q, max_l_kv = a.max_l_kv;
+  const float scale = a.scale;
+  __builtin_amdgcn_sched_barrier(0);
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int L = min(a.l_kv[b], a.max_l_kv);
+  const int L = min(a.l_kv[b], max_l_kv);
   const int base = c * CHD;
   if (base >= L) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int hh = lane & 15, kq = lane >> 4;
-  const int j0 = g * a.g;
-  const int row0 = b * a.h_q + j0;
+  const int row0 = b * h_q + g * gq;
 
   __shared__ float s_p[kWaves][TPW][16][GH];
   __shared__ float s_m[kWaves][GH], s_z[kWaves][GH];
   __shared__ float s_o[kWaves][GH][D];
 
-  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_kv + g) * a.l_max * D;
-  const T* vh = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.h_kv + g) * a.l_max * D;
+  const T* kh = kbase + (size_t)(b * h_kv + g) * l_max * D;
+  const T* vh = vbase + (size_t)(b * h_kv + g) * l_max * D;
   const int wbase = base + wv * 16 * TPW;
 
   // value tiles: load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
@@ -871,9 +875,9 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     }
 
   QK<T, D> qk;
-  qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, a.g, lane);
+  qk.load_q(qbase + (size_t)row0 * D, gq, lane);
   floatx4 sc[TPW];
-  score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+  score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, scale);
 
   float mh = -INFINITY;
 #pragma unroll
@@ -884,8 +888,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
       if (key >= L) sc[t][r] = -INFINITY;
       mh = fmaxf(mh, sc[t][r]);
     }
-  mh = fmaxf(mh, __shfl_xor(mh, 16));
-  mh = fmaxf(mh, __shfl_xor(mh, 32));
+  mh = strided_lane_max<16>(mh);
   float zh = 0.f;
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -895,8 +898,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
       zh += p;
       if (hh < GH) s_p[wv][t][4 * kq + r][hh] = p;
     }
-  zh += __shfl_xor(zh, 16);
-  zh += __shfl_xor(zh, 32);
+  zh = strided_lane_sum<16>(zh);
   if (lane < GH) {
     s_m[wv][lane] = mh;
     s_z[wv][lane] = zh;
@@ -925,11 +927,9 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     }
   // lanes with the same column group (lane % G) hold partial sums over different keys
 #pragma unroll
-  for (int off = G; off < kWave; off <<= 1)
+  for (int h = 0; h < GH; ++h)
 #pragma unroll
-    for (int h = 0; h < GH; ++h)
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) o[h][q] += __shfl_xor(o[h][q], off);
+    for (int q = 0; q < EPL; ++q) o[h][q] = strided_lane_sum<G>(o[h][q]);
   if (lane < G) {
 #pragma unroll
     for (int h = 0; h < GH; ++h)
@@ -939,7 +939,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   __syncthreads();
 
   // merge the 4 waves (each relative to its own maximum) and write the chunk partial
-  for (int idx = tid; idx < a.g * (D + 1); idx += kBlock) {
+  for (int idx = tid; idx < gq * (D + 1); idx += kBlock) {
     const int h = idx / (D + 1), d = idx - h * (D + 1);
     float M = -INFINITY;
 #pragma unroll
