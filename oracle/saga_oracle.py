@@ -164,13 +164,14 @@ def refresh_threshold(q, K, l_kv, N: int, scale: Optional[float] = None):
 
 
 def dense_gqa(q, K, V, l_kv, scale: Optional[float] = None) -> np.ndarray:
-    """Eq. (2)-(4) for one decode token with grouped-query heads (h_k == h_v):
-    softmax over every cached key, then the full P V product."""
+    """Eq. (2)-(4) for one decode token: softmax over every cached key, then the full
+    P V product, with query head j reading key head g(j) and value head v(j). With
+    h_k == h_v this is grouped-query attention (the pages' dense baseline); with
+    h_k < h_v it is SAGA with full attention (section "SAGA Architecture" without
+    the Atop-N selection)."""
     q = np.asarray(q, np.float64)
     B, h_q, d = q.shape
-    h_kv = K.shape[1]
-    if V.shape[1] != h_kv:
-        raise ValueError("dense GQA has as many value heads as key heads")
+    h_k, h_v = K.shape[1], V.shape[1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     O = np.zeros((B, h_q, d))
     for b in range(B):
@@ -178,7 +179,6 @@ def dense_gqa(q, K, V, l_kv, scale: Optional[float] = None) -> np.ndarray:
         if L == 0:
             continue
         for j in range(h_q):
-            g = key_head_of(j, h_q, h_kv)
-            a = attention_logits(q[b, j], K[b, g, :L], scale)
-            O[b, j], _ = sparse_softmax_pv(a, np.asarray(V[b, g, :L], np.float64))
+            a = attention_logits(q[b, j], K[b, key_head_of(j, h_q, h_k), :L], scale)
+            O[b, j], _ = sparse_softmax_pv(a, np.asarray(V[b, value_head_of(j, h_q, h_v), :L], np.float64))
     return O

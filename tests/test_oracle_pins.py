@@ -85,6 +85,21 @@ def test_dense_gqa_ragged_lengths():
             np.testing.assert_allclose(O[b, j], ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("h_k,h_v", [(1, 4), (2, 8), (1, 12)])
+def test_dense_saga_full_attention(h_k, h_v):
+    # h_k < h_v (SAGA, full attention): torch's attention with the key cache and the
+    # value cache each expanded to the query heads by its own group size
+    h_q = 12 if h_v == 12 else 8
+    q, K, V, lens = rand_case(4 + h_v, h_q=h_q, h_k=h_k, h_v=h_v)
+    O = orc.dense_gqa(q, K, V, lens)
+    Kx = torch.from_numpy(K).repeat_interleave(h_q // h_k, dim=1)
+    Vx = torch.from_numpy(V).repeat_interleave(h_q // h_v, dim=1)
+    for b in range(q.shape[0]):
+        L = int(lens[b])
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], Kx[b, :, :L], Vx[b, :, :L])[:, 0]
+        np.testing.assert_allclose(O[b], ref.numpy(), rtol=0, atol=1e-12)
+
+
 # --- refresh step = exact top-N (eq. 6-7) ---------------------------------------
 
 @pytest.mark.parametrize("N", [1, 2, 7, 22, 23])
