@@ -302,6 +302,64 @@ def sweep(torch, args) -> int:
     return 0
 
 
+def decompose(torch, args) -> int:
+    """Where the SAGA + Atop-N gain comes from, at the Qwen2.5-1.5B-shaped 128K layer:
+    the same library's dense attention and Atop-N step, each with grouped-query heads
+    (h_k = h_v = 2, the original layer) and with SAGA heads (h_k = 1, h_v = 4)."""
+    from sparse_decode_attention_saga_amd import api
+    from sparse_decode_attention_saga_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    api.lib()
+    w0 = wl.WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    L = w0.l_kv
+    heads = {"gqa": (w0.dense_h_kv, w0.dense_h_kv), "saga": (w0.h_k, w0.h_v)}
+    res = {}
+    for name, (h_k, h_v) in heads.items():
+        w = w0.with_(h_k=h_k, h_v=h_v, workload_id=w0.workload_id + (100 if name == "gqa" else 0))
+        x = wl.generate(w, seed=0)
+        q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+        l_kv = torch.from_numpy(x.l_kv).to(dev)
+        touched = (k0.numel() + v0.numel()) * k0.element_size()
+        R = max(2, math.ceil((1 << 30) / touched))
+        while math.gcd(R, w0.refresh_period) != 1:
+            R += 1
+        ks = k0.unsqueeze(0).repeat(R, 1, 1, 1, 1)
+        vs = v0.unsqueeze(0).repeat(R, 1, 1, 1, 1)
+        out = torch.empty_like(q0)
+        ws = api.Workspace(api.make_shape(q0, k0, v0), w0.N, L, dev)
+        taus = torch.zeros(R, w0.batch, w0.h_q, dtype=torch.float32, device=dev)
+        for r in range(R):
+            api.refresh_threshold(q0, ks[r], l_kv, taus[r], N=w0.N, max_l_kv=L, workspace=ws)
+
+        def dense_step(t):
+            api.dense_gqa_attn(q0, ks[t % R], vs[t % R], l_kv, max_l_kv=L, out=out, workspace=ws)
+
+        def sparse_step(t):
+            r = t % R
+            api.decode_attn(q0, ks[r], vs[r], l_kv, taus[r], N=w0.N, refresh_period=w0.refresh_period, step=t,
+                            max_l_kv=L, out=out, workspace=ws)
+
+        for label, fn in (("dense", dense_step), ("atopn", sparse_step)):
+            for t in range(W):
+                fn(t)
+            torch.cuda.synchronize()
+            us = pct([1e3 * m / K for m in time_graph(torch, lambda: [fn(t) for t in range(W, W + K)], args.reps)], 50)
+            res[f"{name}_{label}_us"] = us
+            log(f"{name} (h_k={h_k}, h_v={h_v}) {label}: {us:.2f} us/step")
+        del ks, vs
+        torch.cuda.empty_cache()
+    base = res["gqa_dense_us"]
+    line = {"decomposition": w0.name, "N": w0.N, "refresh_period": w0.refresh_period, "steps": K, **res,
+            "speedup_saga_heads_dense": base / res["saga_dense_us"],
+            "speedup_gqa_atopn": base / res["gqa_atopn_us"],
+            "speedup_saga_atopn": base / res["saga_atopn_us"],
+            "saga_over_gqa_with_atopn": res["gqa_atopn_us"] / res["saga_atopn_us"]}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +378,8 @@ def main() -> int:
                     help="print per-kernel averages of rocprofv3 csv files and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="SAGA vs dense step time over l_kv x N x refresh period (one JSON line)")
+    ap.add_argument("--decompose", action="store_true",
+                    help="dense and Atop-N steps with grouped-query and with SAGA heads (one JSON line)")
     args = ap.parse_args()
 
     if args.rocprof_summary:
@@ -340,6 +400,8 @@ def main() -> int:
         return 0
     if args.sweep:
         return sweep(torch, args)
+    if args.decompose:
+        return decompose(torch, args)
 
     from sparse_decode_attention_saga_amd import api
     from sparse_decode_attention_saga_amd import bytemodel

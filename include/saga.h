@@ -106,8 +106,11 @@ saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const voi
                                    float* tau, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
-/* Dense grouped-query attention, eq. (2)-(4) over every cached key and value:
- * the baseline the pages compare against (Figure 2). Requires h_k == h_v. */
+/* Dense attention, eq. (2)-(4) over every cached key and value, with query head j
+ * reading key head g(j) and value head v(j). With h_k == h_v this is grouped-query
+ * attention, the baseline the pages compare against (Figure 2); with h_k < h_v it is
+ * SAGA with full attention (section "SAGA Architecture" without Atop-N selection).
+ * SAGA_ERR_UNSUPPORTED unless h_k divides h_v and h_q / h_v <= 16. */
 saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* k,
                                 const void* v, const int32_t* l_kv, int32_t max_l_kv,
                                 void* out, void* workspace, size_t workspace_bytes,

@@ -349,8 +349,9 @@ saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* 
   if (!s || !q || !k || !v || !l_kv || !out) return SAGA_ERR_NULL;
   saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
   if (st != SAGA_OK) return st;
-  if (s->h_k != s->h_v) return SAGA_ERR_SHAPE;
-  const int g = s->h_q / s->h_k;
+  // the query heads of one value head must share one key head: h_k divides h_v
+  if (s->h_k > s->h_v || s->h_v % s->h_k) return SAGA_ERR_UNSUPPORTED;
+  const int g = s->h_q / s->h_v;
   if (g > 16) return SAGA_ERR_UNSUPPORTED;
   const Layout w = layout(s, max_l_kv);
   const hipStream_t hs = (hipStream_t)stream;
@@ -362,7 +363,8 @@ saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* 
   a.part = at<float>(workspace, w.part);
   a.out = out;
   a.h_q = s->h_q;
-  a.h_kv = s->h_k;
+  a.h_k = s->h_k;
+  a.h_v = s->h_v;
   a.g = g;
   a.l_max = s->l_max;
   a.nchd = w.nch;
@@ -372,7 +374,7 @@ saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* 
   (void)hipGetLastError();
   SAGA_DISPATCH(s->dtype, s->d, {
     if (max_l_kv > 0) {
-      const dim3 grid(w.nch, s->h_k, s->batch);
+      const dim3 grid(w.nch, s->h_v, s->batch);
       if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, D, 4>), grid, dim3(kBlock), 0, hs, a);
       else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, D, 8>), grid, dim3(kBlock), 0, hs, a);
       else hipLaunchKernelGGL((k_dense_partial<T, D, 16>), grid, dim3(kBlock), 0, hs, a);

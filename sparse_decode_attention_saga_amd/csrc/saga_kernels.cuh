@@ -825,15 +825,16 @@ struct DenseArgs {
   const int32_t* l_kv;
   float* part;     // [B*h_q, nchd, D+4] per-chunk (m, Z, -, -, o[D])
   void* out;
-  int h_q, h_kv, g, l_max, nchd, out_bf16;
+  int h_q, h_k, h_v, g, l_max, nchd, out_bf16;  // g = h_q / h_v query heads per value head
   int max_l_kv;
   float scale;
 };
 
-// grid = (nchd, h_kv, B), block = 256. Each block: logits of CHD keys for the g query
-// heads of one key/value head (MFMA), the chunk's softmax numerator relative to the
-// chunk maximum, and its product with the chunk's value rows (VALU). The value and
-// key loads of the chunk are all issued before the first MFMA.
+// grid = (nchd, h_v, B), block = 256. Each block takes one chunk of CHD keys and one
+// value head v: the logits of its g query heads against their key head (h_k divides
+// h_v, so the g heads share one; MFMA), the chunk's softmax numerator relative to the
+// chunk maximum, and its product with the chunk's rows of value head v (VALU). The
+// value and key loads of the chunk are all issued before the first MFMA.
 template <typename T, int D, int GH>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
@@ -844,23 +845,24 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   const T* const kbase = reinterpret_cast<const T*>(a.k);
   const T* const vbase = reinterpret_cast<const T*>(a.v);
   const T* const qbase = reinterpret_cast<const T*>(a.q);
-  const int h_kv = a.h_kv, l_max = a.l_max, gq = a.g, h_q = a.h_q, max_l_kv = a.max_l_kv;
+  const int h_k = a.h_k, h_v = a.h_v, l_max = a.l_max, gq = a.g, h_q = a.h_q, max_l_kv = a.max_l_kv;
   const float scale = a.scale;
   __builtin_amdgcn_sched_barrier(0);
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, vg = blockIdx.y, b = blockIdx.z;
+  const int kg = h_k == h_v ? vg : vg / (h_v / h_k);  // key head of this value head's query heads
   const int L = min(a.l_kv[b], max_l_kv);
   const int base = c * CHD;
   if (base >= L) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int hh = lane & 15, kq = lane >> 4;
-  const int row0 = b * h_q + g * gq;
+  const int row0 = b * h_q + vg * gq;
 
   __shared__ float s_p[kWaves][TPW][16][GH];
   __shared__ float s_m[kWaves][GH], s_z[kWaves][GH];
   __shared__ float s_o[kWaves][GH][D];
 
-  const T* kh = kbase + (size_t)(b * h_kv + g) * l_max * D;
-  const T* vh = vbase + (size_t)(b * h_kv + g) * l_max * D;
+  const T* kh = kbase + (size_t)(b * h_k + kg) * l_max * D;
+  const T* vh = vbase + (size_t)(b * h_v + vg) * l_max * D;
   const int wbase = base + wv * 16 * TPW;
 
   // value tiles: load r of tile t covers flat element (r*64 + lane) of the 16 x G grid

@@ -267,19 +267,22 @@ def test_stages_equal_decode_step():
 
 
 DENSE = [
-    # B, h_q, h_kv, d, lens, dtype
-    (1, 12, 2, 128, [5000], "bf16"),
-    (2, 32, 8, 64, [3000, 17], "bf16"),
-    (3, 4, 1, 64, [1, 0, 700], "f32"),
-    (1, 16, 1, 128, [2049], "f32"),
+    # B, h_q, h_k, h_v, d, lens, dtype  (h_k == h_v: grouped-query; h_k < h_v: SAGA, full attention)
+    (1, 12, 2, 2, 128, [5000], "bf16"),
+    (2, 32, 8, 8, 64, [3000, 17], "bf16"),
+    (3, 4, 1, 1, 64, [1, 0, 700], "f32"),
+    (1, 16, 1, 1, 128, [2049], "f32"),
+    (1, 12, 1, 4, 128, [5000], "bf16"),
+    (2, 32, 2, 8, 64, [3000, 1], "bf16"),
+    (1, 16, 1, 16, 128, [777], "f32"),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(DENSE)))
 def test_dense_gqa(case):
-    B, h_q, h_kv, d, lens, dtype = DENSE[case]
+    B, h_q, h_k, h_v, d, lens, dtype = DENSE[case]
     say(f"dense case {case}: {DENSE[case]}")
-    w, x = small(B, h_q, h_kv, h_kv, d, lens, dtype, seed=40 + case)
+    w, x = small(B, h_q, h_k, h_v, d, lens, dtype, seed=40 + case)
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     l_kv = torch.from_numpy(x.l_kv).to(dev)
@@ -296,6 +299,21 @@ def test_dense_gqa(case):
         for j in range(h_q):
             s = np.abs(ref[b, j]).max()
             assert np.abs(got[b, j] - ref[b, j]).max() <= tol * s, (b, j)
+
+
+def test_dense_saga_full_size():
+    # SAGA with full attention at the Qwen-shaped 128K layer (h_k=1, h_v=4)
+    w = wl.QWEN_128K
+    x = wl.generate(w, seed=0)
+    dev = torch.device("cuda:0")
+    out = api.dense_gqa_attn(x.q.to(dev), x.k.to(dev), x.v.to(dev), torch.from_numpy(x.l_kv).to(dev),
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q64, k64, v64 = x.f64()
+    ref = orc.dense_gqa(q64, k64, v64, x.l_kv)
+    got = out.double().cpu().numpy()
+    err = np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)
+    assert err.max() <= 2e-3, err.max()
 
 
 @pytest.mark.parametrize("name", ["llama3.2-1b-shape-l32k", "qwen2.5-1.5b-shape-l128k"])

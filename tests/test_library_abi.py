@@ -100,10 +100,14 @@ def test_other_entry_points_reject_bad_arguments(lib):
                                   None, FAKE, big, None) == api.ERR_SHAPE
     assert lib.saga_split_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, FAKE, None, FAKE, 0,
                                   None, FAKE, big, None) == api.ERR_SHAPE
-    # dense GQA needs as many value heads as key heads
-    assert lib.saga_dense_gqa_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_SHAPE
+    # dense attention: the query heads of a value head must share a key head (h_k | h_v),
+    # at most 16 query heads per value head
+    more_keys = shape(h_q=8, h_k=4, h_v=2)
+    assert lib.saga_dense_gqa_attn(ctypes.byref(more_keys), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, big,
+                                   None) == api.ERR_UNSUPPORTED
     wide = shape(h_q=32, h_k=1, h_v=1)
     assert lib.saga_dense_gqa_attn(ctypes.byref(wide), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_UNSUPPORTED
+    assert lib.saga_dense_gqa_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, None, FAKE, big, None) == api.ERR_NULL
     assert lib.saga_workspace_init(None, 16, None) == api.ERR_NULL
 
 
