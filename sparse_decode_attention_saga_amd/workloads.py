@@ -76,6 +76,9 @@ LLAMA_32K = Workload("llama3.2-1b-shape-l32k", 2, batch=1, h_q=32, h_k=2, h_v=8,
 QWEN_128K = Workload("qwen2.5-1.5b-shape-l128k", 3, batch=1, h_q=12, h_k=1, h_v=4, d=128,
                      l_kv=131072, N=512, refresh_period=32, dtype="bf16",
                      plant_frac=0.005, dense_h_kv=2)
+QWEN_128K_B16 = Workload("qwen2.5-1.5b-shape-l128k-b16", 6, batch=16, h_q=12, h_k=1, h_v=4, d=128,
+                         l_kv=131072, N=512, refresh_period=32, dtype="bf16",
+                         plant_frac=0.005, dense_h_kv=2)
 RAGGED_B8 = Workload("ragged-b8-l16k-128k", 4, batch=8, h_q=32, h_k=2, h_v=8, d=64,
                      l_kv=131072, l_kv_min=16384, N=256, refresh_period=16,
                      dtype="bf16", plant_frac=0.005, run_len=64)
@@ -86,7 +89,7 @@ SWEEP_L = (4096, 16384, 65536, 131072)
 SWEEP_N = (128, 512, 2048)
 SWEEP_PERIOD = (1, 8, 64)
 
-WORKLOADS = {w.name: w for w in (TINY, LLAMA_32K, QWEN_128K, RAGGED_B8, SWEEP)}
+WORKLOADS = {w.name: w for w in (TINY, LLAMA_32K, QWEN_128K, QWEN_128K_B16, RAGGED_B8, SWEEP)}
 
 
 def streams(workload_id: int, seed: int) -> list:
