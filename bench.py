@@ -360,6 +360,57 @@ def decompose(torch, args) -> int:
     return 0
 
 
+def device_pages(torch, k, v, page_tokens: int, seed: int):
+    """Paged copies of contiguous caches k [B, h_k, L, d], v [B, h_v, L, d] (L a
+    multiple of the page size) on the device, pages in a seeded random order:
+    (k_pages [B*L/P, h_k, P, d], v_pages [B*L/P, h_v, P, d], table [B, L/P] int32)."""
+    B, h_k, L, d = k.shape
+    P = page_tokens
+    n = L // P
+    gen = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(B * n, generator=gen).to(torch.int64)
+    kp = torch.empty((B * n, h_k, P, d), dtype=k.dtype, device=k.device)
+    vp = torch.empty((B * n, v.shape[1], P, d), dtype=v.dtype, device=v.device)
+    kp[perm.to(k.device)] = k.reshape(B, h_k, n, P, d).permute(0, 2, 1, 3, 4).reshape(B * n, h_k, P, d)
+    vp[perm.to(v.device)] = v.reshape(B, v.shape[1], n, P, d).permute(0, 2, 1, 3, 4).reshape(B * n, v.shape[1], P, d)
+    table = perm.to(torch.int32).reshape(B, n).to(k.device)
+    return kp, vp, table
+
+
+def paged_timing(torch, api, w, qs, ks, vs, taus, l_kv, L, args) -> list:
+    """The decode step and the reuse step over paged copies of the rotating sets."""
+    out = []
+    R = len(ks)
+    K, W = args.steps, args.warmup
+    for P in args.paged:
+        if L % P:
+            log(f"paged: skipping {P}-token pages (l_kv is not a multiple)")
+            continue
+        sets = [device_pages(torch, ks[r], vs[r], P, seed=r) for r in range(R)]
+        tau_p = [t.clone() for t in taus]
+        o = torch.empty(w.batch, w.h_q, w.d, dtype=qs[0].dtype, device=qs[0].device)
+        shape = api.make_shape(qs[0], ks[0], vs[0])
+        ws = api.Workspace(shape, w.N, L, qs[0].device)
+
+        def step(t, period):
+            r = t % R
+            kp, vp, tab = sets[r]
+            api.decode_attn_paged(qs[r], kp, vp, tab, l_kv, tau_p[r], N=w.N, refresh_period=period, step=t,
+                                  max_l_kv=L, out=o, workspace=ws)
+
+        for t in range(W):
+            step(t, w.refresh_period)
+        torch.cuda.synchronize()
+        ms = time_graph(torch, lambda: [step(t, w.refresh_period) for t in range(W, W + K)], args.reps)
+        us = pct([1e3 * m / K for m in ms], 50)
+        ms = time_graph(torch, lambda: [step(1 + t, 1 << 30) for t in range(W, W + K)], args.reps)
+        us_steady = pct([1e3 * m / K for m in ms], 50)
+        log(f"paged ({P}-token pages): {us:.2f} us/step, steady {us_steady:.2f} us/step")
+        out.append({"page_tokens": P, "us_per_step": us, "us_steady_step": us_steady})
+        del sets
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,7 +421,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: >= 1 GiB of K)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady"], default="all",
+    ap.add_argument("--paged", type=int, nargs="*", default=[16, 256], metavar="P",
+                    help="also time the step over paged caches with P-token pages (none: skip)")
+    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady", "paged"], default="all",
                     help="time only one part (for profiler runs)")
     ap.add_argument("--probe", choices=["none", "copy", "read"], default="none",
                     help="copy: a plain device copy of 256 MiB (counter calibration); read: read ceilings")
@@ -473,6 +526,9 @@ def main() -> int:
         res["combine_us"] = pct([1e3 * m / K for m in ms], 50)
         log(f"combine kernel alone: {res['combine_us']:.2f} us/launch")
 
+    if args.paged and args.only in ("all", "paged"):
+        res["paged"] = paged_timing(torch, api, w, qs, ks, vs, taus, l_kv, L, args)
+
     # survivor statistics at a step that reuses the threshold of set 0
     cap = 8 * w.N
     sel_count = torch.zeros(w.batch, w.h_q, dtype=torch.int32, device=dev)
@@ -522,6 +578,9 @@ def main() -> int:
         log(f"dense GQA (h_kv={wd.h_k}): {dense['us']:.2f} us/step")
         del kd, vd
 
+    if "paged" in res and "saga_us" in res:
+        for p in res["paged"]:
+            p["vs_contiguous"] = p["us_per_step"] / pct(res["saga_us"], 50)
     if "saga_us" not in res:
         print(json.dumps({"metric": METRIC, "partial": args.only, **res, "dense": dense}))
         return 0
@@ -574,6 +633,7 @@ def main() -> int:
         "survivors_max": int(counts.max()),
         "forced_refresh_rows": forced,
         "read_ceiling": ceil,
+        "paged": res.get("paged"),
         "roofline": roof,
     }
     if dense:

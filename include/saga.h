@@ -154,6 +154,46 @@ saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k
                                int32_t* sel_idx, int32_t sel_cap, int32_t* flags,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Paged (non-contiguous) caches for batched decode (the batch-16 setting of the
+ * summary page's section "Inference Speedups", Figure 2): each sequence's cached
+ * tokens live in fixed-size pages of a shared pool, found through a page table.
+ *   Key pool   k_pages [num_pages, h_k, page_tokens, d] (dtype), one page holds the
+ *              rows of every key head for page_tokens consecutive tokens;
+ *   value pool v_pages [num_pages, h_v, page_tokens, d], with the same page ids;
+ *   table [B, max_pages] int32 (device): table[b*max_pages + p] is the page holding
+ *              tokens [p*page_tokens, (p+1)*page_tokens) of sequence b.
+ * page_tokens is a power of two >= 16; max_pages*page_tokens >= max_l_kv. Entries
+ * for tokens < l_kv[b] must lie in [0, num_pages) (a device-side precondition, like
+ * l_kv); other entries are never used for results, and every page id the kernels
+ * read is clamped into [0, num_pages), so stale entries cannot address memory
+ * outside the pools. Logits, thresholds, kept sets, counts and flags equal those of
+ * the contiguous calls on the same token rows exactly; outputs agree up to the
+ * order of the floating-point sums (the dense call's are identical). */
+typedef struct saga_pages {
+  const int32_t* table;  /* [B, max_pages] page ids (device) */
+  int32_t max_pages;     /* row stride of the table */
+  int32_t page_tokens;   /* tokens per page: a power of two, at least 16 */
+  int32_t num_pages;     /* pages in each pool */
+} saga_pages;
+
+/* saga_decode_attn over paged caches; every other argument as there. s->l_max is
+ * only the capacity bound (max_l_kv <= l_max), not a stride. SAGA_ERR_NULL for a
+ * NULL pages or table, SAGA_ERR_SHAPE for a bad page size or a table too short
+ * for max_l_kv. */
+saga_status saga_decode_attn_paged(const saga_shape* s, const saga_pages* pages, const void* q,
+                                   const void* k_pages, const void* v_pages, const int32_t* l_kv,
+                                   int32_t max_l_kv, int32_t N, int32_t refresh_period, int64_t step,
+                                   float* tau, void* out, int32_t* sel_count, int32_t* sel_idx,
+                                   int32_t sel_cap, int32_t* flags, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* saga_dense_gqa_attn over paged caches (the dense baseline of the same layout);
+ * arguments and errors as in saga_decode_attn_paged and saga_dense_gqa_attn. */
+saga_status saga_dense_gqa_attn_paged(const saga_shape* s, const saga_pages* pages, const void* q,
+                                      const void* k_pages, const void* v_pages, const int32_t* l_kv,
+                                      int32_t max_l_kv, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

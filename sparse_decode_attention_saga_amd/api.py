@@ -18,7 +18,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, BF16 = 0, 1
 EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "saga_decode_attn",
            "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather",
-           "saga_select_gather", "saga_split_combine")
+           "saga_select_gather", "saga_split_combine", "saga_decode_attn_paged", "saga_dense_gqa_attn_paged")
 FLAG_REFRESHED, FLAG_FORCED = 1, 2
 
 
@@ -27,6 +27,12 @@ class SagaShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_k", ctypes.c_int32),
                 ("h_v", ctypes.c_int32), ("d", ctypes.c_int32), ("l_max", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class SagaPages(ctypes.Structure):
+    """Mirror of `saga_pages` in include/saga.h."""
+    _fields_ = [("table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
 
 
 class SagaError(RuntimeError):
@@ -49,6 +55,9 @@ _SIGS = {
     "saga_sparse_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_select_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_split_combine": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_decode_attn_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P,
+                                      _SZ, _P]),
+    "saga_dense_gqa_attn_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
 }
 
 
@@ -264,4 +273,75 @@ def dense_gqa_attn(q, k, v, l_kv, *, max_l_kv: Optional[int] = None, out=None, o
     st = lib().saga_dense_gqa_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv,
                                    _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
     _check(st, "saga_dense_gqa_attn")
+    return out
+
+
+def _prep_paged(q, k_pages, v_pages, table, l_kv, tau, out, out_dtype, max_l_kv, scale):
+    """Shape and page descriptor of a paged call: k_pages [num_pages, h_k, P, d],
+    v_pages [num_pages, h_v, P, d], table [B, max_pages] int32."""
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        _dev(t, name)
+    _dev(table, "table", torch.int32)
+    _dev(l_kv, "l_kv", torch.int32)
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.dim() != 4 or table.dim() != 2:
+        raise ValueError("q [B, h_q, d], k_pages/v_pages [num_pages, heads, page_tokens, d], table [B, max_pages]")
+    B, h_q, d = q.shape
+    num_pages, h_k, P, dk = k_pages.shape
+    if v_pages.shape[0] != num_pages or v_pages.shape[2] != P or dk != d or v_pages.shape[3] != d:
+        raise ValueError("k_pages and v_pages must share num_pages, page_tokens and d with q")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise ValueError("q, k_pages and v_pages must share one dtype")
+    if table.shape[0] != B or l_kv.numel() != B:
+        raise ValueError("table and l_kv need one row per sequence")
+    capacity = table.shape[1] * P
+    if max_l_kv is None:
+        max_l_kv = capacity
+    if out_dtype is None and out is not None:
+        out_dtype = out.dtype
+    shape = SagaShape(B, h_q, h_k, v_pages.shape[1], d, max(int(max_l_kv), 1), dtype_code(q.dtype),
+                      dtype_code(out_dtype or q.dtype), float(scale))
+    pages = SagaPages(table.data_ptr(), table.shape[1], P, num_pages)
+    if tau is not None:
+        _dev(tau, "tau", torch.float32)
+        if tau.numel() != B * h_q:
+            raise ValueError("tau must be [B, h_q]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _dev(out, "out")
+        if tuple(out.shape) != tuple(q.shape) or dtype_code(out.dtype) != shape.out_dtype:
+            raise ValueError("out must be [B, h_q, d] in the output dtype")
+    return shape, pages, int(max_l_kv), out
+
+
+def decode_attn_paged(q, k_pages, v_pages, table, l_kv, tau, *, N: int, refresh_period: int, step: int,
+                      max_l_kv: Optional[int] = None, out=None, out_dtype=None, sel_count=None, sel_idx=None,
+                      flags=None, workspace: Optional[Workspace] = None, scale: float = 0.0, stream=None):
+    """saga_decode_attn_paged: decode_attn over paged caches (pages of page_tokens
+    tokens found through `table`). Returns `out`."""
+    shape, pages, max_l_kv, out = _prep_paged(q, k_pages, v_pages, table, l_kv, tau, out, out_dtype, max_l_kv,
+                                              scale)
+    for name, t in (("sel_count", sel_count), ("sel_idx", sel_idx), ("flags", flags)):
+        if t is not None:
+            _dev(t, name, torch.int32)
+    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    ws = _ws(workspace, shape, N, max_l_kv, q.device)
+    st = lib().saga_decode_attn_paged(ctypes.byref(shape), ctypes.byref(pages), _ptr(q), _ptr(k_pages),
+                                      _ptr(v_pages), _ptr(l_kv), max_l_kv, int(N), int(refresh_period), int(step),
+                                      _ptr(tau), _ptr(out), _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags),
+                                      _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
+    _check(st, "saga_decode_attn_paged")
+    return out
+
+
+def dense_gqa_attn_paged(q, k_pages, v_pages, table, l_kv, *, max_l_kv: Optional[int] = None, out=None,
+                         out_dtype=None, workspace: Optional[Workspace] = None, scale: float = 0.0, stream=None):
+    """saga_dense_gqa_attn_paged: dense attention over paged caches."""
+    shape, pages, max_l_kv, out = _prep_paged(q, k_pages, v_pages, table, l_kv, None, out, out_dtype, max_l_kv,
+                                              scale)
+    ws = _ws(workspace, shape, 1, max_l_kv, q.device)
+    st = lib().saga_dense_gqa_attn_paged(ctypes.byref(shape), ctypes.byref(pages), _ptr(q), _ptr(k_pages),
+                                         _ptr(v_pages), _ptr(l_kv), max_l_kv, _ptr(out), _ptr(ws.buf), ws.nbytes,
+                                         _stream(q.device, stream))
+    _check(st, "saga_dense_gqa_attn_paged")
     return out

@@ -13,6 +13,18 @@ namespace {
 
 constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
 
+// Runs the statement with P = the page flag as a compile-time constant.
+#define SAGA_PAGED(FLAG, ...)          \
+  do {                                 \
+    if (FLAG) {                        \
+      constexpr bool P = true;         \
+      __VA_ARGS__                      \
+    } else {                           \
+      constexpr bool P = false;        \
+      __VA_ARGS__                      \
+    }                                  \
+  } while (0)
+
 #define SAGA_DISPATCH(DT, DIM, ...)                                   \
   do {                                                                \
     if ((DT) == SAGA_BF16 && (DIM) == 128) {                          \
@@ -113,9 +125,34 @@ P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
 }
 
+int log2_exact(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Paged caches: the table must cover max_l_kv tokens; pages hold a power of two
+// tokens, at least 16 (a 16-key tile then lies inside one page).
+saga_status check_pages(const saga_pages* pg, int32_t max_l_kv) {
+  if (!pg) return SAGA_ERR_NULL;
+  if (!pg->table) return SAGA_ERR_NULL;
+  const int pt = pg->page_tokens;
+  if (pt < 16 || pt > kMaxContext || (pt & (pt - 1)) != 0) return SAGA_ERR_SHAPE;
+  if (pg->max_pages < 1 || pg->num_pages < 1) return SAGA_ERR_SHAPE;
+  if ((long long)pg->max_pages * pt < max_l_kv) return SAGA_ERR_SHAPE;
+  return SAGA_OK;
+}
+
 StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const void* q, const void* k,
-                       const void* v, const int32_t* l_kv, int32_t max_l_kv, const float* tau, int N) {
+                       const void* v, const int32_t* l_kv, int32_t max_l_kv, const float* tau, int N,
+                       const saga_pages* pg = nullptr) {
   StreamArgs a{};
+  if (pg) {
+    a.ptab = pg->table;
+    a.ptab_stride = pg->max_pages;
+    a.page_shift = log2_exact(pg->page_tokens);
+    a.num_pages = pg->num_pages;
+  }
   a.q = q;
   a.k = k;
   a.v = v;
@@ -162,9 +199,9 @@ dim3 stream_grid(const saga_shape* s, const Layout& w) {
 }
 
 void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, float* tau, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, {
-    hipLaunchKernelGGL((k_scores_hist<T, D>), stream_grid(s, w), dim3(kBlock), 0, st, a);
-  });
+  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(a.ptab != nullptr, {
+    hipLaunchKernelGGL((k_scores_hist<T, D, P>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+  }););
   hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
   hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);
 }
@@ -172,31 +209,31 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
 // Scores and Atop-N comparison; with `gather` also the chunk records of eq. (7).
 void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, bool gather,
                    hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, {
+  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(a.ptab != nullptr, {
     dim3 grid = stream_grid(s, w);
     grid.y *= a.hsplit;
     if (!gather)
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, false>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, false, P>), grid, dim3(kBlock), 0, st, a);
     else if (from_scores)
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromScores, true>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromScores, true, P>), grid, dim3(kBlock), 0, st, a);
     else if (s->batch == 1)  // one sequence: its chunks reach max_l_kv, key loads need not wait for l_kv
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeysSpeculative, true>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeysSpeculative, true, P>), grid, dim3(kBlock), 0, st, a);
     else
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, true>), grid, dim3(kBlock), 0, st, a);
-  });
+      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, true, P>), grid, dim3(kBlock), 0, st, a);
+  }););
 }
 
 // Chunk records from the kept lists (only for the separate gather stage).
 void launch_chunk_gather(const saga_shape* s, const Layout& w, const StreamArgs& a, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, {
-    hipLaunchKernelGGL((k_chunk_gather<T, D>), stream_grid(s, w), dim3(kBlock), 0, st, a);
-  });
+  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(a.ptab != nullptr, {
+    hipLaunchKernelGGL((k_chunk_gather<T, D, P>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+  }););
 }
 
 void launch_combine(const saga_shape* s, const GatherArgs& g, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, {
-    hipLaunchKernelGGL((k_split_combine<T, D>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
-  });
+  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(g.s.ptab != nullptr, {
+    hipLaunchKernelGGL((k_split_combine<T, D, P>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+  }););
 }
 
 GatherArgs gather_args(const saga_shape* s, const StreamArgs& sa, float* tau, void* out, int32_t* sel_count,
@@ -212,6 +249,75 @@ GatherArgs gather_args(const saga_shape* s, const StreamArgs& sa, float* tau, vo
   g.out_bf16 = s->out_dtype == SAGA_BF16;
   g.refreshed = refreshed ? 1 : 0;
   return g;
+}
+
+saga_status decode_impl(const saga_shape* s, const saga_pages* pg, const void* q, const void* k, const void* v,
+                        const int32_t* l_kv, int32_t max_l_kv, int32_t N, int32_t refresh_period, int64_t step,
+                        float* tau, void* out, int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap,
+                        int32_t* flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !tau || !out) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
+  if (st != SAGA_OK) return st;
+  if (refresh_period < 1 || step < 0 || (sel_idx && sel_cap < 1)) return SAGA_ERR_SHAPE;
+  const Layout w = layout(s, max_l_kv);
+  const hipStream_t hs = (hipStream_t)stream;
+  const bool refresh = (step % refresh_period) == 0;
+  (void)hipGetLastError();
+  const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N, pg);
+  if (max_l_kv > 0) {
+    if (refresh) launch_refresh(s, w, a, tau, hs);
+    launch_select(s, w, a, refresh, true, hs);
+  }
+  launch_combine(s, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
+  return launched();
+}
+
+saga_status dense_impl(const saga_shape* s, const saga_pages* pg, const void* q, const void* k, const void* v,
+                       const int32_t* l_kv, int32_t max_l_kv, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!s || !q || !k || !v || !l_kv || !out) return SAGA_ERR_NULL;
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
+  if (st != SAGA_OK) return st;
+  // the query heads of one value head must share one key head: h_k divides h_v
+  if (s->h_k > s->h_v || s->h_v % s->h_k) return SAGA_ERR_UNSUPPORTED;
+  const int g = s->h_q / s->h_v;
+  if (g > 16) return SAGA_ERR_UNSUPPORTED;
+  const Layout w = layout(s, max_l_kv);
+  const hipStream_t hs = (hipStream_t)stream;
+  DenseArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.l_kv = l_kv;
+  a.part = at<float>(workspace, w.part);
+  a.out = out;
+  a.h_q = s->h_q;
+  a.h_k = s->h_k;
+  a.h_v = s->h_v;
+  a.g = g;
+  a.l_max = s->l_max;
+  a.nchd = w.nch;
+  a.max_l_kv = max_l_kv;
+  a.out_bf16 = s->out_dtype == SAGA_BF16;
+  a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
+  if (pg) {
+    a.ptab = pg->table;
+    a.ptab_stride = pg->max_pages;
+    a.page_shift = log2_exact(pg->page_tokens);
+    a.num_pages = pg->num_pages;
+  }
+  (void)hipGetLastError();
+  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(pg != nullptr, {
+    if (max_l_kv > 0) {
+      const dim3 grid(w.nch, s->h_v, s->batch);
+      if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, D, 4, P>), grid, dim3(kBlock), 0, hs, a);
+      else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, D, 8, P>), grid, dim3(kBlock), 0, hs, a);
+      else hipLaunchKernelGGL((k_dense_partial<T, D, 16, P>), grid, dim3(kBlock), 0, hs, a);
+    }
+    hipLaunchKernelGGL((k_dense_combine<D>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
+                       (int)StreamCfg<T, D>::kChunk);
+  }););
+  return launched();
 }
 
 }  // namespace
@@ -253,21 +359,20 @@ saga_status saga_decode_attn(const saga_shape* s, const void* q, const void* k, 
                              int64_t step, float* tau, void* out, int32_t* sel_count, int32_t* sel_idx,
                              int32_t sel_cap, int32_t* flags, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  if (!s || !q || !k || !v || !l_kv || !tau || !out) return SAGA_ERR_NULL;
-  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
+  return decode_impl(s, nullptr, q, k, v, l_kv, max_l_kv, N, refresh_period, step, tau, out, sel_count, sel_idx,
+                     sel_cap, flags, workspace, workspace_bytes, stream);
+}
+
+saga_status saga_decode_attn_paged(const saga_shape* s, const saga_pages* pages, const void* q,
+                                   const void* k_pages, const void* v_pages, const int32_t* l_kv,
+                                   int32_t max_l_kv, int32_t N, int32_t refresh_period, int64_t step,
+                                   float* tau, void* out, int32_t* sel_count, int32_t* sel_idx,
+                                   int32_t sel_cap, int32_t* flags, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const saga_status st = check_pages(pages, max_l_kv);
   if (st != SAGA_OK) return st;
-  if (refresh_period < 1 || step < 0 || (sel_idx && sel_cap < 1)) return SAGA_ERR_SHAPE;
-  const Layout w = layout(s, max_l_kv);
-  const hipStream_t hs = (hipStream_t)stream;
-  const bool refresh = (step % refresh_period) == 0;
-  (void)hipGetLastError();
-  const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
-  if (max_l_kv > 0) {
-    if (refresh) launch_refresh(s, w, a, tau, hs);
-    launch_select(s, w, a, refresh, true, hs);
-  }
-  launch_combine(s, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
-  return launched();
+  return decode_impl(s, pages, q, k_pages, v_pages, l_kv, max_l_kv, N, refresh_period, step, tau, out, sel_count,
+                     sel_idx, sel_cap, flags, workspace, workspace_bytes, stream);
 }
 
 saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const void* k, const int32_t* l_kv,
@@ -346,43 +451,16 @@ saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k
 saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* k, const void* v,
                                 const int32_t* l_kv, int32_t max_l_kv, void* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  if (!s || !q || !k || !v || !l_kv || !out) return SAGA_ERR_NULL;
-  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
+  return dense_impl(s, nullptr, q, k, v, l_kv, max_l_kv, out, workspace, workspace_bytes, stream);
+}
+
+saga_status saga_dense_gqa_attn_paged(const saga_shape* s, const saga_pages* pages, const void* q,
+                                      const void* k_pages, const void* v_pages, const int32_t* l_kv,
+                                      int32_t max_l_kv, void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  const saga_status st = check_pages(pages, max_l_kv);
   if (st != SAGA_OK) return st;
-  // the query heads of one value head must share one key head: h_k divides h_v
-  if (s->h_k > s->h_v || s->h_v % s->h_k) return SAGA_ERR_UNSUPPORTED;
-  const int g = s->h_q / s->h_v;
-  if (g > 16) return SAGA_ERR_UNSUPPORTED;
-  const Layout w = layout(s, max_l_kv);
-  const hipStream_t hs = (hipStream_t)stream;
-  DenseArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.l_kv = l_kv;
-  a.part = at<float>(workspace, w.part);
-  a.out = out;
-  a.h_q = s->h_q;
-  a.h_k = s->h_k;
-  a.h_v = s->h_v;
-  a.g = g;
-  a.l_max = s->l_max;
-  a.nchd = w.nch;
-  a.max_l_kv = max_l_kv;
-  a.out_bf16 = s->out_dtype == SAGA_BF16;
-  a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
-  (void)hipGetLastError();
-  SAGA_DISPATCH(s->dtype, s->d, {
-    if (max_l_kv > 0) {
-      const dim3 grid(w.nch, s->h_v, s->batch);
-      if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, D, 4>), grid, dim3(kBlock), 0, hs, a);
-      else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, D, 8>), grid, dim3(kBlock), 0, hs, a);
-      else hipLaunchKernelGGL((k_dense_partial<T, D, 16>), grid, dim3(kBlock), 0, hs, a);
-    }
-    hipLaunchKernelGGL((k_dense_combine<D>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
-                       (int)StreamCfg<T, D>::kChunk);
-  });
-  return launched();
+  return dense_impl(s, pages, q, k_pages, v_pages, l_kv, max_l_kv, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -150,18 +150,26 @@ template <int D> struct QK<float, D> {
   }
 };
 
-// Scaled logits of TPW consecutive 16-key tiles starting at key `wbase` of the key
-// head whose rows start at `kh`. Rows past the valid length L are clamped to L-1 for
-// the load (always in bounds); callers mask them. Requires L >= 1. All TPW*kLoads
-// loads of a lane are in flight together (the K stream is latency-bound per wave).
-template <typename T, int D, int TPW>
-__device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& qk, const T* kh,
+// Scaled logits of TPW consecutive 16-key tiles starting at key `wbase` (wave-uniform)
+// of one key head, whose rows `rows` locates (row(i), and tile(t0) for the first row
+// of a tile). Rows past the valid length L are clamped to L-1 for the load (always
+// in bounds); callers mask them. Requires L >= 1. All TPW*kLoads loads of a lane are
+// in flight together (the K stream is latency-bound per wave).
+template <typename T, int D, int TPW, typename R>
+__device__ __forceinline__ void score_tiles(floatx4 (&sc)[TPW], const QK<T, D>& qk, const R& rows,
                                             int wbase, int L, int lane, float scale) {
   uint4 kb[TPW][QK<T, D>::kLoads];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int key = min(wbase + 16 * t + (lane & 15), L - 1);
-    QK<T, D>::load_k(kb[t], kh + (size_t)key * D, lane);
+    if constexpr (R::kPaged) {
+      // a tile lies inside one page: one page lookup per tile, for the clamped tile
+      const int t0 = min(wbase + 16 * t, (L - 1) & ~15);
+      const int key = min(t0 + (lane & 15), L - 1);
+      QK<T, D>::load_k(kb[t], rows.tile(t0) + (size_t)(key - t0) * D, lane);
+    } else {
+      const int key = min(wbase + 16 * t + (lane & 15), L - 1);
+      QK<T, D>::load_k(kb[t], rows.row(key), lane);
+    }
   }
   // every key load of the wave is issued before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);

@@ -63,22 +63,93 @@ struct StreamArgs {
   float* part;             // [B*h_q, D/16, nch, 16] chunk records: sum w*v, 16 columns per slice
   unsigned* hist;          // [B*h_q, 256] top-digit histogram (zero between calls)
   unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
+  const int32_t* ptab;     // paged caches: [B, ptab_stride] page ids (the kernels' PAGED form)
   long long lpad;
   int h_q, h_k, h_v, g_k, g_v, htiles, l_max, nch, N;  // g_k = h_q/h_k, g_v = h_q/h_v
   int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   int hsplit;              // blocks sharing one chunk in k_qk_select (heads split among them)
   float scale;
+  int ptab_stride, page_shift;  // paged caches: page table row stride, log2(tokens per page)
+  int num_pages;           // paged caches: pages per pool (page ids are clamped below it)
 };
+
+// Token rows of one (sequence, head) of a key or value cache. Contiguous caches hold
+// [B, heads, l_max, D]. Paged caches (PAGED) hold pages of 2^shift tokens (at least
+// 16, so a 16-key tile never straddles two pages), each page [heads, 2^shift, D];
+// sequence b's page table row lists the page of its tokens [p 2^shift, (p+1) 2^shift).
+template <typename T, int D, bool PAGED> struct CacheRows;
+
+template <typename T, int D> struct CacheRows<T, D, false> {
+  static constexpr bool kPaged = false;
+  const T* p;
+  __device__ __forceinline__ CacheRows(const void* base, const int32_t*, int, int, int, int b, int head,
+                                       int heads, int l_max)
+      : p(reinterpret_cast<const T*>(base) + (size_t)(b * heads + head) * l_max * D) {}
+  __device__ __forceinline__ const T* row(int i) const { return p + (size_t)i * D; }
+  // first row of the 16-key tile starting at t0 (a multiple of 16, wave-uniform)
+  __device__ __forceinline__ const T* tile(int t0) const { return p + (size_t)t0 * D; }
+};
+
+// Page ids are clamped into the pool, so a table entry that is never meant to be
+// used (a page past the sequence's length, read by a speculative load) still
+// addresses memory inside the pool.
+template <typename T, int D> struct CacheRows<T, D, true> {
+  static constexpr bool kPaged = true;
+  const T* p;            // this head's rows in page 0
+  const int32_t* tab;    // this sequence's page table row
+  size_t page_elems;     // elements per page (all heads)
+  int shift;
+  unsigned last_page;
+  __device__ __forceinline__ CacheRows(const void* base, const int32_t* ptab, int stride, int shift_,
+                                       int num_pages, int b, int head, int heads, int)
+      : p(reinterpret_cast<const T*>(base) + ((size_t)head * D << shift_)),
+        tab(ptab + (size_t)b * stride),
+        page_elems((size_t)heads * D << shift_),
+        shift(shift_),
+        last_page((unsigned)num_pages - 1u) {}
+  __device__ __forceinline__ const T* in_page(int page, int i) const {
+    const unsigned pg = min((unsigned)page, last_page);
+    return p + (size_t)pg * page_elems + (size_t)(i & ((1 << shift) - 1)) * D;
+  }
+  __device__ __forceinline__ const T* row(int i) const { return in_page(tab[i >> shift], i); }
+  __device__ __forceinline__ const T* tile(int t0) const {
+    const int tu = __builtin_amdgcn_readfirstlane(t0);  // one page-table read per wave
+    return in_page(tab[tu >> shift], tu);
+  }
+};
+
+template <typename T, int D, bool PAGED>
+__device__ __forceinline__ CacheRows<T, D, PAGED> key_rows(const StreamArgs& a, int b, int g) {
+  return CacheRows<T, D, PAGED>(a.k, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, g, a.h_k, a.l_max);
+}
+template <typename T, int D, bool PAGED>
+__device__ __forceinline__ CacheRows<T, D, PAGED> value_rows(const StreamArgs& a, int b, int vh) {
+  return CacheRows<T, D, PAGED>(a.v, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vh, a.h_v, a.l_max);
+}
 
 // Kept entries of one chunk, per head of the tile, staged in LDS: offset of the key
 // inside the chunk and its logit; plus the count and the largest kept logit (as an
-// order key) per head.
+// order key) per head; with paged caches also the pages of the chunk's tokens.
 template <int CH> struct KeptLds {
   uint16_t off[16][CH];
   float val[16][CH];
   int cnt[16];
   unsigned mx[16];
+  int32_t pg[CH >= 16 ? CH / 16 : 1];
 };
+
+// Paged caches: the page ids of the tokens [base, base + CH) of sequence b into
+// kl.pg (one page when pages hold at least CH tokens, else CH / 2^shift pages; ids
+// past the table row read as page 0 and are never used). Threads 0..CH/16-1.
+template <int CH>
+__device__ __forceinline__ void stage_pages(KeptLds<CH>& kl, const StreamArgs& a, int b, int base) {
+  const int np = (CH >> a.page_shift) > 0 ? (CH >> a.page_shift) : 1;
+  const int t = threadIdx.x;
+  if (t < np) {
+    const int pi = (base >> a.page_shift) + t;
+    kl.pg[t] = pi < a.ptab_stride ? a.ptab[(size_t)b * a.ptab_stride + pi] : 0;
+  }
+}
 
 // Eq. (7) split over chunks of keys: the chunk record of row (b, j) for every head j
 // of the tile that this block owns (heads j0 + h with h mod hsplit == hs): the value
@@ -89,7 +160,7 @@ template <int CH> struct KeptLds {
 // groups each, taking alternate kept entries); the groups of one head add their sums
 // in LDS. Rows without kept entries in the chunk write nothing. Called by every
 // thread of the block.
-template <typename T, int D, int CH>
+template <typename T, int D, int CH, bool PAGED>
 __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const StreamArgs& a, int b, int j0, int nh,
                                               int c, int hs, int hsplit) {
   constexpr int EPL = Unpack<T>::kN;                    // columns per 16-byte piece
@@ -114,6 +185,8 @@ __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const Strea
   const int vh = j / a.g_v;
   const int base = c * CH;
   const T* vrow = reinterpret_cast<const T*>(a.v) + ((size_t)(b * a.h_v + vh) * a.l_max + base) * D + pc * EPL;
+  const CacheRows<T, D, true> vpg(a.v, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vh, a.h_v, 0);
+  const int pbase = base & ((1 << a.page_shift) - 1);  // offset of the chunk in its first page
   const float m = act ? order_key_to_f32(kl.mx[h]) : 0.f;
   float acc[PPL][EPL];
 #pragma unroll
@@ -132,7 +205,9 @@ __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const Strea
 #pragma unroll
       for (int p = 0; p < PPL; ++p) x[u][p] = make_uint4(0, 0, 0, 0);
       if (e < n) {
-        const T* r = vrow + (size_t)kl.off[h][e] * D;
+        const int off = kl.off[h][e];
+        const T* r = PAGED ? vpg.in_page(kl.pg[(pbase + off) >> a.page_shift], base + off) + pc * EPL
+                           : vrow + (size_t)off * D;
 #pragma unroll
         for (int p = 0; p < PPL; ++p) x[u][p] = ld16(r + 16 * p * EPL);
         w[u] = expf(kl.val[h][e] - m);
@@ -211,7 +286,7 @@ enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 // the heads h of the tile with h mod hsplit == hs (every block computes all the
 // tile's logits; its duplicate key reads hit the cache).
 // grid = (nch, h_k * htiles * hsplit, B), block = 256.
-template <typename T, int D, int MODE, bool GATHER>
+template <typename T, int D, int MODE, bool GATHER, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
   constexpr int CH = StreamCfg<T, D>::kChunk;
@@ -238,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
 
   floatx4 sc[TPW];
   QK<T, D> qk;
-  const T* kh = kbase + (size_t)(b * h_k + g) * l_max * D;
+  const CacheRows<T, D, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, g, h_k, l_max);
   if constexpr (MODE == kFromKeysSpeculative) {
     qk.load_q(qbase + (size_t)row0 * D, nh, lane);
     score_tiles<T, D, TPW>(sc, qk, kh, wbase, max_l_kv, lane, scale);
@@ -251,6 +326,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     kl.cnt[tid] = 0;
     kl.mx[tid] = 0u;
   }
+  if constexpr (PAGED && GATHER) stage_pages<CH>(kl, a, b, base);
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
   if constexpr (MODE == kFromScores) {
     const float* srow = a.scores + (long long)(row0 + (live ? hh : 0)) * a.lpad;
@@ -300,13 +376,13 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
     *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
   }
-  if constexpr (GATHER) chunk_records<T, D, CH>(kl, a, b, j0, nh, c, hs, hsplit);
+  if constexpr (GATHER) chunk_records<T, D, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit);
 }
 
 // The chunk records of eq. (7) from kept lists already in the workspace (the
 // separately callable gather stage): stages each head's kept entries of the chunk
 // in LDS, then chunk_records. grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
   constexpr int CH = StreamCfg<T, D>::kChunk;
   const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
@@ -324,6 +400,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
     kl.cnt[tid] = h.cnt;
     kl.mx[tid] = order_key(h.mx);
   }
+  if constexpr (PAGED) stage_pages<CH>(kl, a, b, base);
   __syncthreads();
   for (int e = tid; e < nh * CH; e += kBlock) {
     const int h = e / CH, i = e - h * CH;
@@ -334,14 +411,14 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
     }
   }
   __syncthreads();
-  chunk_records<T, D, CH>(kl, a, b, j0, nh, c, 0, 1);
+  chunk_records<T, D, CH, PAGED>(kl, a, b, j0, nh, c, 0, 1);
 }
 
 // ----------------------------------------------------------------------------
 // Refresh, pass 1: logits of every cached key stored as fp32, plus a histogram of
 // the top 8 bits of their order keys per query head (accumulated into a.hist).
 // grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
   constexpr int CH = StreamCfg<T, D>::kChunk;
@@ -361,7 +438,7 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
 
   QK<T, D> qk;
   qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
-  const T* kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.h_k + g) * a.l_max * D;
+  const auto kh = key_rows<T, D, PAGED>(a, b, g);
   const int wbase = base + wv * 16 * TPW;
   floatx4 sc[TPW];
   score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
@@ -564,7 +641,7 @@ __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[
 // N-th largest as a new threshold (a forced refresh), then the kept set, its maximum
 // and the sparse softmax-PV. Used for a stale threshold that keeps nothing (the
 // forced refresh). Writes out, tau (refresh only), sel_count, sel_idx and flags.
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, bool PAGED>
 __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh_tau, float (*s_red)[D],
                           float* s_z) {
   constexpr int NW = NT / kWave;
@@ -583,7 +660,7 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
   {
     QK<T, D> qk;
     qk.load_q(reinterpret_cast<const T*>(s.q) + (size_t)(b * s.h_q + j0) * D, nh, lane);
-    const T* kh = reinterpret_cast<const T*>(s.k) + (size_t)(b * s.h_k + g) * s.l_max * D;
+    const auto kh = key_rows<T, D, PAGED>(s, b, g);
     const int kq = lane >> 4;
     for (int base = 0; base < L; base += NW * 16 * TPW) {
       const int wbase = base + wv * 16 * TPW;
@@ -628,7 +705,7 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
 
   const int vh = j / s.g_v;
   const int grp = tid / RG::G, gl = tid - grp * RG::G;
-  const T* vbase = reinterpret_cast<const T*>(s.v) + (size_t)(b * s.h_v + vh) * s.l_max * D + gl * RG::EPL;
+  const auto vr = value_rows<T, D, PAGED>(s, b, vh);
   float acc[RG::EPL];
 #pragma unroll
   for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
@@ -652,7 +729,7 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
       const int idx = s_list_i[p];
       const float w = expf(s_list_v[p] - m);
       float x[RG::EPL];
-      Unpack<T>::run(ld16(vbase + (size_t)idx * D), x);
+      Unpack<T>::run(ld16(vr.row(idx) + gl * RG::EPL), x);
 #pragma unroll
       for (int e = 0; e < RG::EPL; ++e) acc[e] += w * x[e];
       z += w;
@@ -685,7 +762,7 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
 // by block 0 (forced refresh). grid = (D / 16, h_q, B), block = 256.
 constexpr int kCombRegs = 8;  // chunk slots per thread read speculatively
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   constexpr int CH = StreamCfg<T, D>::kChunk;
   constexpr int CB = D / 16;
@@ -748,7 +825,7 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   int total;
   int pos = block_max_excl_scan(m, qd == 0 ? tsum : 0, s_ftmp, s_itmp, M, total);
   if (total == 0) {
-    if (cb == 0) exact_row<T, D, kBlock>(a, b, j, L, true, s_red, s_z);
+    if (cb == 0) exact_row<T, D, kBlock, PAGED>(a, b, j, L, true, s_red, s_z);
     return;
   }
 
@@ -825,9 +902,11 @@ struct DenseArgs {
   const int32_t* l_kv;
   float* part;     // [B*h_q, nchd, D+4] per-chunk (m, Z, -, -, o[D])
   void* out;
+  const int32_t* ptab;  // paged caches: [B, ptab_stride] page ids
   int h_q, h_k, h_v, g, l_max, nchd, out_bf16;  // g = h_q / h_v query heads per value head
   int max_l_kv;
   float scale;
+  int ptab_stride, page_shift, num_pages;     // paged caches (see StreamArgs)
 };
 
 // grid = (nchd, h_v, B), block = 256. Each block takes one chunk of CHD keys and one
@@ -835,7 +914,7 @@ struct DenseArgs {
 // h_v, so the g heads share one; MFMA), the chunk's softmax numerator relative to the
 // chunk maximum, and its product with the chunk's rows of value head v (VALU). The
 // value and key loads of the chunk are all issued before the first MFMA.
-template <typename T, int D, int GH>
+template <typename T, int D, int GH, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   constexpr int TPW = StreamCfg<T, D>::kTPW;
   constexpr int CHD = StreamCfg<T, D>::kChunk;
@@ -861,20 +940,28 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   __shared__ float s_m[kWaves][GH], s_z[kWaves][GH];
   __shared__ float s_o[kWaves][GH][D];
 
-  const T* kh = kbase + (size_t)(b * h_k + kg) * l_max * D;
-  const T* vh = vbase + (size_t)(b * h_v + vg) * l_max * D;
+  const CacheRows<T, D, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, kg, h_k, l_max);
+  const CacheRows<T, D, PAGED> vh(vbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vg, h_v, l_max);
   const int wbase = base + wv * 16 * TPW;
 
   // value tiles: load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
   uint4 vb[TPW][VL];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int t = 0; t < TPW; ++t) {
+    const int t0 = min(wbase + 16 * t, (L - 1) & ~15);  // a clamped tile lies inside one page
+    const T* vt = PAGED ? vh.tile(t0) : vh.row(0);
 #pragma unroll
     for (int r = 0; r < VL; ++r) {
       const int e = r * kWave + lane;
-      const int key = min(wbase + 16 * t + e / G, L - 1);
-      vb[t][r] = ld16(vh + (size_t)key * D + (e % G) * EPL);
+      if constexpr (PAGED) {
+        const int key = min(t0 + e / G, L - 1);
+        vb[t][r] = ld16(vt + (size_t)(key - t0) * D + (e % G) * EPL);
+      } else {
+        const int key = min(wbase + 16 * t + e / G, L - 1);
+        vb[t][r] = ld16(vt + (size_t)key * D + (e % G) * EPL);
+      }
     }
+  }
 
   QK<T, D> qk;
   qk.load_q(qbase + (size_t)row0 * D, gq, lane);

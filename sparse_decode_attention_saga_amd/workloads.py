@@ -181,6 +181,45 @@ def generate(w: Workload, seed: int = 0, l_max: Optional[int] = None,
     return Inputs(to_dtype(q, dt), to_dtype(K, dt), to_dtype(V, dt), lens)
 
 
+@dataclass
+class PagedKV:
+    """Paged copies of a K/V cache pair (the layout of the library's paged calls).
+
+    k_pages [num_pages, h_k, P, d] and v_pages [num_pages, h_v, P, d] hold the token
+    rows, P = page_tokens per page; table[b, p] is the page of tokens [p*P, (p+1)*P)
+    of sequence b. Pages are placed in a seeded random order, with `spare` pool pages
+    that no sequence uses; table entries for pages wholly past l_kv[b] are set to
+    `stale` (any value: the library never uses them for results).
+    """
+
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    table: torch.Tensor  # int32 [B, max_pages]
+    page_tokens: int
+
+
+def paginate(k: torch.Tensor, v: torch.Tensor, l_kv: np.ndarray, page_tokens: int, seed: int = 0,
+             spare: int = 3, stale: int = -1) -> PagedKV:
+    """Scatter contiguous caches k [B, h_k, L_max, d], v [B, h_v, L_max, d] into pages."""
+    B, h_k, L_max, d = k.shape
+    P = int(page_tokens)
+    max_pages = max(1, -(-L_max // P))
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x9A9E, seed])))
+    num_pages = B * max_pages + spare
+    order = rng.permutation(num_pages).astype(np.int32)
+    table = order[:B * max_pages].reshape(B, max_pages).copy()
+    kp = torch.zeros((num_pages, h_k, P, d), dtype=k.dtype)
+    vp = torch.zeros((num_pages, v.shape[1], P, d), dtype=v.dtype)
+    for b in range(B):
+        for p in range(max_pages):
+            lo, hi = p * P, min((p + 1) * P, L_max)
+            kp[table[b, p], :, :hi - lo] = k[b, :, lo:hi]
+            vp[table[b, p], :, :hi - lo] = v[b, :, lo:hi]
+        used = -(-int(l_kv[b]) // P)
+        table[b, used:] = stale
+    return PagedKV(kp, vp, torch.from_numpy(table), P)
+
+
 class DecodeStream:
     """A growing cache for multi-step decode runs: appends rows and drifts q.
 

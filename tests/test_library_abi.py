@@ -111,6 +111,53 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.saga_workspace_init(None, 16, None) == api.ERR_NULL
 
 
+def pages(table=FAKE, max_pages=64, page_tokens=16, num_pages=64):
+    return api.SagaPages(table.value if table is not None else None, max_pages, page_tokens, num_pages)
+
+
+def decode_paged(lib, pg, max_l=1024, s=None):
+    s = shape() if s is None else s
+    return lib.saga_decode_attn_paged(ctypes.byref(s), None if pg is None else ctypes.byref(pg), FAKE, FAKE,
+                                      FAKE, FAKE, max_l, 8, 4, 1, FAKE, FAKE, None, None, 0, None, FAKE,
+                                      1 << 40, None)
+
+
+def test_paged_entry_points_reject_bad_page_descriptors(lib):
+    assert decode_paged(lib, None) == api.ERR_NULL
+    assert decode_paged(lib, pages(table=None)) == api.ERR_NULL
+    assert decode_paged(lib, pages(page_tokens=8)) == api.ERR_SHAPE          # below one 16-key tile
+    assert decode_paged(lib, pages(page_tokens=48)) == api.ERR_SHAPE         # not a power of two
+    assert decode_paged(lib, pages(max_pages=63)) == api.ERR_SHAPE           # 63 * 16 < 1024 tokens
+    assert decode_paged(lib, pages(num_pages=0)) == api.ERR_SHAPE
+    assert decode_paged(lib, pages(), s=shape(h_k=5)) == api.ERR_SHAPE       # shape checks still apply
+    assert decode_paged(lib, pages(), max_l=131073) == api.ERR_SHAPE
+    pg = pages(page_tokens=32)
+    assert lib.saga_dense_gqa_attn_paged(ctypes.byref(shape()), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, 1024,
+                                         None, FAKE, 1 << 40, None) == api.ERR_NULL
+    assert lib.saga_dense_gqa_attn_paged(ctypes.byref(shape()), ctypes.byref(pages(max_pages=1)), FAKE, FAKE,
+                                         FAKE, FAKE, 1024, FAKE, FAKE, 1 << 40, None) == api.ERR_SHAPE
+
+
+def test_paginate_places_every_token_row():
+    import numpy as np
+    import torch
+    from sparse_decode_attention_saga_amd import workloads as wl
+    w = wl.Workload("paginate", 7, batch=3, h_q=4, h_k=2, h_v=4, d=64, l_kv=300, N=4, refresh_period=1,
+                    dtype="bf16", plant_frac=0.0)
+    x = wl.generate(w, seed=1, lengths=[300, 17, 0], l_max=300)
+    pk = wl.paginate(x.k, x.v, x.l_kv, 64, seed=2, stale=-9)
+    assert pk.k_pages.shape == (3 * 5 + 3, 2, 64, 64) and pk.v_pages.shape == (18, 4, 64, 64)
+    tab = pk.table.numpy()
+    assert np.all(tab[1, 1:] == -9) and np.all(tab[2] == -9)
+    used = tab[tab >= 0]
+    assert len(set(used.tolist())) == used.size                                # no page shared
+    for b in range(3):
+        for i in range(int(x.l_kv[b])):
+            pg = tab[b, i // 64]
+            assert torch.equal(pk.k_pages[pg, :, i % 64], x.k[b, :, i])
+            assert torch.equal(pk.v_pages[pg, :, i % 64], x.v[b, :, i])
+
+
 def test_binding_requires_gpu_tensors(lib):
     import torch
     q = torch.zeros(1, 4, 64)
