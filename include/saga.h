@@ -194,6 +194,62 @@ saga_status saga_dense_gqa_attn_paged(const saga_shape* s, const saga_pages* pag
                                       int32_t max_l_kv, void* out, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------
+ * A decode layer around the attention step (one new token per sequence), for
+ * measuring the step inside a model layer with random weights. Eq. (1) of the
+ * summary page ("Attention Mechanism Formalization"): Q = X W_Q, K = X W_K,
+ * V = X W_V, with h_k key heads and h_v value heads ("SAGA Architecture"), then the
+ * attention and the output projection W_O. Normalisation, rotary embeddings, biases
+ * and the residual are the caller's (the pages define none for this step).
+ * Weights and activations are bf16, products accumulate in fp32.
+ *   x      [B, d_model]                     the new token's hidden state per sequence
+ *   w_qkv  [(h_q + h_k + h_v)*d, d_model]   rows: the q features (head-major), then
+ *                                           the k features, then the v features
+ *                                           (i.e. W_Q, W_K, W_V transposed, stacked)
+ *   w_o    [d_model, h_q*d]                 W_O transposed: row o gives output o
+ *   y      [B, d_model]                     attn.out_dtype
+ * ------------------------------------------------------------------------------ */
+typedef enum saga_attention { SAGA_ATTN_ATOPN = 0, SAGA_ATTN_DENSE = 1 } saga_attention;
+
+typedef struct saga_layer {
+  saga_shape attn;   /* heads, d, cache capacity l_max, scale; dtype must be SAGA_BF16;
+                        out_dtype is the dtype of y (the attention output feeding
+                        W_O is bf16) */
+  int32_t d_model;   /* hidden size: a multiple of 32 */
+} saga_layer;
+
+/* y[b, o] = sum_i x[b, i] * w[o, i]: x [batch, n_in] bf16, w [n_out, n_in] bf16,
+ * y [batch, n_out] in out_dtype; fp32 accumulation, bf16 output rounded to nearest
+ * even. n_in must be a multiple of 32 (SAGA_ERR_SHAPE otherwise). */
+saga_status saga_linear(int32_t batch, int32_t n_in, int32_t n_out, const void* x, const void* w, void* y,
+                        int32_t out_dtype, void* stream);
+
+/* Eq. (1) for the new token plus the cache append: q [B, h_q, d] (bf16) = the first
+ * h_q*d projections; the next h_k*d and h_v*d projections, rounded to bf16, become
+ * row l_kv[b] of every key and value head of sequence b (caches [B, h_k, l_max, d]
+ * and [B, h_v, l_max, d]); l_kv_next[b] = l_kv[b] + 1. A full cache (l_kv[b] ==
+ * l_max) gets no row and l_kv_next[b] = l_max. l_kv and l_kv_next must be different
+ * arrays. */
+saga_status saga_qkv_append(const saga_layer* L, const void* x, const void* w_qkv, void* k_cache,
+                            void* v_cache, const int32_t* l_kv, int32_t* l_kv_next, void* q,
+                            void* stream);
+
+/* Workspace of saga_decode_layer: the attention's workspace (same zero-fill rule,
+ * saga_workspace_init) plus the q and attention-output activations. 0 if invalid. */
+size_t saga_layer_workspace_bytes(const saga_layer* L, int32_t N, int32_t max_l_kv);
+
+/* One decode layer: saga_qkv_append, then the attention over the l_kv_next[b] rows
+ * (attention = SAGA_ATTN_ATOPN: saga_decode_attn with N, refresh_period, step, tau,
+ * sel_count and flags as there; SAGA_ATTN_DENSE: saga_dense_gqa_attn, tau, N and
+ * the step arguments unused), then y = O W_O with O [B, h_q*d] the bf16 attention
+ * output. max_l_kv (host) bounds l_kv_next[] (<= l_max). Every argument is checked
+ * before the first launch. */
+saga_status saga_decode_layer(const saga_layer* L, int32_t attention, const void* x, const void* w_qkv,
+                              const void* w_o, void* k_cache, void* v_cache, const int32_t* l_kv,
+                              int32_t* l_kv_next, int32_t max_l_kv, int32_t N, int32_t refresh_period,
+                              int64_t step, float* tau, void* y, int32_t* sel_count, int32_t* flags,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

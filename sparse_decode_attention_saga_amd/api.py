@@ -18,7 +18,9 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, BF16 = 0, 1
 EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "saga_decode_attn",
            "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather",
-           "saga_select_gather", "saga_split_combine", "saga_decode_attn_paged", "saga_dense_gqa_attn_paged")
+           "saga_select_gather", "saga_split_combine", "saga_decode_attn_paged", "saga_dense_gqa_attn_paged",
+           "saga_linear", "saga_qkv_append", "saga_layer_workspace_bytes", "saga_decode_layer")
+ATTN_ATOPN, ATTN_DENSE = 0, 1
 FLAG_REFRESHED, FLAG_FORCED = 1, 2
 
 
@@ -33,6 +35,11 @@ class SagaPages(ctypes.Structure):
     """Mirror of `saga_pages` in include/saga.h."""
     _fields_ = [("table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32)]
+
+
+class SagaLayer(ctypes.Structure):
+    """Mirror of `saga_layer` in include/saga.h."""
+    _fields_ = [("attn", SagaShape), ("d_model", ctypes.c_int32)]
 
 
 class SagaError(RuntimeError):
@@ -58,6 +65,11 @@ _SIGS = {
     "saga_decode_attn_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P,
                                       _SZ, _P]),
     "saga_dense_gqa_attn_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_linear": (_I32, [_I32, _I32, _I32, _P, _P, _P, _I32, _P]),
+    "saga_qkv_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "saga_layer_workspace_bytes": (_SZ, [_P, _I32, _I32]),
+    "saga_decode_layer": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P,
+                                 _SZ, _P]),
 }
 
 
@@ -344,4 +356,107 @@ def dense_gqa_attn_paged(q, k_pages, v_pages, table, l_kv, *, max_l_kv: Optional
                                          _ptr(v_pages), _ptr(l_kv), max_l_kv, _ptr(out), _ptr(ws.buf), ws.nbytes,
                                          _stream(q.device, stream))
     _check(st, "saga_dense_gqa_attn_paged")
+    return out
+
+
+# --- decode layer (eq. (1) projections, cache append, attention, W_O) -------------
+
+def linear(x, w, *, out=None, out_dtype=None, stream=None):
+    """saga_linear: y = x w^T for x [B, n_in] and w [n_out, n_in], both bfloat16."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [B, n_in] and w [n_out, n_in]")
+    B, n_out = x.shape[0], w.shape[0]
+    if out is None:
+        out = torch.empty(B, n_out, dtype=out_dtype or torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out")
+        if tuple(out.shape) != (B, n_out):
+            raise ValueError("out must be [B, n_out]")
+    st = lib().saga_linear(B, x.shape[1], n_out, _ptr(x), _ptr(w), _ptr(out), dtype_code(out.dtype),
+                           _stream(x.device, stream))
+    _check(st, "saga_linear")
+    return out
+
+
+def layer_desc(x, k_cache, v_cache, h_q: int, out_dtype=None, scale: float = 0.0) -> SagaLayer:
+    """The layer descriptor for x [B, d_model] and caches [B, h_k, l_max, d], [B, h_v, l_max, d]."""
+    if x.dim() != 2 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("x must be [B, d_model], caches [B, heads, l_max, d]")
+    B, h_k, l_max, d = k_cache.shape
+    if v_cache.shape[0] != B or v_cache.shape[2:] != k_cache.shape[2:] or x.shape[0] != B:
+        raise ValueError("x, k_cache and v_cache disagree")
+    for t in (x, k_cache, v_cache):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("the layer computes in bfloat16")
+    shape = SagaShape(B, h_q, h_k, v_cache.shape[1], d, l_max, BF16, dtype_code(out_dtype or torch.bfloat16),
+                      float(scale))
+    return SagaLayer(shape, x.shape[1])
+
+
+def qkv_append(x, w_qkv, k_cache, v_cache, l_kv, l_kv_next, *, h_q: int, q=None, stream=None):
+    """saga_qkv_append: q (returned, [B, h_q, d] bf16) and the new cache rows."""
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, torch.bfloat16)
+    _dev(l_kv, "l_kv", torch.int32)
+    _dev(l_kv_next, "l_kv_next", torch.int32)
+    L = layer_desc(x, k_cache, v_cache, h_q)
+    if tuple(w_qkv.shape) != ((h_q + L.attn.h_k + L.attn.h_v) * L.attn.d, L.d_model):
+        raise ValueError("w_qkv must be [(h_q + h_k + h_v) * d, d_model]")
+    if q is None:
+        q = torch.empty(x.shape[0], h_q, L.attn.d, dtype=torch.bfloat16, device=x.device)
+    st = lib().saga_qkv_append(ctypes.byref(L), _ptr(x), _ptr(w_qkv), _ptr(k_cache), _ptr(v_cache), _ptr(l_kv),
+                               _ptr(l_kv_next), _ptr(q), _stream(x.device, stream))
+    _check(st, "saga_qkv_append")
+    return q
+
+
+class LayerWorkspace:
+    """Device workspace of saga_decode_layer, zero-filled once."""
+
+    def __init__(self, L: SagaLayer, N: int, max_l_kv: int, device, stream=None):
+        n = lib().saga_layer_workspace_bytes(ctypes.byref(L), int(N), int(max_l_kv))
+        if n == 0:
+            raise ValueError("invalid layer shape for the workspace")
+        self.nbytes = int(n)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        _check(lib().saga_workspace_init(_ptr(self.buf), self.nbytes, _stream(self.buf.device, stream)),
+               "saga_workspace_init")
+
+
+def decode_layer(x, w_qkv, w_o, k_cache, v_cache, l_kv, l_kv_next, *, h_q: int, attention: int = ATTN_ATOPN,
+                 N: int = 1, refresh_period: int = 1, step: int = 0, tau=None, max_l_kv: Optional[int] = None,
+                 out=None, out_dtype=None, sel_count=None, flags=None, workspace: Optional[LayerWorkspace] = None,
+                 scale: float = 0.0, stream=None):
+    """saga_decode_layer: one decode layer for the new token x [B, d_model]; returns y [B, d_model]."""
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("w_o", w_o), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, torch.bfloat16)
+    _dev(l_kv, "l_kv", torch.int32)
+    _dev(l_kv_next, "l_kv_next", torch.int32)
+    if out_dtype is None and out is not None:
+        out_dtype = out.dtype
+    L = layer_desc(x, k_cache, v_cache, h_q, out_dtype, scale)
+    if tuple(w_qkv.shape) != ((h_q + L.attn.h_k + L.attn.h_v) * L.attn.d, L.d_model):
+        raise ValueError("w_qkv must be [(h_q + h_k + h_v) * d, d_model]")
+    if tuple(w_o.shape) != (L.d_model, h_q * L.attn.d):
+        raise ValueError("w_o must be [d_model, h_q * d]")
+    if tau is not None:
+        _dev(tau, "tau", torch.float32)
+    for name, t in (("sel_count", sel_count), ("flags", flags)):
+        if t is not None:
+            _dev(t, name, torch.int32)
+    if max_l_kv is None:
+        max_l_kv = L.attn.l_max
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out")
+    n = N if attention == ATTN_ATOPN else 1
+    ws = workspace or LayerWorkspace(L, n, max_l_kv, x.device)
+    st = lib().saga_decode_layer(ctypes.byref(L), int(attention), _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(l_kv), _ptr(l_kv_next), int(max_l_kv), int(N),
+                                 int(refresh_period), int(step), _ptr(tau), _ptr(out), _ptr(sel_count),
+                                 _ptr(flags), _ptr(ws.buf), ws.nbytes, _stream(x.device, stream))
+    _check(st, "saga_decode_layer")
     return out

@@ -10,8 +10,9 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libsaga.so")
-SOURCES = [os.path.join(HERE, "csrc", "saga_api.hip")]
-# the decode library's sources (what a build of its kernels depends on)
+SOURCES = [os.path.join(HERE, "csrc", "saga_api.hip"), os.path.join(HERE, "csrc", "saga_layer.hip")]
+# the decode-attention kernels' sources (what a build of those kernels depends on;
+# the layer's projection kernels are not among them)
 LIB_FILES = [os.path.join(HERE, "csrc", n) for n in ("saga_api.hip", "saga_device.cuh", "saga_kernels.cuh")] + \
     [os.path.join(ROOT, "include", "saga.h")]
 # streaming-read probe used by the benchmark (not part of the decode library)

@@ -220,6 +220,48 @@ def paginate(k: torch.Tensor, v: torch.Tensor, l_kv: np.ndarray, page_tokens: in
     return PagedKV(kp, vp, torch.from_numpy(table), P)
 
 
+@dataclass
+class LayerInputs:
+    """Random-init weights of one attention layer and the new token's hidden state
+    (the layout of the library's layer calls), as CPU bfloat16 tensors."""
+
+    x: torch.Tensor       # [B, D]
+    w_qkv: torch.Tensor   # [(h_q + h_k + h_v) * d, D]: rows of W_Q^T, then W_K^T, then W_V^T
+    w_o: torch.Tensor     # [D, h_q * d]: rows of W_O^T
+
+
+def layer_inputs(w: Workload, seed: int = 0, d_model: Optional[int] = None, h_k: Optional[int] = None,
+                 h_v: Optional[int] = None, exact: bool = False) -> LayerInputs:
+    """Weights at the workload's head shape (h_k / h_v override it, e.g. for the dense
+    baseline's h_kv heads). D = d_model defaults to h_q * d, the hidden size of both
+    models the pages time (Llama 3.2-1B: 32 x 64; Qwen2.5-1.5B: 12 x 128).
+
+    Default: x ~ N(0, 1); weight entries ~ N(0, 1 / fan_in) (fan_in = D for w_qkv,
+    h_q d for w_o); all rounded to bfloat16 (nearest even).
+    exact=True: x entries in {-1, 0, +1} with at most 255 nonzero entries per row and
+    w_qkv entries +-2^-4, so every projection is a multiple of 2^-4 of magnitude below
+    16: exact in any fp32 summation order and in bfloat16 (at most 8 significant bits).
+    w_o is drawn as in the default."""
+    h_k = w.h_k if h_k is None else h_k
+    h_v = w.h_v if h_v is None else h_v
+    D = w.h_q * w.d if d_model is None else int(d_model)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.workload_id, seed, 0x1A7E])))
+    n_qkv = (w.h_q + h_k + h_v) * w.d
+    if exact:
+        x = np.zeros((w.batch, D), np.float32)
+        nnz = min(255, D // 4)
+        for b in range(w.batch):
+            cols = rng.choice(D, size=nnz, replace=False)
+            x[b, cols] = rng.choice(np.array([-1.0, 1.0], np.float32), size=nnz)
+        w_qkv = rng.choice(np.array([-1.0, 1.0], np.float32), size=(n_qkv, D)) * np.float32(2.0 ** -4)
+    else:
+        x = rng.standard_normal((w.batch, D), dtype=np.float32)
+        w_qkv = rng.standard_normal((n_qkv, D), dtype=np.float32) / np.float32(np.sqrt(D))
+    w_o = rng.standard_normal((D, w.h_q * w.d), dtype=np.float32) / np.float32(np.sqrt(w.h_q * w.d))
+    bf = torch.bfloat16
+    return LayerInputs(to_dtype(x, bf), to_dtype(w_qkv, bf), to_dtype(w_o, bf))
+
+
 class DecodeStream:
     """A growing cache for multi-step decode runs: appends rows and drifts q.
 

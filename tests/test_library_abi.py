@@ -138,6 +138,42 @@ def test_paged_entry_points_reject_bad_page_descriptors(lib):
                                          FAKE, FAKE, 1024, FAKE, FAKE, 1 << 40, None) == api.ERR_SHAPE
 
 
+def layer(d_model=1536, **kw):
+    return api.SagaLayer(shape(l_max=4096, **kw), d_model)
+
+
+def test_layer_entry_points_reject_bad_arguments(lib):
+    big = 1 << 40
+    L = layer()
+    assert lib.saga_layer_workspace_bytes(ctypes.byref(L), 512, 4096) > lib.saga_workspace_bytes(
+        ctypes.byref(L.attn), 512, 4096)
+    assert lib.saga_layer_workspace_bytes(ctypes.byref(layer(d_model=100)), 512, 4096) == 0
+    assert lib.saga_layer_workspace_bytes(ctypes.byref(layer(dtype=api.F32)), 512, 4096) == 0
+    assert lib.saga_linear(1, 1536, 10, FAKE, FAKE, None, api.F32, None) == api.ERR_NULL
+    assert lib.saga_linear(1, 100, 10, FAKE, FAKE, FAKE, api.F32, None) == api.ERR_SHAPE   # n_in % 32
+    assert lib.saga_linear(0, 64, 10, FAKE, FAKE, FAKE, api.F32, None) == api.ERR_SHAPE
+    assert lib.saga_linear(1, 64, 10, FAKE, FAKE, FAKE, 7, None) == api.ERR_UNSUPPORTED
+    assert lib.saga_linear(1, 1 << 20, 10, FAKE, FAKE, FAKE, api.F32, None) == api.ERR_UNSUPPORTED
+    assert lib.saga_qkv_append(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == api.ERR_NULL
+    assert lib.saga_qkv_append(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == api.ERR_SHAPE
+    assert lib.saga_qkv_append(ctypes.byref(layer(dtype=api.F32)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                               ctypes.c_void_p(0x2000), FAKE, None) == api.ERR_UNSUPPORTED
+
+    def dl(L, attention=api.ATTN_ATOPN, tau=FAKE, max_l=4096, N=8, period=4, step=1, ws=big, l_next=None):
+        return lib.saga_decode_layer(ctypes.byref(L), attention, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     l_next or ctypes.c_void_p(0x2000), max_l, N, period, step, tau, FAKE, None,
+                                     None, FAKE, ws, None)
+    assert dl(L, tau=None) == api.ERR_NULL
+    assert dl(L, attention=5) == api.ERR_UNSUPPORTED
+    assert dl(L, max_l=4097) == api.ERR_SHAPE
+    assert dl(L, N=0) == api.ERR_SHAPE
+    assert dl(L, period=0) == api.ERR_SHAPE
+    assert dl(L, l_next=FAKE) == api.ERR_SHAPE            # l_kv and l_kv_next alias
+    assert dl(L, ws=1024) == api.ERR_WORKSPACE
+    assert dl(layer(d_model=48)) == api.ERR_SHAPE
+    assert dl(layer(h_q=8, h_k=4, h_v=2), attention=api.ATTN_DENSE, tau=None) == api.ERR_UNSUPPORTED
+
+
 def test_paginate_places_every_token_row():
     import numpy as np
     import torch
