@@ -34,6 +34,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -182,7 +184,28 @@ def read_probe(torch, reps: int) -> dict:
         table[blocks] = (n / (ms_big * 1e-3) / 1e9, (n // 32) / (ms_small * 1e-3) / 1e9, ms_small * 1e3)
     best_big = max(table, key=lambda b: table[b][0])
     best_small = max(table, key=lambda b: table[b][1])
+
+    # one read of S bytes per launch, consecutive slices over the whole GiB (so that
+    # no slice is still in the 256 MB cache when it is read again): the time of a
+    # short launch is a fixed part plus S over a streaming rate
+    by_size = {}
+    for mib in (2, 4, 8, 16, 32):
+        S = mib << 20
+        blocks = max(256, min(2048, S // 16384))
+
+        def sized():
+            for i in range(n // S):
+                launch(i * S, S, blocks)
+
+        sized()
+        torch.cuda.synchronize()
+        by_size[mib] = min(time_graph(torch, sized, reps)) / (n // S) * 1e3
+    xs = np.array([m * 1048576.0 for m in by_size])
+    ys = np.array([by_size[m] for m in by_size])
+    slope, t0 = np.polyfit(xs, ys, 1)
     return {"kernel": "k_stream_read (libsaga_probe.so)",
+            "per_launch_us_by_mib": {str(m): round(v, 3) for m, v in by_size.items()},
+            "fit_fixed_us": float(t0), "fit_stream_gbs": float(1e-3 / slope),
             "gib_read_gbs": table[best_big][0], "gib_blocks": best_big,
             "mib32_read_gbs": table[best_small][1], "mib32_read_us": table[best_small][2], "mib32_blocks": best_small,
             "by_blocks": {str(b): {"gib_gbs": round(v[0], 1), "mib32_gbs": round(v[1], 1), "mib32_us": round(v[2], 3)}
@@ -411,6 +434,85 @@ def paged_timing(torch, api, w, qs, ks, vs, taus, l_kv, L, args) -> list:
     return out
 
 
+def layer_timing(torch, api, wl, w, ks, vs, L, args) -> dict:
+    """One decode layer (QKV projection + cache append, attention, W_O) with random
+    weights at the workload's model shape: SAGA heads with Atop-N over the rotating
+    cache sets, against the dense GQA layer of the original head shape (dense_h_kv
+    key and value heads). Weights rotate with the caches. The new token is appended
+    at row L - 1, so the attention reads L rows as in the attention-only step."""
+    dev = ks[0].device
+    R = len(ks)
+    K, W = args.steps, args.warmup
+    D = w.h_q * w.d
+    bf = torch.bfloat16
+
+    def weight_sets(h_k, h_v, n):
+        return [wl.layer_inputs(w, seed=r, h_k=h_k, h_v=h_v) for r in range(n)]
+
+    l_kv = torch.full((w.batch,), L - 1, dtype=torch.int32, device=dev)
+    l_next = torch.empty_like(l_kv)
+    out = {"d_model": D}
+
+    def run(kset, vset, wsets, mode, label):
+        n = len(kset)
+        xs = [s.x.to(dev) for s in wsets]
+        wq = [s.w_qkv.to(dev) for s in wsets]
+        wo = [s.w_o.to(dev) for s in wsets]
+        taus = [torch.zeros(w.batch, w.h_q, dtype=torch.float32, device=dev) for _ in range(n)]
+        y = torch.empty(w.batch, D, dtype=bf, device=dev)
+        desc = api.layer_desc(xs[0], kset[0], vset[0], w.h_q, bf)
+        lws = api.LayerWorkspace(desc, w.N, L, dev)
+
+        def step(t):
+            r = t % n
+            api.decode_layer(xs[r], wq[r], wo[r], kset[r], vset[r], l_kv, l_next, h_q=w.h_q, attention=mode,
+                             N=w.N, refresh_period=w.refresh_period, step=t, tau=taus[r], max_l_kv=L, out=y,
+                             workspace=lws)
+
+        def proj(t):
+            r = t % n
+            q = api.qkv_append(xs[r], wq[r], kset[r], vset[r], l_kv, l_next, h_q=w.h_q)
+            api.linear(q.reshape(w.batch, -1), wo[r], out=y)
+
+        # every set starts from an exact threshold, as a decode loop would
+        for r in range(n):
+            api.decode_layer(xs[r], wq[r], wo[r], kset[r], vset[r], l_kv, l_next, h_q=w.h_q, attention=mode,
+                             N=w.N, refresh_period=1, step=0, tau=taus[r], max_l_kv=L, out=y, workspace=lws)
+        for t in range(W):
+            step(t)
+        torch.cuda.synchronize()
+        ms = time_graph(torch, lambda: [step(t) for t in range(W, W + K)], args.reps)
+        us = pct([1e3 * m / K for m in ms], 50)
+        ms = time_graph(torch, lambda: [proj(t) for t in range(W, W + K)], args.reps)
+        us_proj = pct([1e3 * m / K for m in ms], 50)
+        wbytes = (wq[0].numel() + wo[0].numel()) * 2
+        log(f"layer ({label}): {us:.2f} us/step; its two projections alone {us_proj:.2f} us "
+            f"({wbytes / 1e6:.1f} MB of weights)")
+        return us, us_proj, wbytes
+
+    us, us_proj, wb = run(ks, vs, weight_sets(w.h_k, w.h_v, R), api.ATTN_ATOPN, "SAGA + Atop-N")
+    out.update({"saga_us": us, "saga_projections_us": us_proj, "saga_weight_bytes": wb})
+    if w.dense_h_kv:
+        wd = w.with_(h_k=w.dense_h_kv, h_v=w.dense_h_kv, workload_id=w.workload_id + 100)
+        xd = wl.generate(wd, seed=0)
+        Rd = rotating_sets(bytemodel_dense_bytes(wd, L), 1, 0)
+        kd = [xd.k.to(dev)]
+        vd = [xd.v.to(dev)]
+        kd += [kd[0].clone() for _ in range(Rd - 1)]
+        vd += [vd[0].clone() for _ in range(Rd - 1)]
+        us_d, us_dp, wbd = run(kd, vd, weight_sets(wd.h_k, wd.h_v, Rd), api.ATTN_DENSE,
+                               f"dense GQA, h_kv={wd.h_k}")
+        out.update({"dense_h_kv": wd.h_k, "dense_us": us_d, "dense_projections_us": us_dp,
+                    "dense_weight_bytes": wbd, "speedup": us_d / us})
+        del kd, vd
+    return out
+
+
+def bytemodel_dense_bytes(wd, L) -> int:
+    from sparse_decode_attention_saga_amd import bytemodel
+    return bytemodel.dense_bytes(wd.h_k, wd.d, [L] * wd.batch, 2 if wd.dtype == "bf16" else 4)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,7 +525,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paged", type=int, nargs="*", default=[16, 256], metavar="P",
                     help="also time the step over paged caches with P-token pages (none: skip)")
-    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady", "paged"], default="all",
+    ap.add_argument("--no-layer", action="store_true", help="skip the decode-layer timing")
+    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady", "paged", "layer"], default="all",
                     help="time only one part (for profiler runs)")
     ap.add_argument("--probe", choices=["none", "copy", "read"], default="none",
                     help="copy: a plain device copy of 256 MiB (counter calibration); read: read ceilings")
@@ -578,6 +681,9 @@ def main() -> int:
         log(f"dense GQA (h_kv={wd.h_k}): {dense['us']:.2f} us/step")
         del kd, vd
 
+    if not args.no_layer and args.only in ("all", "layer"):
+        res["layer"] = layer_timing(torch, api, wl, w, ks, vs, L, args)
+
     if "paged" in res and "saga_us" in res:
         for p in res["paged"]:
             p["vs_contiguous"] = p["us_per_step"] / pct(res["saga_us"], 50)
@@ -634,6 +740,7 @@ def main() -> int:
         "forced_refresh_rows": forced,
         "read_ceiling": ceil,
         "paged": res.get("paged"),
+        "layer": res.get("layer"),
         "roofline": roof,
     }
     if dense:
@@ -643,6 +750,8 @@ def main() -> int:
                              "roofline_frac": dense["bytes"] / td / 1e9 / HBM_PEAK_GBS,
                              "rotating_sets": dense["sets"]}
         line["speedup_vs_dense"] = td / t_step
+        if line["layer"] and "speedup" in line["layer"]:
+            line["layer"]["attention_only_speedup"] = td / t_step
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -32,9 +32,6 @@ template <typename T, int D> struct StreamCfg {
   static constexpr int kChunk = 16 * kTPW * kWaves;
 };
 
-constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 for raw gfx9 buffers
-constexpr int kCoherent = 16;           // sc1 cache policy: coherent across the device's L2s
-
 // Summary of one chunk of one row (b, j), written by the select kernels: the number
 // of kept entries, the largest kept logit m and, once gathered, sum_i exp(A_i - m).
 struct __align__(16) ChunkHdr {
