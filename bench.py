@@ -520,6 +520,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--reps", type=int, default=20, help="timed graph replays (median, p10, p90 reported)")
     ap.add_argument("--workload", default="qwen2.5-1.5b-shape-l128k")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: >= 1 GiB of K)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -564,6 +565,8 @@ def main() -> int:
     from sparse_decode_attention_saga_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    if args.batch:
+        w = w.with_(batch=args.batch)
     dev = torch.device("cuda:0")
     api.lib()
     L = w.l_kv

@@ -22,12 +22,16 @@
 namespace saga {
 
 // Keys per block of the key-streaming kernels: 4 waves x TPW tiles x 16 keys.
+// W = 2 is the wide form for launches with many blocks: twice the tiles per wave
+// (at most 8: the kept mask of a lane holds 32 entries), so each resident block
+// keeps twice the keys in flight and a step has half the chunk records.
 #ifndef SAGA_KEY_BYTES_PER_WAVE
 #define SAGA_KEY_BYTES_PER_WAVE 16384  // K bytes one wave has in flight per chunk
 #endif
-template <typename T, int D> struct StreamCfg {
+template <typename T, int D, int W = 1> struct StreamCfg {
   static constexpr int kRowBytes = D * (int)sizeof(T);
-  static constexpr int kTPW = SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) > 0 ? SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) : 1;  // 16-key tiles per wave
+  static constexpr int kBase = SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) > 0 ? SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) : 1;
+  static constexpr int kTPW = kBase * W > 8 ? 8 : kBase * W;  // 16-key tiles per wave
   static_assert(kTPW >= 1, "at least one tile per wave");
   static constexpr int kChunk = 16 * kTPW * kWaves;
 };
@@ -283,10 +287,10 @@ enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 // the heads h of the tile with h mod hsplit == hs (every block computes all the
 // tile's logits; its duplicate key reads hit the cache).
 // grid = (nch, h_k * htiles * hsplit, B), block = 256.
-template <typename T, int D, int MODE, bool GATHER, bool PAGED>
+template <typename T, int D, int MODE, bool GATHER, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
-  constexpr int TPW = StreamCfg<T, D>::kTPW;
-  constexpr int CH = StreamCfg<T, D>::kChunk;
+  constexpr int TPW = StreamCfg<T, D, W>::kTPW;
+  constexpr int CH = StreamCfg<T, D, W>::kChunk;
   // every argument the key stream needs is read in one batch, before any arithmetic
   // on them (otherwise the pointers' reads may wait behind the index arithmetic)
   const T* const kbase = reinterpret_cast<const T*>(a.k);
@@ -379,9 +383,9 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
 // The chunk records of eq. (7) from kept lists already in the workspace (the
 // separately callable gather stage): stages each head's kept entries of the chunk
 // in LDS, then chunk_records. grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
-  constexpr int CH = StreamCfg<T, D>::kChunk;
+  constexpr int CH = StreamCfg<T, D, W>::kChunk;
   const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
   const int L = min(a.l_kv[b], a.max_l_kv);
   const int base = c * CH;
@@ -415,10 +419,10 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
 // Refresh, pass 1: logits of every cached key stored as fp32, plus a histogram of
 // the top 8 bits of their order keys per query head (accumulated into a.hist).
 // grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
-  constexpr int TPW = StreamCfg<T, D>::kTPW;
-  constexpr int CH = StreamCfg<T, D>::kChunk;
+  constexpr int TPW = StreamCfg<T, D, W>::kTPW;
+  constexpr int CH = StreamCfg<T, D, W>::kChunk;
   const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
   const int L = min(a.l_kv[b], a.max_l_kv);
   const int base = c * CH;
@@ -759,9 +763,9 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
 // by block 0 (forced refresh). grid = (D / 16, h_q, B), block = 256.
 constexpr int kCombRegs = 8;  // chunk slots per thread read speculatively
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
-  constexpr int CH = StreamCfg<T, D>::kChunk;
+  constexpr int CH = StreamCfg<T, D, W>::kChunk;
   constexpr int CB = D / 16;
   constexpr int kSlots = kBlock / 4;  // chunks per pass of the block
   const StreamArgs& sa = a.s;

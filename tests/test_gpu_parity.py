@@ -80,6 +80,32 @@ def test_small_shapes_refresh_and_stale(case):
     assert np.array_equal(got1["count"], got["count"])
 
 
+# launches with many blocks take the wide chunks (twice the keys per block); these
+# shapes reach them at sizes the oracle finishes quickly
+WIDE = [
+    # B, h_q, h_k, h_v, d, lens, dtype, N
+    (16, 12, 1, 4, 128, [16384, 1, 9000, 16383, 256, 511, 12000, 16384, 700, 16000, 3, 8192, 8193, 15000, 4097,
+                         16384], "bf16", 64),
+    (8, 32, 2, 8, 128, [16384, 16000, 9000, 16384, 2049, 16384, 12345, 16384], "bf16", 2048),
+    (16, 16, 1, 2, 128, [16384] * 16, "f32", 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE)))
+def test_wide_chunks_refresh_and_stale(case):
+    B, h_q, h_k, h_v, d, lens, dtype, N = WIDE[case]
+    say(f"wide case {case}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} N={N} {dtype}")
+    w, x = small(B, h_q, h_k, h_v, d, lens, dtype, seed=50 + case)
+    g = GpuCase(x, N, sel_cap=min(max(lens), 4 * N))
+    got = g.step(4, 0)
+    ref = oracle_step(x, N, 4, 0)
+    compare(got, ref, x, dtype, check_tau=True)
+    got1 = g.step(4, 1)
+    ref1 = oracle_step(x, N, 4, 1, tau_in=ref.tau)
+    compare(got1, ref1, x, dtype, check_tau=False)
+    assert np.array_equal(got1["count"], got["count"])
+
+
 def test_bf16_output_rounding():
     w, x = small(1, 12, 1, 4, 128, [5000], "bf16", seed=20)
     g = GpuCase(x, 64, out_dtype=torch.bfloat16)
