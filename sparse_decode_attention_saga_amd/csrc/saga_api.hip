@@ -120,7 +120,7 @@ Layout layout(const saga_shape* s, int max_l_kv) {
     return at;
   };
   // counters first: they must be zero before the first call and every call leaves them at zero
-  w.hist = take(rows * 256 * 4);
+  w.hist = take((size_t)kHistCopies * rows * 256 * 4);
   w.cand_cnt = take(rows * 4);
   w.scores = take(rows * (size_t)w.lpad * 4);
   w.surv_idx = take(rows * (size_t)w.lpad * 4);

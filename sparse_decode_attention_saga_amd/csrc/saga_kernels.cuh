@@ -8,7 +8,7 @@
 //
 // No kernel waits on another workgroup and none needs a device-scope fence: every
 // exchange between workgroups goes through a kernel boundary (the threshold
-// candidates are appended with device atomics and read by the next kernel).
+// histograms are accumulated with device atomics and read by the next kernel).
 //
 // Paper: "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding"
 // (summary page picx.dev DRD92V): eq. (2) logits, section "Methodology > Atop-N
@@ -62,7 +62,7 @@ struct StreamArgs {
   float* surv_val;         // [B*h_q, lpad] kept logits; also the threshold candidates
   ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
   float* part;             // [B*h_q, D/16, nch, 16] chunk records: sum w*v, 16 columns per slice
-  unsigned* hist;          // [B*h_q, 256] top-digit histogram (zero between calls)
+  unsigned* hist;          // [8, B*h_q, 256] top-digit histogram copies (zero between calls)
   unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
   const int32_t* ptab;     // paged caches: [B, ptab_stride] page ids (the kernels' PAGED form)
   long long lpad;
@@ -417,8 +417,12 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
 
 // ----------------------------------------------------------------------------
 // Refresh, pass 1: logits of every cached key stored as fp32, plus a histogram of
-// the top 8 bits of their order keys per query head (accumulated into a.hist).
+// the top 8 bits of their order keys per query head, accumulated into copy
+// (chunk mod kHistCopies) of a.hist: the logits of a row fall into a few bins, and
+// the copies spread the device atomics of the row's blocks over more addresses.
 // grid = (nch, h_k * htiles, B), block = 256.
+constexpr int kHistCopies = 8;
+
 template <typename T, int D, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D, W>::kTPW;
@@ -463,22 +467,41 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   __syncthreads();
   for (int e = tid; e < nh * 256; e += kBlock) {
     const unsigned h = s_hist[e];
-    if (h) atomicAdd(&a.hist[(long long)(row0 + e / 256) * 256 + (e & 255)], h);
+    if (h) {
+      const long long rows = (long long)gridDim.z * a.h_q;
+      atomicAdd(&a.hist[((c % kHistCopies) * rows + row0 + e / 256) * 256 + (e & 255)], h);
+    }
   }
 }
 
 // ----------------------------------------------------------------------------
-// Refresh, pass 2: candidates for the exact threshold. The top-digit histogram of a
-// row gives the 8-bit bin that holds its N-th largest logit; each block copies the
-// logits of its slice that fall in that bin to the row's candidate list (stored in
-// the row's kept-logit buffer, free at this point of a refresh step).
+// Refresh, pass 2: candidates for the exact threshold. The sum of the row's
+// histogram copies gives the 8-bit bin that holds its N-th largest logit; each block
+// copies the logits of its slice that fall in that bin to the row's candidate list
+// (stored in the row's kept-logit buffer, free at this point of a refresh step).
 // grid = (P, h_q, B) with P = ceil(max_l_kv / kSelSlice), block = 256.
 constexpr int kSelSlice = 4096;   // logits scanned per block
 constexpr int kCandLds = 8192;    // candidates the finishing block stages in LDS
 constexpr int kRowThreads = 1024; // threads of the one-block-per-row kernels
 
+// Sum of the kHistCopies copies of bin `bin` of row `row`; with `clear`, the copies
+// are returned to zero.
+__device__ __forceinline__ unsigned hist_sum(unsigned* hist, long long rows, long long row, int bin, bool clear) {
+  unsigned v[kHistCopies];
+#pragma unroll
+  for (int cp = 0; cp < kHistCopies; ++cp) v[cp] = hist[(cp * rows + row) * 256 + bin];
+  unsigned h = 0u;
+#pragma unroll
+  for (int cp = 0; cp < kHistCopies; ++cp) {
+    h += v[cp];
+    if (clear) hist[(cp * rows + row) * 256 + bin] = 0u;
+  }
+  return h;
+}
+
 __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const long long rows = (long long)gridDim.z * a.h_q;
   const long long row = (long long)b * a.h_q + j;
   const int L = min(a.l_kv[b], a.max_l_kv);
   const int N = a.N;
@@ -493,11 +516,7 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
   __shared__ float s_cand[kSelSlice];
   __shared__ int s_cc, s_base;
 
-  s_hist[tid] = a.hist[row * 256 + tid];
-  if (tid == 0) s_cc = 0;
-  __syncthreads();
-  digit_of_kth_largest(s_hist, (unsigned)N, s_itmp, s_res);
-  const unsigned d1 = s_res[0];
+  // the slice's logits are loaded with the histogram, before the bin is known
   const int hi = min(lo + kSelSlice, L);
   constexpr int PER = kSelSlice / kBlock;
   float vals[PER];
@@ -506,6 +525,11 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
     const int i = lo + u * kBlock + tid;
     vals[u] = (i < hi) ? a.scores[rbase + i] : 0.f;
   }
+  s_hist[tid] = hist_sum(a.hist, rows, row, tid, false);
+  if (tid == 0) s_cc = 0;
+  __syncthreads();
+  digit_of_kth_largest(s_hist, (unsigned)N, s_itmp, s_res);
+  const unsigned d1 = s_res[0];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int i = lo + u * kBlock + tid;
@@ -520,32 +544,32 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
 
 // Refresh, pass 3: the remaining 24 bits of the N-th largest logit resolved on the
 // candidates (counting repeats); writes tau (-inf when N >= l_kv, unchanged when
-// l_kv == 0) and returns the row's histogram and candidate count to zero.
+// l_kv == 0) and returns the row's histogram copies and candidate count to zero.
 // grid = (h_q, B), block = 1024.
 __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs a, float* tau_out) {
   constexpr int NT = kRowThreads;
   const int j = blockIdx.x, b = blockIdx.y;
+  const long long rows = (long long)gridDim.y * a.h_q;
   const long long row = (long long)b * a.h_q + j;
   const int L = min(a.l_kv[b], a.max_l_kv);
   const int N = a.N;
   const int tid = threadIdx.x;
-  if (L <= 0) return;
+  if (L <= 0) return;  // no block added to this row's histograms
 
   __shared__ unsigned s_hist[256];
   __shared__ int s_itmp[NT / kWave];
   __shared__ unsigned s_res[2];
   __shared__ float s_cand[kCandLds];
 
+  const unsigned C = a.cand_cnt[row];
+  if (tid < 256) s_hist[tid] = hist_sum(a.hist, rows, row, tid, true);
   if (N >= L) {
     if (tid == 0) tau_out[row] = -INFINITY;
-    if (tid < 256) a.hist[row * 256 + tid] = 0u;
     return;
   }
-  if (tid < 256) s_hist[tid] = a.hist[row * 256 + tid];
   __syncthreads();
   digit_of_kth_largest<NT>(s_hist, (unsigned)N, s_itmp, s_res);
   const unsigned d1 = s_res[0], k1 = s_res[1];
-  const unsigned C = a.cand_cnt[row];
   const float* cand = a.surv_val + row * a.lpad;
   if (C <= (unsigned)kCandLds) {
     for (int i0 = 0; i0 < (int)C; i0 += 4 * NT) {
@@ -572,7 +596,6 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
     tau_out[row] = order_key_to_f32(key);
     a.cand_cnt[row] = 0u;
   }
-  if (tid < 256) a.hist[row * 256 + tid] = 0u;
 }
 
 // ----------------------------------------------------------------------------
