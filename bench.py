@@ -43,7 +43,14 @@ if ROOT not in sys.path:
 METRIC = "decode-attn steps/s + % HBM roofline at l_kv=128K, bs=1 (SAGA+Atop-N vs dense GQA)"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_qk_select_gather_qwen128k_traffic.txt")
-DOMINANT = "k_qk_select<bf16, d=128, speculative keys, gather> (saga_select_gather)"
+DEFAULT_WORKLOAD = "qwen2.5-1.5b-shape-l128k"
+
+
+def dominant_kernel(w) -> str:
+    """Name of the select kernel a workload's step spends most of its time in."""
+    dims = f"d={w.d}" if w.dv == w.d else f"d_k={w.d}, d_v={w.dv}"
+    keys = "speculative keys" if w.batch == 1 else "keys after l_kv"
+    return f"k_qk_select<{w.dtype}, {dims}, {keys}, gather> (saga_select_gather)"
 
 
 def log(msg: str) -> None:
@@ -384,18 +391,19 @@ def decompose(torch, args) -> int:
 
 
 def device_pages(torch, k, v, page_tokens: int, seed: int):
-    """Paged copies of contiguous caches k [B, h_k, L, d], v [B, h_v, L, d] (L a
+    """Paged copies of contiguous caches k [B, h_k, L, d], v [B, h_v, L, d_v] (L a
     multiple of the page size) on the device, pages in a seeded random order:
-    (k_pages [B*L/P, h_k, P, d], v_pages [B*L/P, h_v, P, d], table [B, L/P] int32)."""
+    (k_pages [B*L/P, h_k, P, d], v_pages [B*L/P, h_v, P, d_v], table [B, L/P] int32)."""
     B, h_k, L, d = k.shape
+    h_v, dv = v.shape[1], v.shape[3]
     P = page_tokens
     n = L // P
     gen = torch.Generator().manual_seed(seed)
     perm = torch.randperm(B * n, generator=gen).to(torch.int64)
     kp = torch.empty((B * n, h_k, P, d), dtype=k.dtype, device=k.device)
-    vp = torch.empty((B * n, v.shape[1], P, d), dtype=v.dtype, device=v.device)
+    vp = torch.empty((B * n, h_v, P, dv), dtype=v.dtype, device=v.device)
     kp[perm.to(k.device)] = k.reshape(B, h_k, n, P, d).permute(0, 2, 1, 3, 4).reshape(B * n, h_k, P, d)
-    vp[perm.to(v.device)] = v.reshape(B, v.shape[1], n, P, d).permute(0, 2, 1, 3, 4).reshape(B * n, v.shape[1], P, d)
+    vp[perm.to(v.device)] = v.reshape(B, h_v, n, P, dv).permute(0, 2, 1, 3, 4).reshape(B * n, h_v, P, dv)
     table = perm.to(torch.int32).reshape(B, n).to(k.device)
     return kp, vp, table
 
@@ -411,7 +419,7 @@ def paged_timing(torch, api, w, qs, ks, vs, taus, l_kv, L, args) -> list:
             continue
         sets = [device_pages(torch, ks[r], vs[r], P, seed=r) for r in range(R)]
         tau_p = [t.clone() for t in taus]
-        o = torch.empty(w.batch, w.h_q, w.d, dtype=qs[0].dtype, device=qs[0].device)
+        o = torch.empty(w.batch, w.h_q, w.dv, dtype=qs[0].dtype, device=qs[0].device)
         shape = api.make_shape(qs[0], ks[0], vs[0])
         ws = api.Workspace(shape, w.N, L, qs[0].device)
 
@@ -519,7 +527,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--reps", type=int, default=20, help="timed graph replays (median, p10, p90 reported)")
-    ap.add_argument("--workload", default="qwen2.5-1.5b-shape-l128k")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: >= 1 GiB of K)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -573,7 +581,8 @@ def main() -> int:
     es = 2 if w.dtype == "bf16" else 4
     bytes_k = bytemodel.key_bytes(w.h_k, w.d, [L] * w.batch, es)
     R = rotating_sets(bytes_k, w.refresh_period, args.sets)
-    log(f"workload {w.name}: B={w.batch} h_q={w.h_q} h_k={w.h_k} h_v={w.h_v} d={w.d} l_kv={L} "
+    dims = f"d={w.d}" if w.dv == w.d else f"d_k={w.d} d_v={w.dv}"
+    log(f"workload {w.name}: B={w.batch} h_q={w.h_q} h_k={w.h_k} h_v={w.h_v} {dims} l_kv={L} "
         f"N={w.N} n={w.refresh_period}; {R} rotating sets")
 
     t0 = time.perf_counter()
@@ -585,11 +594,11 @@ def main() -> int:
     ks = [k0] + [k0.clone() for _ in range(R - 1)]
     vs = [v0] + [v0.clone() for _ in range(R - 1)]
     taus = [torch.zeros(w.batch, w.h_q, dtype=torch.float32, device=dev) for _ in range(R)]
-    out = torch.empty(w.batch, w.h_q, w.d, dtype=q0.dtype, device=dev)
+    out = torch.empty(w.batch, w.h_q, w.dv, dtype=q0.dtype, device=dev)
     shape = api.make_shape(q0, k0, v0)
     ws = api.Workspace(shape, w.N, L, dev)
     for r in range(R):
-        api.refresh_threshold(qs[r], ks[r], l_kv, taus[r], N=w.N, max_l_kv=L, workspace=ws)
+        api.refresh_threshold(qs[r], ks[r], l_kv, taus[r], N=w.N, max_l_kv=L, workspace=ws, d_v=w.dv)
     torch.cuda.synchronize()
 
     def saga_step(t):
@@ -654,8 +663,8 @@ def main() -> int:
             for j in heads:
                 rows.update(idx[b, j, : min(counts[b, j], cap)].tolist())
             union_rows.append(len(rows))
-    bytes_v = bytemodel.selected_value_bytes(union_rows, w.d, es)
-    bytes_v_per_head = int(counts.sum()) * w.d * es
+    bytes_v = bytemodel.selected_value_bytes(union_rows, w.dv, es)
+    bytes_v_per_head = int(counts.sum()) * w.dv * es
     bytes_step = bytes_k + bytes_v
 
     dense = {}
@@ -684,7 +693,7 @@ def main() -> int:
         log(f"dense GQA (h_kv={wd.h_k}): {dense['us']:.2f} us/step")
         del kd, vd
 
-    if not args.no_layer and args.only in ("all", "layer"):
+    if not args.no_layer and args.only in ("all", "layer") and w.dv == w.d:
         res["layer"] = layer_timing(torch, api, wl, w, ks, vs, L, args)
 
     if "paged" in res and "saga_us" in res:
@@ -701,12 +710,14 @@ def main() -> int:
     us = pct(res["saga_us"], 50)
     t_step = us * 1e-6
     step_gbs = bytes_step / t_step / 1e9
-    traffic, traffic_src = recorded_traffic()
+    # the recorded counters are those of the default workload's select kernel
+    traffic, traffic_src = recorded_traffic() if w.name == DEFAULT_WORKLOAD else (None, None)
     roof = None
     if "select_us" in res:
         achieved = bytes_step / (res["select_us"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": DOMINANT,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": dominant_kernel(w),
                 "kernel_us": res["select_us"], "bytes_per_launch": bytes_step,
                 "traffic_source": traffic_src}
     line = {
@@ -723,7 +734,7 @@ def main() -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_k": w.h_k, "h_v": w.h_v,
-                   "d": w.d, "l_kv": L, "N": w.N, "refresh_period": w.refresh_period,
+                   "d": w.d, "d_v": w.dv, "l_kv": L, "N": w.N, "refresh_period": w.refresh_period,
                    "accumulate": "f32", "rotating_sets": R, "dense_h_kv": w.dense_h_kv},
         "us_per_step": us,
         "us_per_step_p10": pct(res["saga_us"], 10),

@@ -16,8 +16,9 @@
  *   - Pointers are DEVICE pointers unless marked (host). The caller owns all memory;
  *     the library allocates nothing, keeps no pointer after returning, never
  *     synchronises the stream, never prints and never aborts.
- *   - Layouts (row-major, contiguous): q [B,h_q,d]; K [B,h_k,l_max,d]; V [B,h_v,l_max,d];
- *     out [B,h_q,d]; l_kv [B] int32; tau [B,h_q] float32. Rows >= l_kv[b] are never read.
+ *   - Layouts (row-major, contiguous): q [B,h_q,d]; K [B,h_k,l_max,d]; V [B,h_v,l_max,d_v];
+ *     out [B,h_q,d_v]; l_kv [B] int32; tau [B,h_q] float32. Rows >= l_kv[b] are never read.
+ *     d is the query/key head dimension, d_v the value head dimension (saga_shape.d_v).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *     Results are valid once the stream reaches the call.
  *   - Arguments are checked on the host before anything is launched; on any error
@@ -45,7 +46,7 @@ typedef enum saga_status {
   SAGA_OK = 0,
   SAGA_ERR_NULL = 1,        /* a required pointer is NULL */
   SAGA_ERR_SHAPE = 2,       /* inconsistent sizes: heads not divisible, N < 1, period < 1, ... */
-  SAGA_ERR_UNSUPPORTED = 3, /* valid but not built: d not in {64,128}, unknown dtype, too long */
+  SAGA_ERR_UNSUPPORTED = 3, /* valid but not built: (d, d_v) not built, unknown dtype, too long */
   SAGA_ERR_WORKSPACE = 4,   /* workspace smaller than saga_workspace_bytes() */
   SAGA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
 } saga_status;
@@ -59,7 +60,11 @@ typedef struct saga_shape {
   int32_t h_q;        /* query heads; multiple of h_k and of h_v */
   int32_t h_k;        /* key heads */
   int32_t h_v;        /* value heads */
-  int32_t d;          /* head dimension of q, K and V: 64 or 128 */
+  int32_t d;          /* head dimension of q and K (d_k): 32, 64 or 128, see d_v */
+  int32_t d_v;        /* head dimension of V and out; 0 means d. Built: d_v == d in {64, 128},
+                       * and the reduced key dimensions (d, d_v) = (32, 64), and (64, 128)
+                       * for bf16 (section "Training from Scratch": a key head dimension
+                       * below the value head dimension). The logit scale is 1/sqrt(d). */
   int32_t l_max;      /* cache capacity: row stride (in tokens) of K and V */
   int32_t dtype;      /* saga_dtype of q, K and V */
   int32_t out_dtype;  /* saga_dtype of out (bf16 output is rounded to nearest even) */
@@ -85,7 +90,7 @@ saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream);
  *   tau [B,h_q] in/out: the per-(sequence, query head) threshold state.
  *   Kept set S[b,j] = { i < l_kv[b] : A[b,j,i] >= tau[b,j] } (ties kept). If a stale
  *     threshold keeps nothing, that row is refreshed exactly at this step.
- *   out [B,h_q,d] (out_dtype): eq. (7) over S.
+ *   out [B,h_q,d_v] (out_dtype): eq. (7) over S.
  *   sel_count [B,h_q] (optional, may be NULL): |S[b,j]|.
  *   sel_idx [B,h_q,sel_cap] (optional): the first min(|S|, sel_cap) kept indices,
  *     in no particular order; entries past that are left untouched.
@@ -159,7 +164,7 @@ saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k
  * tokens live in fixed-size pages of a shared pool, found through a page table.
  *   Key pool   k_pages [num_pages, h_k, page_tokens, d] (dtype), one page holds the
  *              rows of every key head for page_tokens consecutive tokens;
- *   value pool v_pages [num_pages, h_v, page_tokens, d], with the same page ids;
+ *   value pool v_pages [num_pages, h_v, page_tokens, d_v], with the same page ids;
  *   table [B, max_pages] int32 (device): table[b*max_pages + p] is the page holding
  *              tokens [p*page_tokens, (p+1)*page_tokens) of sequence b.
  * page_tokens is a power of two >= 16; max_pages*page_tokens >= max_l_kv. Entries
@@ -212,7 +217,8 @@ saga_status saga_dense_gqa_attn_paged(const saga_shape* s, const saga_pages* pag
 typedef enum saga_attention { SAGA_ATTN_ATOPN = 0, SAGA_ATTN_DENSE = 1 } saga_attention;
 
 typedef struct saga_layer {
-  saga_shape attn;   /* heads, d, cache capacity l_max, scale; dtype must be SAGA_BF16;
+  saga_shape attn;   /* heads, d, cache capacity l_max, scale; dtype must be SAGA_BF16
+                        and d_v 0 or d (one head dimension for q, K and V);
                         out_dtype is the dtype of y (the attention output feeding
                         W_O is bf16) */
   int32_t d_model;   /* hidden size: a multiple of 32 */

@@ -32,7 +32,11 @@ Readings taken where the pages are silent (each one is a documented parameter):
     that step (the softmax of an empty set is undefined);
   * N >= l_kv gives threshold -inf, i.e. dense attention;
   * query head j reads key head floor(j*h_k/h_q) and value head floor(j*h_v/h_q);
-  * scale = 1/sqrt(d) unless given; thresholds are per (sequence, query head);
+  * scale = 1/sqrt(d) unless given, d the query/key head dimension; thresholds are
+    per (sequence, query head);
+  * the value head dimension d_v may differ from d (section "Training from
+    Scratch" compares a key head dimension below the value head dimension); the
+    output rows then have d_v entries;
   * l_kv[b] == 0 gives O = 0, an empty selection and an unchanged threshold.
 """
 from __future__ import annotations
@@ -84,7 +88,7 @@ def sparse_softmax_pv(a_sel: np.ndarray, V_sel: np.ndarray):
 
 @dataclass
 class DecodeResult:
-    O: np.ndarray                 # [B, h_q, d] float64
+    O: np.ndarray                 # [B, h_q, d_v] float64
     tau: np.ndarray               # [B, h_q] float64, threshold state after the step
     sel: List[List[np.ndarray]]   # sel[b][j] = sorted kept indices
     logits: List[List[np.ndarray]]  # logits[b][j] = A[b, j, :l_kv[b]]
@@ -98,7 +102,7 @@ def saga_decode_step(q, K, V, l_kv, N: int, refresh_period: int, step: int,
                      keep_logits: bool = True) -> DecodeResult:
     """One SAGA + Atop-N decode step for a batch.
 
-    q [B, h_q, d], K [B, h_k, L_max, d], V [B, h_v, L_max, d], l_kv [B].
+    q [B, h_q, d], K [B, h_k, L_max, d], V [B, h_v, L_max, d_v], l_kv [B].
     `tau_in` [B, h_q] is the threshold carried from the last refresh (ignored at a
     refresh step). Returns the output, the new threshold state and the selections.
     """
@@ -115,7 +119,7 @@ def saga_decode_step(q, K, V, l_kv, N: int, refresh_period: int, step: int,
     if not refresh and tau_in is None:
         raise ValueError("a stale step needs the carried threshold")
 
-    O = np.zeros((B, h_q, d))
+    O = np.zeros((B, h_q, V.shape[3]))
     tau = tau_prev.copy()
     sum_p = np.zeros((B, h_q))
     refreshed = np.zeros((B, h_q), bool)
@@ -173,7 +177,7 @@ def dense_gqa(q, K, V, l_kv, scale: Optional[float] = None) -> np.ndarray:
     B, h_q, d = q.shape
     h_k, h_v = K.shape[1], V.shape[1]
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
-    O = np.zeros((B, h_q, d))
+    O = np.zeros((B, h_q, V.shape[3]))
     for b in range(B):
         L = int(l_kv[b])
         if L == 0:

@@ -27,7 +27,7 @@ FLAG_REFRESHED, FLAG_FORCED = 1, 2
 class SagaShape(ctypes.Structure):
     """Mirror of `saga_shape` in include/saga.h."""
     _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_k", ctypes.c_int32),
-                ("h_v", ctypes.c_int32), ("d", ctypes.c_int32), ("l_max", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d", ctypes.c_int32), ("d_v", ctypes.c_int32), ("l_max", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
@@ -106,7 +106,9 @@ def dtype_code(dt: torch.dtype) -> int:
 
 
 def make_shape(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
-               out_dtype: Optional[torch.dtype] = None, scale: float = 0.0) -> SagaShape:
+               out_dtype: Optional[torch.dtype] = None, scale: float = 0.0, d_v: int = 0) -> SagaShape:
+    """Shape of q [B, h_q, d], k [B, h_k, l_max, d] and v [B, h_v, l_max, d_v]. Without
+    v, `d_v` gives the value head dimension (0: d)."""
     if q.dim() != 3 or k.dim() != 4:
         raise ValueError("q must be [B, h_q, d] and k [B, h_k, l_max, d]")
     B, h_q, d = q.shape
@@ -114,15 +116,20 @@ def make_shape(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = Non
         raise ValueError("k does not match q")
     h_v = k.shape[1]
     if v is not None:
-        if v.dim() != 4 or v.shape[0] != B or v.shape[2] != k.shape[2] or v.shape[3] != d:
-            raise ValueError("v must be [B, h_v, l_max, d] matching k")
+        if v.dim() != 4 or v.shape[0] != B or v.shape[2] != k.shape[2]:
+            raise ValueError("v must be [B, h_v, l_max, d_v] matching k")
         if v.dtype != q.dtype:
             raise ValueError("q, k and v must share one dtype")
         h_v = v.shape[1]
+        d_v = v.shape[3]
     if k.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
-    return SagaShape(B, h_q, k.shape[1], h_v, d, k.shape[2], dtype_code(q.dtype),
+    return SagaShape(B, h_q, k.shape[1], h_v, d, 0 if d_v == d else int(d_v), k.shape[2], dtype_code(q.dtype),
                      dtype_code(out_dtype or q.dtype), float(scale))
+
+
+def value_dim(shape: SagaShape) -> int:
+    return shape.d_v if shape.d_v > 0 else shape.d
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -165,7 +172,9 @@ class Workspace:
         return cls(shape, N, k.shape[2] if max_l_kv is None else max_l_kv, q.device)
 
 
-def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale):
+def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale, d_v=0, need_out=True):
+    """Checks the tensors of a call and returns (shape, max_l_kv, out); without
+    `need_out` the call writes no output and `out` is None."""
     for name, t in (("q", q), ("k", k)):
         _dev(t, name)
     if v is not None:
@@ -173,7 +182,7 @@ def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale):
     _dev(l_kv, "l_kv", torch.int32)
     if out_dtype is None and out is not None:
         out_dtype = out.dtype
-    shape = make_shape(q, k, v, out_dtype, scale)
+    shape = make_shape(q, k, v, out_dtype, scale, d_v)
     if l_kv.numel() != shape.batch:
         raise ValueError("l_kv must have one entry per sequence")
     if tau is not None:
@@ -182,12 +191,15 @@ def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale):
             raise ValueError("tau must be [B, h_q]")
     if max_l_kv is None:
         max_l_kv = shape.l_max
+    out_shape = (shape.batch, shape.h_q, value_dim(shape))
+    if not need_out:
+        return shape, int(max_l_kv), None
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = torch.empty(out_shape, dtype=out_dtype or q.dtype, device=q.device)
     else:
         _dev(out, "out")
-        if tuple(out.shape) != tuple(q.shape) or dtype_code(out.dtype) != shape.out_dtype:
-            raise ValueError("out must be [B, h_q, d] in the output dtype")
+        if tuple(out.shape) != out_shape or dtype_code(out.dtype) != shape.out_dtype:
+            raise ValueError("out must be [B, h_q, d_v] in the output dtype")
     return shape, int(max_l_kv), out
 
 
@@ -218,9 +230,10 @@ def decode_attn(q, k, v, l_kv, tau, *, N: int, refresh_period: int, step: int,
 
 
 def refresh_threshold(q, k, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
-                      workspace: Optional[Workspace] = None, scale: float = 0.0, stream=None):
-    """saga_refresh_threshold: writes the exact threshold into `tau` [B, h_q]."""
-    shape, max_l_kv, _ = _prep(q, k, None, l_kv, tau, q, None, max_l_kv, scale)
+                      workspace: Optional[Workspace] = None, scale: float = 0.0, d_v: int = 0, stream=None):
+    """saga_refresh_threshold: writes the exact threshold into `tau` [B, h_q]. `d_v`:
+    the value head dimension of the caches (0: that of q and k)."""
+    shape, max_l_kv, _ = _prep(q, k, None, l_kv, tau, None, None, max_l_kv, scale, d_v, need_out=False)
     ws = _ws(workspace, shape, N, max_l_kv, q.device)
     st = lib().saga_refresh_threshold(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(l_kv), max_l_kv, int(N),
                                       _ptr(tau), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
@@ -229,9 +242,10 @@ def refresh_threshold(q, k, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None
 
 
 def qk_select(q, k, l_kv, tau, *, max_l_kv: Optional[int] = None, workspace: Optional[Workspace] = None,
-              scale: float = 0.0, stream=None):
-    """saga_qk_select: the scoring and threshold-comparison stage (into the workspace)."""
-    shape, max_l_kv, _ = _prep(q, k, None, l_kv, tau, q, None, max_l_kv, scale)
+              scale: float = 0.0, d_v: int = 0, stream=None):
+    """saga_qk_select: the scoring and threshold-comparison stage (into the workspace).
+    `d_v`: the value head dimension of the caches (0: that of q and k)."""
+    shape, max_l_kv, _ = _prep(q, k, None, l_kv, tau, None, None, max_l_kv, scale, d_v, need_out=False)
     ws = _ws(workspace, shape, 1, max_l_kv, q.device)
     st = lib().saga_qk_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(l_kv), max_l_kv, _ptr(tau),
                               _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
@@ -256,7 +270,7 @@ def select_gather(q, k, v, l_kv, tau, *, max_l_kv: Optional[int] = None, workspa
                   scale: float = 0.0, stream=None):
     """saga_select_gather: scoring, threshold comparison and the per-chunk parts of the
     softmax-weighted value sum (into the workspace)."""
-    shape, max_l_kv, _ = _prep(q, k, v, l_kv, tau, q, None, max_l_kv, scale)
+    shape, max_l_kv, _ = _prep(q, k, v, l_kv, tau, None, None, max_l_kv, scale, need_out=False)
     ws = _ws(workspace, shape, 1, max_l_kv, q.device)
     st = lib().saga_select_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv,
                                   _ptr(tau), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
@@ -290,17 +304,19 @@ def dense_gqa_attn(q, k, v, l_kv, *, max_l_kv: Optional[int] = None, out=None, o
 
 def _prep_paged(q, k_pages, v_pages, table, l_kv, tau, out, out_dtype, max_l_kv, scale):
     """Shape and page descriptor of a paged call: k_pages [num_pages, h_k, P, d],
-    v_pages [num_pages, h_v, P, d], table [B, max_pages] int32."""
+    v_pages [num_pages, h_v, P, d_v], table [B, max_pages] int32."""
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
         _dev(t, name)
     _dev(table, "table", torch.int32)
     _dev(l_kv, "l_kv", torch.int32)
     if q.dim() != 3 or k_pages.dim() != 4 or v_pages.dim() != 4 or table.dim() != 2:
-        raise ValueError("q [B, h_q, d], k_pages/v_pages [num_pages, heads, page_tokens, d], table [B, max_pages]")
+        raise ValueError("q [B, h_q, d], k_pages [num_pages, h_k, page_tokens, d], "
+                         "v_pages [num_pages, h_v, page_tokens, d_v], table [B, max_pages]")
     B, h_q, d = q.shape
     num_pages, h_k, P, dk = k_pages.shape
-    if v_pages.shape[0] != num_pages or v_pages.shape[2] != P or dk != d or v_pages.shape[3] != d:
-        raise ValueError("k_pages and v_pages must share num_pages, page_tokens and d with q")
+    d_v = v_pages.shape[3]
+    if v_pages.shape[0] != num_pages or v_pages.shape[2] != P or dk != d:
+        raise ValueError("k_pages and v_pages must share num_pages and page_tokens, and k_pages d with q")
     if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise ValueError("q, k_pages and v_pages must share one dtype")
     if table.shape[0] != B or l_kv.numel() != B:
@@ -310,19 +326,19 @@ def _prep_paged(q, k_pages, v_pages, table, l_kv, tau, out, out_dtype, max_l_kv,
         max_l_kv = capacity
     if out_dtype is None and out is not None:
         out_dtype = out.dtype
-    shape = SagaShape(B, h_q, h_k, v_pages.shape[1], d, max(int(max_l_kv), 1), dtype_code(q.dtype),
-                      dtype_code(out_dtype or q.dtype), float(scale))
+    shape = SagaShape(B, h_q, h_k, v_pages.shape[1], d, 0 if d_v == d else d_v, max(int(max_l_kv), 1),
+                      dtype_code(q.dtype), dtype_code(out_dtype or q.dtype), float(scale))
     pages = SagaPages(table.data_ptr(), table.shape[1], P, num_pages)
     if tau is not None:
         _dev(tau, "tau", torch.float32)
         if tau.numel() != B * h_q:
             raise ValueError("tau must be [B, h_q]")
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = torch.empty((B, h_q, d_v), dtype=out_dtype or q.dtype, device=q.device)
     else:
         _dev(out, "out")
-        if tuple(out.shape) != tuple(q.shape) or dtype_code(out.dtype) != shape.out_dtype:
-            raise ValueError("out must be [B, h_q, d] in the output dtype")
+        if tuple(out.shape) != (B, h_q, d_v) or dtype_code(out.dtype) != shape.out_dtype:
+            raise ValueError("out must be [B, h_q, d_v] in the output dtype")
     return shape, pages, int(max_l_kv), out
 
 
@@ -390,7 +406,7 @@ def layer_desc(x, k_cache, v_cache, h_q: int, out_dtype=None, scale: float = 0.0
     for t in (x, k_cache, v_cache):
         if t.dtype != torch.bfloat16:
             raise ValueError("the layer computes in bfloat16")
-    shape = SagaShape(B, h_q, h_k, v_cache.shape[1], d, l_max, BF16, dtype_code(out_dtype or torch.bfloat16),
+    shape = SagaShape(B, h_q, h_k, v_cache.shape[1], d, 0, l_max, BF16, dtype_code(out_dtype or torch.bfloat16),
                       float(scale))
     return SagaLayer(shape, x.shape[1])
 

@@ -37,31 +37,59 @@ constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
     }                                  \
   } while (0)
 
-#define SAGA_DISPATCH(DT, DIM, ...)                                   \
+// Runs the statement with T = the element type, DK and DV = the key and value head
+// dimensions as compile-time constants (the built combinations; check_shape refuses
+// the others).
+#define SAGA_DIMS(DKV, DVV, ...)                                      \
   do {                                                                \
-    if ((DT) == SAGA_BF16 && (DIM) == 128) {                          \
-      using T = bf16_t;                                               \
-      constexpr int D = 128;                                          \
+    if ((DKV) == 128 && (DVV) == 128) {                               \
+      constexpr int DK = 128, DV = 128;                               \
       __VA_ARGS__                                                     \
-    } else if ((DT) == SAGA_BF16 && (DIM) == 64) {                    \
-      using T = bf16_t;                                               \
-      constexpr int D = 64;                                           \
+    } else if ((DKV) == 64 && (DVV) == 64) {                          \
+      constexpr int DK = 64, DV = 64;                                 \
       __VA_ARGS__                                                     \
-    } else if ((DT) == SAGA_F32 && (DIM) == 128) {                    \
-      using T = float;                                                \
-      constexpr int D = 128;                                          \
+    } else if ((DKV) == 64 && (DVV) == 128) {                         \
+      constexpr int DK = 64, DV = 128;                                \
       __VA_ARGS__                                                     \
     } else {                                                          \
-      using T = float;                                                \
-      constexpr int D = 64;                                           \
+      constexpr int DK = 32, DV = 64;                                 \
       __VA_ARGS__                                                     \
     }                                                                 \
   } while (0)
 
-// Keys per chunk of the stream kernels at width W (1 or 2).
+// fp32 caches: the same without (64, 128)
+#define SAGA_DIMS_F32(DKV, DVV, ...)                                  \
+  do {                                                                \
+    if ((DKV) == 128 && (DVV) == 128) {                               \
+      constexpr int DK = 128, DV = 128;                               \
+      __VA_ARGS__                                                     \
+    } else if ((DKV) == 64 && (DVV) == 64) {                          \
+      constexpr int DK = 64, DV = 64;                                 \
+      __VA_ARGS__                                                     \
+    } else {                                                          \
+      constexpr int DK = 32, DV = 64;                                 \
+      __VA_ARGS__                                                     \
+    }                                                                 \
+  } while (0)
+
+#define SAGA_DISPATCH(DT, DKV, DVV, ...)                              \
+  do {                                                                \
+    if ((DT) == SAGA_BF16) {                                          \
+      using T = bf16_t;                                               \
+      SAGA_DIMS(DKV, DVV, __VA_ARGS__);                               \
+    } else {                                                          \
+      using T = float;                                                \
+      SAGA_DIMS_F32(DKV, DVV, __VA_ARGS__);                           \
+    }                                                                 \
+  } while (0)
+
+// Value head dimension of a shape (0 in the struct means d).
+int value_dim(const saga_shape* s) { return s->d_v > 0 ? s->d_v : s->d; }
+
+// Keys per chunk of the stream kernels at width W (1 or 2); d is the key head dimension.
 int chunk_keys(int dtype, int d, int W) {
   int ch = 0;
-  SAGA_DISPATCH(dtype, d, ch = W == 2 ? StreamCfg<T, D, 2>::kChunk : StreamCfg<T, D, 1>::kChunk;);
+  SAGA_DISPATCH(dtype, d, d, ch = W == 2 ? StreamCfg<T, DK, 2>::kChunk : StreamCfg<T, DK, 1>::kChunk;);
   return ch;
 }
 
@@ -87,7 +115,14 @@ saga_status check_shape(const saga_shape* s) {
   if (!(s->scale >= 0.f) || !std::isfinite(s->scale)) return SAGA_ERR_SHAPE;
   if ((s->dtype != SAGA_F32 && s->dtype != SAGA_BF16) || (s->out_dtype != SAGA_F32 && s->out_dtype != SAGA_BF16))
     return SAGA_ERR_UNSUPPORTED;
-  if (s->d != 64 && s->d != 128) return SAGA_ERR_UNSUPPORTED;
+  // head dimensions: d_k == d_v in {64, 128}, or the reduced key dimensions
+  // (d_k, d_v) = (64, 128) in bf16 and (32, 64) (section "Training from Scratch":
+  // a key head dimension below the value head dimension)
+  if (s->d_v < 0) return SAGA_ERR_SHAPE;
+  const int dv = value_dim(s);
+  const bool same = s->d == dv && (s->d == 64 || s->d == 128);
+  const bool reduced = (s->d == 32 && dv == 64) || (s->d == 64 && dv == 128 && s->dtype == SAGA_BF16);
+  if (!same && !reduced) return SAGA_ERR_UNSUPPORTED;
   if (s->batch > 65535 || s->h_q > 65535 || s->l_max > kMaxContext) return SAGA_ERR_UNSUPPORTED;
   return SAGA_OK;
 }
@@ -126,7 +161,8 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   w.surv_idx = take(rows * (size_t)w.lpad * 4);
   w.surv_val = take(rows * (size_t)w.lpad * 4);
   w.chunk_hdr = take(rows * (size_t)w.nch * sizeof(ChunkHdr));
-  w.part = take(rows * (size_t)(w.nch > w.nchd ? w.nch : w.nchd) * (s->d + 4) * 4);  // chunk records (sparse: D floats, dense: D+4)
+  // chunk records (sparse: d_v floats, dense: d_v + 4)
+  w.part = take(rows * (size_t)(w.nch > w.nchd ? w.nch : w.nchd) * (value_dim(s) + 4) * 4);
   w.total = off;
   return w;
 }
@@ -141,7 +177,7 @@ int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
   const int g_k = s->h_q / s->h_k;
   const int heads = g_k < 16 ? g_k : 16;
   const int elem = s->dtype == SAGA_BF16 ? 2 : 4;
-  const int pieces = s->d * elem / 16;                 // 16-byte pieces per value row
+  const int pieces = value_dim(s) * elem / 16;         // 16-byte pieces per value row
   const int rows_per_group_load = pieces >= 16 ? 1 : 16 / pieces;
   const long long kept = (long long)w.ch * (N < max_l_kv ? N : max_l_kv) / max_l_kv;
   const long long per_group = 2LL * rows_per_group_load * 4;  // two rounds of 4 loads
@@ -230,8 +266,8 @@ dim3 stream_grid(const saga_shape* s, const Layout& w) {
 }
 
 void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, float* tau, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
-    hipLaunchKernelGGL((k_scores_hist<T, D, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
+    hipLaunchKernelGGL((k_scores_hist<T, DK, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });););
   hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
   hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);
@@ -240,30 +276,30 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
 // Scores and Atop-N comparison; with `gather` also the chunk records of eq. (7).
 void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, bool gather,
                    hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
     dim3 grid = stream_grid(s, w);
     grid.y *= a.hsplit;
     if (!gather)
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, false, P, W>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeys, false, P, W>), grid, dim3(kBlock), 0, st, a);
     else if (from_scores)
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromScores, true, P, W>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromScores, true, P, W>), grid, dim3(kBlock), 0, st, a);
     else if (s->batch == 1)  // one sequence: its chunks reach max_l_kv, key loads need not wait for l_kv
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeysSpeculative, true, P, W>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeysSpeculative, true, P, W>), grid, dim3(kBlock), 0, st, a);
     else
-      hipLaunchKernelGGL((k_qk_select<T, D, kFromKeys, true, P, W>), grid, dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeys, true, P, W>), grid, dim3(kBlock), 0, st, a);
   });););
 }
 
 // Chunk records from the kept lists (only for the separate gather stage).
 void launch_chunk_gather(const saga_shape* s, const Layout& w, const StreamArgs& a, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
-    hipLaunchKernelGGL((k_chunk_gather<T, D, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
+    hipLaunchKernelGGL((k_chunk_gather<T, DK, DV, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });););
 }
 
 void launch_combine(const saga_shape* s, const Layout& w, const GatherArgs& g, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(g.s.ptab != nullptr, SAGA_WIDTH(w.W, {
-    hipLaunchKernelGGL((k_split_combine<T, D, P, W>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(g.s.ptab != nullptr, SAGA_WIDTH(w.W, {
+    hipLaunchKernelGGL((k_split_combine<T, DK, DV, P, W>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
   });););
 }
 
@@ -338,15 +374,15 @@ saga_status dense_impl(const saga_shape* s, const saga_pages* pg, const void* q,
     a.num_pages = pg->num_pages;
   }
   (void)hipGetLastError();
-  SAGA_DISPATCH(s->dtype, s->d, SAGA_PAGED(pg != nullptr, {
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(pg != nullptr, {
     if (max_l_kv > 0) {
       const dim3 grid(w.nchd, s->h_v, s->batch);
-      if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, D, 4, P>), grid, dim3(kBlock), 0, hs, a);
-      else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, D, 8, P>), grid, dim3(kBlock), 0, hs, a);
-      else hipLaunchKernelGGL((k_dense_partial<T, D, 16, P>), grid, dim3(kBlock), 0, hs, a);
+      if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 4, P>), grid, dim3(kBlock), 0, hs, a);
+      else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 8, P>), grid, dim3(kBlock), 0, hs, a);
+      else hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 16, P>), grid, dim3(kBlock), 0, hs, a);
     }
-    hipLaunchKernelGGL((k_dense_combine<D>), dim3(D / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
-                       (int)StreamCfg<T, D>::kChunk);
+    hipLaunchKernelGGL((k_dense_combine<DV>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
+                       (int)StreamCfg<T, DK>::kChunk);
   }););
   return launched();
 }

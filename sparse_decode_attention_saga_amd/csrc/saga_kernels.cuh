@@ -52,16 +52,16 @@ struct StreamArgs {
   // pointers first: the compiler may merge neighbouring field loads into one vector
   // load, and a pointer rebuilt from a merged integer loses its global address space
   // (its loads become flat loads, which the LDS waits of a thread also wait for)
-  const void* q;           // [B, h_q, D]
-  const void* k;           // [B, h_k, l_max, D]
-  const void* v;           // [B, h_v, l_max, D] (gathering kernels)
+  const void* q;           // [B, h_q, DK]
+  const void* k;           // [B, h_k, l_max, DK]
+  const void* v;           // [B, h_v, l_max, DV] (gathering kernels)
   const int32_t* l_kv;     // [B]
   const float* tau;        // [B*h_q] threshold (select kernels)
   float* scores;           // [B*h_q, lpad] fp32 logits (refresh steps and forced refresh)
   int32_t* surv_idx;       // [B*h_q, lpad] kept indices, one CH-segment per chunk
   float* surv_val;         // [B*h_q, lpad] kept logits; also the threshold candidates
   ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
-  float* part;             // [B*h_q, D/16, nch, 16] chunk records: sum w*v, 16 columns per slice
+  float* part;             // [B*h_q, DV/16, nch, 16] chunk records: sum w*v, 16 columns per slice
   unsigned* hist;          // [8, B*h_q, 256] top-digit histogram copies (zero between calls)
   unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
   const int32_t* ptab;     // paged caches: [B, ptab_stride] page ids (the kernels' PAGED form)
@@ -160,7 +160,7 @@ __device__ __forceinline__ void stage_pages(KeptLds<CH>& kl, const StreamArgs& a
 // The block's 16 groups of 16 lanes are spread over the owned heads (16 / owned
 // groups each, taking alternate kept entries); the groups of one head add their sums
 // in LDS. Rows without kept entries in the chunk write nothing. Called by every
-// thread of the block.
+// thread of the block. D is the value head dimension.
 template <typename T, int D, int CH, bool PAGED>
 __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const StreamArgs& a, int b, int j0, int nh,
                                               int c, int hs, int hsplit) {
@@ -286,11 +286,12 @@ enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 // When hsplit > 1, hsplit blocks share each chunk: block hs compares and gathers only
 // the heads h of the tile with h mod hsplit == hs (every block computes all the
 // tile's logits; its duplicate key reads hit the cache).
+// DK and DV are the key and value head dimensions.
 // grid = (nch, h_k * htiles * hsplit, B), block = 256.
-template <typename T, int D, int MODE, bool GATHER, bool PAGED, int W>
+template <typename T, int DK, int DV, int MODE, bool GATHER, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
-  constexpr int TPW = StreamCfg<T, D, W>::kTPW;
-  constexpr int CH = StreamCfg<T, D, W>::kChunk;
+  constexpr int TPW = StreamCfg<T, DK, W>::kTPW;
+  constexpr int CH = StreamCfg<T, DK, W>::kChunk;
   // every argument the key stream needs is read in one batch, before any arithmetic
   // on them (otherwise the pointers' reads may wait behind the index arithmetic)
   const T* const kbase = reinterpret_cast<const T*>(a.k);
@@ -313,11 +314,11 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   const bool live = hh < nh && (hsplit == 1 || hh % hsplit == hs);
 
   floatx4 sc[TPW];
-  QK<T, D> qk;
-  const CacheRows<T, D, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, g, h_k, l_max);
+  QK<T, DK> qk;
+  const CacheRows<T, DK, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, g, h_k, l_max);
   if constexpr (MODE == kFromKeysSpeculative) {
-    qk.load_q(qbase + (size_t)row0 * D, nh, lane);
-    score_tiles<T, D, TPW>(sc, qk, kh, wbase, max_l_kv, lane, scale);
+    qk.load_q(qbase + (size_t)row0 * DK, nh, lane);
+    score_tiles<T, DK, TPW>(sc, qk, kh, wbase, max_l_kv, lane, scale);
   }
   const int L = min(a.l_kv[b], a.max_l_kv);
   if (base >= L) return;
@@ -334,8 +335,8 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) sc[t] = *reinterpret_cast<const floatx4*>(srow + wbase + 16 * t + 4 * kq);
   } else if constexpr (MODE == kFromKeys) {
-    qk.load_q(qbase + (size_t)row0 * D, nh, lane);
-    score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, scale);
+    qk.load_q(qbase + (size_t)row0 * DK, nh, lane);
+    score_tiles<T, DK, TPW>(sc, qk, kh, wbase, L, lane, scale);
   }
   __syncthreads();
 
@@ -377,15 +378,15 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
     *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
   }
-  if constexpr (GATHER) chunk_records<T, D, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit);
+  if constexpr (GATHER) chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit);
 }
 
 // The chunk records of eq. (7) from kept lists already in the workspace (the
 // separately callable gather stage): stages each head's kept entries of the chunk
 // in LDS, then chunk_records. grid = (nch, h_k * htiles, B), block = 256.
-template <typename T, int D, bool PAGED, int W>
+template <typename T, int DK, int DV, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
-  constexpr int CH = StreamCfg<T, D, W>::kChunk;
+  constexpr int CH = StreamCfg<T, DK, W>::kChunk;
   const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
   const int L = min(a.l_kv[b], a.max_l_kv);
   const int base = c * CH;
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
     }
   }
   __syncthreads();
-  chunk_records<T, D, CH, PAGED>(kl, a, b, j0, nh, c, 0, 1);
+  chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, 0, 1);
 }
 
 // ----------------------------------------------------------------------------
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
 // the top 8 bits of their order keys per query head, accumulated into copy
 // (chunk mod kHistCopies) of a.hist: the logits of a row fall into a few bins, and
 // the copies spread the device atomics of the row's blocks over more addresses.
-// grid = (nch, h_k * htiles, B), block = 256.
+// D is the key head dimension. grid = (nch, h_k * htiles, B), block = 256.
 constexpr int kHistCopies = 8;
 
 template <typename T, int D, bool PAGED, int W>
@@ -605,7 +606,7 @@ struct GatherArgs {
   // own pointers before the embedded block (no pointer right after a scalar field:
   // see StreamArgs)
   float* tau;             // [B*h_q] (written only where a row is refreshed)
-  void* out;              // [B*h_q, D]
+  void* out;              // [B*h_q, DV]
   int32_t* sel_count;     // [B*h_q] or null
   int32_t* sel_idx;       // [B*h_q, sel_cap] or null
   int32_t* flags;         // [B*h_q] or null
@@ -665,12 +666,12 @@ __device__ __forceinline__ void reduce_rows(float* acc, float z, float (*s_red)[
 // N-th largest as a new threshold (a forced refresh), then the kept set, its maximum
 // and the sparse softmax-PV. Used for a stale threshold that keeps nothing (the
 // forced refresh). Writes out, tau (refresh only), sel_count, sel_idx and flags.
-template <typename T, int D, int NT, bool PAGED>
-__device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh_tau, float (*s_red)[D],
+template <typename T, int DK, int DV, int NT, bool PAGED>
+__device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh_tau, float (*s_red)[DV],
                           float* s_z) {
   constexpr int NW = NT / kWave;
-  constexpr int TPW = StreamCfg<T, D>::kTPW;
-  using RG = RowGather<T, D, NT>;
+  constexpr int TPW = StreamCfg<T, DK>::kTPW;
+  using RG = RowGather<T, DV, NT>;
   const StreamArgs& s = a.s;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const long long row = (long long)b * s.h_q + j;
@@ -682,15 +683,15 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
   const int jj = j - j0;
 
   {
-    QK<T, D> qk;
-    qk.load_q(reinterpret_cast<const T*>(s.q) + (size_t)(b * s.h_q + j0) * D, nh, lane);
-    const auto kh = key_rows<T, D, PAGED>(s, b, g);
+    QK<T, DK> qk;
+    qk.load_q(reinterpret_cast<const T*>(s.q) + (size_t)(b * s.h_q + j0) * DK, nh, lane);
+    const auto kh = key_rows<T, DK, PAGED>(s, b, g);
     const int kq = lane >> 4;
     for (int base = 0; base < L; base += NW * 16 * TPW) {
       const int wbase = base + wv * 16 * TPW;
       if (wbase < L) {
         floatx4 sc[TPW];
-        score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, s.scale);
+        score_tiles<T, DK, TPW>(sc, qk, kh, wbase, L, lane, s.scale);
         if ((lane & 15) == jj) {
 #pragma unroll
           for (int t = 0; t < TPW; ++t)
@@ -729,7 +730,7 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
 
   const int vh = j / s.g_v;
   const int grp = tid / RG::G, gl = tid - grp * RG::G;
-  const auto vr = value_rows<T, D, PAGED>(s, b, vh);
+  const auto vr = value_rows<T, DV, PAGED>(s, b, vh);
   float acc[RG::EPL];
 #pragma unroll
   for (int e = 0; e < RG::EPL; ++e) acc[e] = 0.f;
@@ -762,8 +763,8 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
     kept += n;
     __syncthreads();
   }
-  reduce_rows<T, D, NT>(acc, z, s_red, s_z);
-  for (int d = tid; d < D; d += NT) store_out<D>(a, row, d, kept > 0 ? s_red[0][d] / s_z[0] : 0.f);
+  reduce_rows<T, DV, NT>(acc, z, s_red, s_z);
+  for (int d = tid; d < DV; d += NT) store_out<DV>(a, row, d, kept > 0 ? s_red[0][d] / s_z[0] : 0.f);
   if (tid == 0) {
     if (refresh_tau) a.tau[row] = tau;
     if (a.sel_count) a.sel_count[row] = kept;
@@ -783,13 +784,14 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
 // and whether or not a chunk kept anything; values of chunks past l_kv or without
 // kept entries are never used. The kept indices are exported in the same pass
 // (chunk c by block c mod gridDim.x). A row that kept nothing is recomputed exactly
-// by block 0 (forced refresh). grid = (D / 16, h_q, B), block = 256.
+// by block 0 (forced refresh). DK and DV are the key and value head dimensions.
+// grid = (DV / 16, h_q, B), block = 256.
 constexpr int kCombRegs = 8;  // chunk slots per thread read speculatively
 
-template <typename T, int D, bool PAGED, int W>
+template <typename T, int DK, int DV, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
-  constexpr int CH = StreamCfg<T, D, W>::kChunk;
-  constexpr int CB = D / 16;
+  constexpr int CH = StreamCfg<T, DK, W>::kChunk;
+  constexpr int CB = DV / 16;
   constexpr int kSlots = kBlock / 4;  // chunks per pass of the block
   const StreamArgs& sa = a.s;
   const int cb = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -801,7 +803,7 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   __shared__ int s_itmp[kWaves];
   __shared__ float s_ftmp[kWaves];
   __shared__ float s_acc[kWaves][4][17];
-  __shared__ float s_red[kWaves][D];
+  __shared__ float s_red[kWaves][DV];
   __shared__ float s_z[kWaves];
 
   const ChunkHdr* hdr = sa.chunk_hdr + row * sa.nch;
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   }
   const int L = min(sa.l_kv[b], sa.max_l_kv);
   if (L <= 0) {
-    if (tid < 16) store_out<D>(a, row, col + tid, 0.f);
+    if (tid < 16) store_out<DV>(a, row, col + tid, 0.f);
     if (cb == 0 && tid == 0) {
       if (a.sel_count) a.sel_count[row] = 0;
       if (a.flags) a.flags[row] = 0;
@@ -849,7 +851,7 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
   int total;
   int pos = block_max_excl_scan(m, qd == 0 ? tsum : 0, s_ftmp, s_itmp, M, total);
   if (total == 0) {
-    if (cb == 0) exact_row<T, D, kBlock, PAGED>(a, b, j, L, true, s_red, s_z);
+    if (cb == 0) exact_row<T, DK, DV, kBlock, PAGED>(a, b, j, L, true, s_red, s_z);
     return;
   }
 
@@ -908,7 +910,7 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
         oo += s_acc[w][r][tid];
         zz += s_acc[w][r][16];
       }
-    store_out<D>(a, row, col + tid, oo / zz);
+    store_out<DV>(a, row, col + tid, oo / zz);
   }
   if (cb == 0 && tid == 0) {
     if (a.sel_count) a.sel_count[row] = total;
@@ -924,7 +926,7 @@ struct DenseArgs {
   const void* k;
   const void* v;
   const int32_t* l_kv;
-  float* part;     // [B*h_q, nchd, D+4] per-chunk (m, Z, -, -, o[D])
+  float* part;     // [B*h_q, nchd, DV+4] per-chunk (m, Z, -, -, o[DV])
   void* out;
   const int32_t* ptab;  // paged caches: [B, ptab_stride] page ids
   int h_q, h_k, h_v, g, l_max, nchd, out_bf16;  // g = h_q / h_v query heads per value head
@@ -933,18 +935,19 @@ struct DenseArgs {
   int ptab_stride, page_shift, num_pages;     // paged caches (see StreamArgs)
 };
 
+// DK and DV are the key and value head dimensions.
 // grid = (nchd, h_v, B), block = 256. Each block takes one chunk of CHD keys and one
 // value head v: the logits of its g query heads against their key head (h_k divides
 // h_v, so the g heads share one; MFMA), the chunk's softmax numerator relative to the
 // chunk maximum, and its product with the chunk's rows of value head v (VALU). The
 // value and key loads of the chunk are all issued before the first MFMA.
-template <typename T, int D, int GH, bool PAGED>
+template <typename T, int DK, int DV, int GH, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
-  constexpr int TPW = StreamCfg<T, D>::kTPW;
-  constexpr int CHD = StreamCfg<T, D>::kChunk;
+  constexpr int TPW = StreamCfg<T, DK>::kTPW;
+  constexpr int CHD = StreamCfg<T, DK>::kChunk;
   constexpr int EPL = Unpack<T>::kN;
-  constexpr int G = D / EPL;                         // lanes per value row
-  constexpr int VL = (16 * D) / (EPL * kWave);       // 16-byte value loads per lane per tile
+  constexpr int G = DV / EPL;                        // lanes per value row
+  constexpr int VL = (16 * DV) / (EPL * kWave);      // 16-byte value loads per lane per tile
   const T* const kbase = reinterpret_cast<const T*>(a.k);
   const T* const vbase = reinterpret_cast<const T*>(a.v);
   const T* const qbase = reinterpret_cast<const T*>(a.q);
@@ -962,10 +965,10 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
 
   __shared__ float s_p[kWaves][TPW][16][GH];
   __shared__ float s_m[kWaves][GH], s_z[kWaves][GH];
-  __shared__ float s_o[kWaves][GH][D];
+  __shared__ float s_o[kWaves][GH][DV];
 
-  const CacheRows<T, D, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, kg, h_k, l_max);
-  const CacheRows<T, D, PAGED> vh(vbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vg, h_v, l_max);
+  const CacheRows<T, DK, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, kg, h_k, l_max);
+  const CacheRows<T, DV, PAGED> vh(vbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vg, h_v, l_max);
   const int wbase = base + wv * 16 * TPW;
 
   // value tiles: load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
@@ -979,18 +982,18 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
       const int e = r * kWave + lane;
       if constexpr (PAGED) {
         const int key = min(t0 + e / G, L - 1);
-        vb[t][r] = ld16(vt + (size_t)(key - t0) * D + (e % G) * EPL);
+        vb[t][r] = ld16(vt + (size_t)(key - t0) * DV + (e % G) * EPL);
       } else {
         const int key = min(wbase + 16 * t + e / G, L - 1);
-        vb[t][r] = ld16(vt + (size_t)key * D + (e % G) * EPL);
+        vb[t][r] = ld16(vt + (size_t)key * DV + (e % G) * EPL);
       }
     }
   }
 
-  QK<T, D> qk;
-  qk.load_q(qbase + (size_t)row0 * D, gq, lane);
+  QK<T, DK> qk;
+  qk.load_q(qbase + (size_t)row0 * DK, gq, lane);
   floatx4 sc[TPW];
-  score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, scale);
+  score_tiles<T, DK, TPW>(sc, qk, kh, wbase, L, lane, scale);
 
   float mh = -INFINITY;
 #pragma unroll
@@ -1052,8 +1055,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   __syncthreads();
 
   // merge the 4 waves (each relative to its own maximum) and write the chunk partial
-  for (int idx = tid; idx < gq * (D + 1); idx += kBlock) {
-    const int h = idx / (D + 1), d = idx - h * (D + 1);
+  for (int idx = tid; idx < gq * (DV + 1); idx += kBlock) {
+    const int h = idx / (DV + 1), d = idx - h * (DV + 1);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
@@ -1062,10 +1065,10 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     for (int w = 0; w < kWaves; ++w) {
       const float mw = s_m[w][h];
       const float sw = (mw == -INFINITY) ? 0.f : expf(mw - M);
-      acc += sw * (d < D ? s_o[w][h][d] : s_z[w][h]);
+      acc += sw * (d < DV ? s_o[w][h][d] : s_z[w][h]);
     }
-    float* pp = a.part + ((long long)(row0 + h) * a.nchd + c) * (D + 4);
-    if (d < D) pp[4 + d] = acc;
+    float* pp = a.part + ((long long)(row0 + h) * a.nchd + c) * (DV + 4);
+    if (d < DV) pp[4 + d] = acc;
     else {
       pp[0] = M;
       pp[1] = acc;
@@ -1074,8 +1077,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
 }
 
 // Log-sum-exp merge of the chunk partials of each row (b, j). Thread t takes chunks
-// t, t+256, ... and 16 columns (four 16-byte loads per chunk).
-// grid = (D / 16, h_q, B), block = 256.
+// t, t+256, ... and 16 columns (four 16-byte loads per chunk). D is the value head
+// dimension. grid = (D / 16, h_q, B), block = 256.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_dense_combine(const DenseArgs a, int chd) {
   const int cg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;

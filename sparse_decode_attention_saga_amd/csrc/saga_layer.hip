@@ -144,7 +144,7 @@ saga_status check_layer(const saga_layer* L, int32_t N, int32_t max_l_kv, size_t
   const saga_shape s = attn_shape(L);
   const size_t n = saga_workspace_bytes(&s, N, max_l_kv);
   if (n == 0) return SAGA_ERR_SHAPE;
-  if (s.dtype != SAGA_BF16) return SAGA_ERR_UNSUPPORTED;
+  if (s.dtype != SAGA_BF16 || (s.d_v != 0 && s.d_v != s.d)) return SAGA_ERR_UNSUPPORTED;
   if (!linear_dims_ok(s.batch, L->d_model, (long long)(s.h_q + s.h_k + s.h_v) * s.d) ||
       !linear_dims_ok(s.batch, (long long)s.h_q * s.d, L->d_model))
     return L->d_model % 32 != 0 || L->d_model < 32 ? SAGA_ERR_SHAPE : SAGA_ERR_UNSUPPORTED;

@@ -7,7 +7,7 @@ fed from it without sharing any of the method.
 Layout (the pages fix none; this is the library's):
   q  [B, h_q, d]            one query row per sequence and query head
   K  [B, h_k, L_max, d]     key cache, token rows d-contiguous
-  V  [B, h_v, L_max, d]     value cache, token rows d-contiguous
+  V  [B, h_v, L_max, d_v]   value cache, token rows d_v-contiguous (d_v = d unless set)
   l_kv [B] int32            valid cache length per sequence (rows >= l_kv[b] are zero)
 
 Recipe (stands in for the model workloads of "More Value per Key: Asymmetric
@@ -58,6 +58,11 @@ class Workload:
     run_len: int = 1
     l_kv_min: Optional[int] = None  # set => per-sequence l_kv ~ U{l_kv_min..l_kv}
     dense_h_kv: Optional[int] = None  # head count of the dense GQA baseline
+    d_v: Optional[int] = None      # value head dimension when it differs from d
+
+    @property
+    def dv(self) -> int:
+        return self.d if self.d_v is None else self.d_v
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -85,11 +90,19 @@ RAGGED_B8 = Workload("ragged-b8-l16k-128k", 4, batch=8, h_q=32, h_k=2, h_v=8, d=
 SWEEP = Workload("qwen2.5-1.5b-shape-sweep", 5, batch=1, h_q=12, h_k=1, h_v=4, d=128,
                  l_kv=4096, N=512, refresh_period=8, dtype="bf16", plant_frac=0.005,
                  dense_h_kv=2)
+# Key heads of half the dimension, twice as many (the same key bytes per token as
+# the Llama- and Qwen-shaped workloads above): the reduced key head dimension that
+# the pages compare with fewer key heads (section "Training from Scratch").
+SIGMA_LLAMA_32K = Workload("llama3.2-1b-shape-sigma-keys-l32k", 7, batch=1, h_q=32, h_k=4, h_v=8, d=32,
+                           d_v=64, l_kv=32768, N=256, refresh_period=16, dtype="bf16", plant_frac=0.005)
+SIGMA_QWEN_128K = Workload("qwen2.5-1.5b-shape-sigma-keys-l128k", 8, batch=1, h_q=12, h_k=2, h_v=4, d=64,
+                           d_v=128, l_kv=131072, N=512, refresh_period=32, dtype="bf16", plant_frac=0.005)
 SWEEP_L = (4096, 16384, 65536, 131072)
 SWEEP_N = (128, 512, 2048)
 SWEEP_PERIOD = (1, 8, 64)
 
-WORKLOADS = {w.name: w for w in (TINY, LLAMA_32K, QWEN_128K, QWEN_128K_B16, RAGGED_B8, SWEEP)}
+WORKLOADS = {w.name: w for w in (TINY, LLAMA_32K, QWEN_128K, QWEN_128K_B16, RAGGED_B8, SWEEP,
+                                 SIGMA_LLAMA_32K, SIGMA_QWEN_128K)}
 
 
 def streams(workload_id: int, seed: int) -> list:
@@ -144,18 +157,18 @@ def generate(w: Workload, seed: int = 0, l_max: Optional[int] = None,
     if int(lens.max()) > L_max:
         raise ValueError("l_max is smaller than a sequence length")
     frac = w.plant_frac if plant_frac is None else plant_frac
-    B, h_q, h_k, h_v, d = w.batch, w.h_q, w.h_k, w.h_v, w.d
+    B, h_q, h_k, h_v, d, dv = w.batch, w.h_q, w.h_k, w.h_v, w.d, w.dv
     g_k = h_q // h_k
 
     q = rs[S_Q].standard_normal((B, h_q, d), dtype=np.float32)
     K = np.zeros((B, h_k, L_max, d), dtype=np.float32)
-    V = np.zeros((B, h_v, L_max, d), dtype=np.float32)
+    V = np.zeros((B, h_v, L_max, dv), dtype=np.float32)
     for b in range(B):
         L = int(lens[b])
         for g in range(h_k):
             K[b, g, :L] = rs[S_K].standard_normal((L, d), dtype=np.float32)
         for h in range(h_v):
-            V[b, h, :L] = rs[S_V].standard_normal((L, d), dtype=np.float32)
+            V[b, h, :L] = rs[S_V].standard_normal((L, dv), dtype=np.float32)
 
     qhat = q / np.linalg.norm(q, axis=-1, keepdims=True)
     for b in range(B):
@@ -200,7 +213,7 @@ class PagedKV:
 
 def paginate(k: torch.Tensor, v: torch.Tensor, l_kv: np.ndarray, page_tokens: int, seed: int = 0,
              spare: int = 3, stale: int = -1) -> PagedKV:
-    """Scatter contiguous caches k [B, h_k, L_max, d], v [B, h_v, L_max, d] into pages."""
+    """Scatter contiguous caches k [B, h_k, L_max, d], v [B, h_v, L_max, d_v] into pages."""
     B, h_k, L_max, d = k.shape
     P = int(page_tokens)
     max_pages = max(1, -(-L_max // P))
@@ -209,7 +222,7 @@ def paginate(k: torch.Tensor, v: torch.Tensor, l_kv: np.ndarray, page_tokens: in
     order = rng.permutation(num_pages).astype(np.int32)
     table = order[:B * max_pages].reshape(B, max_pages).copy()
     kp = torch.zeros((num_pages, h_k, P, d), dtype=k.dtype)
-    vp = torch.zeros((num_pages, v.shape[1], P, d), dtype=v.dtype)
+    vp = torch.zeros((num_pages, v.shape[1], P, v.shape[3]), dtype=v.dtype)
     for b in range(B):
         for p in range(max_pages):
             lo, hi = p * P, min((p + 1) * P, L_max)
@@ -288,7 +301,7 @@ class DecodeStream:
             if L + rows > self.k.shape[2]:
                 raise ValueError("cache capacity exceeded")
             kn = self._append.standard_normal((w.h_k, rows, w.d), dtype=np.float32)
-            vn = self._append.standard_normal((w.h_v, rows, w.d), dtype=np.float32)
+            vn = self._append.standard_normal((w.h_v, rows, w.dv), dtype=np.float32)
             self.k[b, :, L:L + rows] = to_dtype(kn, w.torch_dtype)
             self.v[b, :, L:L + rows] = to_dtype(vn, w.torch_dtype)
             self.l_kv[b] = L + rows

@@ -38,12 +38,13 @@ class GpuCase:
         self.q, self.k, self.v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
         self.l_kv = torch.from_numpy(np.asarray(x.l_kv, np.int32)).to(dev)
         B, h_q, d = x.q.shape
-        self.B, self.h_q, self.d = B, h_q, d
+        d_v = x.v.shape[3]
+        self.B, self.h_q, self.d, self.d_v = B, h_q, d, d_v
         self.max_l_kv = int(x.k.shape[2] if max_l_kv is None else max_l_kv)
         self.N = N
         self.cap = max(1, int(sel_cap or min(self.max_l_kv, max(4 * N, 64))))
         self.tau = torch.zeros(B, h_q, dtype=torch.float32, device=dev)
-        self.out = torch.empty(B, h_q, d, dtype=out_dtype, device=dev)
+        self.out = torch.empty(B, h_q, d_v, dtype=out_dtype, device=dev)
         self.sel_count = torch.zeros(B, h_q, dtype=torch.int32, device=dev)
         self.sel_idx = torch.full((B, h_q, self.cap), -1, dtype=torch.int32, device=dev)
         self.flags = torch.full((B, h_q), -1, dtype=torch.int32, device=dev)

@@ -40,10 +40,10 @@ class PagedCase:
         self.kp, self.vp, self.table = pk.k_pages.to(DEV), pk.v_pages.to(DEV), pk.table.to(DEV)
         self.q = x.q.to(DEV)
         self.l_kv = torch.from_numpy(np.asarray(x.l_kv, np.int32)).to(DEV)
-        B, h_q, d = x.q.shape
+        B, h_q, _ = x.q.shape
         self.N, self.max_l_kv, self.cap = N, max_l_kv, sel_cap
         self.tau = torch.zeros(B, h_q, dtype=torch.float32, device=DEV)
-        self.out = torch.empty(B, h_q, d, dtype=torch.float32, device=DEV)
+        self.out = torch.empty(B, h_q, x.v.shape[3], dtype=torch.float32, device=DEV)
         self.sel_count = torch.zeros(B, h_q, dtype=torch.int32, device=DEV)
         self.sel_idx = torch.full((B, h_q, sel_cap), -1, dtype=torch.int32, device=DEV)
         self.flags = torch.full((B, h_q), -1, dtype=torch.int32, device=DEV)

@@ -41,7 +41,8 @@ def test_status_strings(lib):
 
 
 def shape(**kw):
-    d = dict(batch=1, h_q=12, h_k=1, h_v=4, d=128, l_max=131072, dtype=api.BF16, out_dtype=api.BF16, scale=0.0)
+    d = dict(batch=1, h_q=12, h_k=1, h_v=4, d=128, d_v=0, l_max=131072, dtype=api.BF16, out_dtype=api.BF16,
+             scale=0.0)
     d.update(kw)
     return api.SagaShape(**d)
 
@@ -57,6 +58,19 @@ def test_workspace_bytes(lib):
     assert lib.saga_workspace_bytes(ctypes.byref(s), 0, 1024) == 0
     assert lib.saga_workspace_bytes(ctypes.byref(s), 8, 131073) == 0
     assert lib.saga_workspace_bytes(None, 8, 16) == 0
+
+
+def test_head_dimension_pairs(lib):
+    """Built (d, d_v): equal dimensions 64 and 128, and the reduced key dimensions
+    (32, 64) and, for bf16, (64, 128); d_v = 0 means d_v = d."""
+    def ok(**kw):
+        return lib.saga_workspace_bytes(ctypes.byref(shape(**kw)), 64, 4096) > 0
+    assert ok(d=128, d_v=0) and ok(d=128, d_v=128) and ok(d=64, d_v=0)
+    assert ok(d=32, d_v=64) and ok(d=32, d_v=64, dtype=api.F32, out_dtype=api.F32)
+    assert ok(d=64, d_v=128) and not ok(d=64, d_v=128, dtype=api.F32, out_dtype=api.F32)
+    assert not ok(d=32, d_v=0) and not ok(d=128, d_v=64) and not ok(d=64, d_v=-1) and not ok(d=32, d_v=128)
+    small = lib.saga_workspace_bytes(ctypes.byref(shape(d=64, d_v=64)), 64, 4096)
+    assert lib.saga_workspace_bytes(ctypes.byref(shape(d=64, d_v=128)), 64, 4096) > small
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks

@@ -20,11 +20,11 @@ from sparse_decode_attention_saga_amd import bytemodel
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def rand_case(seed, B=2, h_q=8, h_k=2, h_v=4, d=16, L_max=40, lens=(40, 23)):
+def rand_case(seed, B=2, h_q=8, h_k=2, h_v=4, d=16, L_max=40, lens=(40, 23), d_v=None):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, h_q, d))
     K = rng.standard_normal((B, h_k, L_max, d))
-    V = rng.standard_normal((B, h_v, L_max, d))
+    V = rng.standard_normal((B, h_v, L_max, d if d_v is None else d_v))
     return q, K, V, np.array(lens[:B])
 
 
@@ -98,6 +98,35 @@ def test_dense_saga_full_attention(h_k, h_v):
         L = int(lens[b])
         ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], Kx[b, :, :L], Vx[b, :, :L])[:, 0]
         np.testing.assert_allclose(O[b], ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("d,d_v", [(8, 16), (16, 32), (32, 8)])
+def test_value_dim_differs_from_key_dim(d, d_v):
+    # a key head dimension below (or above) the value head dimension: torch's
+    # attention takes value rows of their own width and scales by 1/sqrt(d) of q, k
+    q, K, V, lens = rand_case(40 + d, h_q=8, h_k=2, h_v=4, d=d, d_v=d_v)
+    dense = orc.dense_gqa(q, K, V, lens)
+    full = orc.saga_decode_step(q, K, V, lens, N=10 ** 6, refresh_period=1, step=0)
+    Kx = torch.from_numpy(K).repeat_interleave(4, dim=1)
+    Vx = torch.from_numpy(V).repeat_interleave(2, dim=1)
+    for b in range(q.shape[0]):
+        L = int(lens[b])
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], Kx[b, :, :L], Vx[b, :, :L])[:, 0]
+        np.testing.assert_allclose(dense[b], ref.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(full.O[b], ref.numpy(), rtol=0, atol=1e-12)
+    # and the top-N selection is that of the logits alone: with N = 3 the masked
+    # library attention over each row's three best keys
+    top = orc.saga_decode_step(q, K, V, lens, N=3, refresh_period=1, step=0)
+    for b in range(q.shape[0]):
+        L = int(lens[b])
+        for j in range(8):
+            want, _ = brute_topn(q[b, j], K[b, j // 4, :L], 3)
+            assert top.sel[b][j].tolist() == want
+            mask = np.zeros(L, bool)
+            mask[want] = True
+            ref = sdpa_row(q[b, j], K[b, j // 4, :L], V[b, j // 2, :L], mask)
+            assert top.O[b, j].shape == (d_v,)
+            np.testing.assert_allclose(top.O[b, j], ref, rtol=0, atol=1e-12)
 
 
 # --- refresh step = exact top-N (eq. 6-7) ---------------------------------------
