@@ -332,6 +332,78 @@ def sweep(torch, args) -> int:
     return 0
 
 
+def merge_bench(torch, args) -> int:
+    """The GQA-to-SAGA key-head merge (closed-form initialisation) at the Llama 3.2-1B
+    shape: D = 2048, h_q = 32, 8 teacher key heads of d = 64 merged into 4, on T
+    calibration tokens of random hidden states with random-init projections. Times the
+    device part (saga_merge_losses: projections, Grams, per-pair closed form and
+    losses; saga_merge_keys) with HIP events, the host matching, and the CPU oracle
+    on the same inputs at the smaller T."""
+    from sparse_decode_attention_saga_amd import api
+    from sparse_decode_attention_saga_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    api.lib()
+    D, h_q, h_k, d = 2048, 32, 8, 64
+    res = {}
+    for T in args.merge_tokens:
+        inp = wl.merge_inputs(T, D, h_q, h_k, d, seed=0)
+        x, wq, wk = inp.x.to(dev), inp.w_q.to(dev), inp.w_k.to(dev)
+        loss, ws = api.merge_losses(x, wq, wk, h_q=h_q, h_k=h_k)
+        partner, total = api.min_weight_pairing(loss.cpu())
+        out = api.merge_keys(x, wq, wk, partner, h_q=h_q, h_k=h_k, workspace=ws)
+        torch.cuda.synchronize()
+        t_loss, t_keys, t_host = [], [], []
+        for _ in range(max(args.reps, 3)):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            torch.cuda.synchronize()
+            e0.record()
+            api.merge_losses(x, wq, wk, h_q=h_q, h_k=h_k, workspace=ws)
+            e1.record()
+            api.merge_keys(x, wq, wk, partner, h_q=h_q, h_k=h_k, workspace=ws, out=out)
+            e2.record()
+            torch.cuda.synchronize()
+            t_loss.append(1e3 * e0.elapsed_time(e1))
+            t_keys.append(1e3 * e1.elapsed_time(e2))
+            h0 = time.perf_counter()
+            api.min_weight_pairing(loss.cpu())
+            t_host.append(1e6 * (time.perf_counter() - h0))
+        n_cols = (h_q + h_k) * d
+        flops = 2.0 * T * D * n_cols + 2.0 * (h_k * d * d * (h_q // h_k) * T + (h_k * d) ** 2 * T)
+        r = {"us_merge_losses": pct(t_loss, 50), "us_merge_keys": pct(t_keys, 50),
+             "us_host_pairing_incl_copy": pct(t_host, 50),
+             "projection_and_gram_flop": flops,
+             "pairs": sorted((a, b) for a, b in enumerate(partner) if a < b), "total_loss": total}
+        log(f"merge T={T}: losses {r['us_merge_losses']:.1f} us, keys {r['us_merge_keys']:.1f} us, "
+            f"host pairing {r['us_host_pairing_incl_copy']:.1f} us")
+        if not args.no_cpu_baseline and T == min(args.merge_tokens):
+            from threadpoolctl import threadpool_info
+            from oracle import convert_oracle as cv
+            X = inp.x.double().numpy()
+            W_Q, W_K = inp.w_q.double().numpy().T, inp.w_k.double().numpy().T
+            t0 = time.perf_counter()
+            n = 0
+            while True:
+                cv.convert(X, W_Q, W_K, h_q, h_k, d)
+                n += 1
+                if time.perf_counter() - t0 >= args.cpu_seconds:
+                    break
+            el = time.perf_counter() - t0
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            r["cpu_baseline"] = {"value": n / el, "unit": "conversions/s", "cores": int(threads), "kind": "oracle",
+                                 "sample": f"{n} full oracle conversions (all 28 pair losses by eq. (13), "
+                                           f"merges, matching) of this T={T} input, {el:.1f} s"}
+            r["gpu_conversions_per_s"] = 1e6 / (r["us_merge_losses"] + r["us_merge_keys"] +
+                                                r["us_host_pairing_incl_copy"])
+        res[str(T)] = r
+    print(json.dumps({"metric": "GQA-to-SAGA key-head merge time (closed-form initialisation)",
+                      "unit": "us", "config": {"workload": "llama3.2-1b-shape key-head merge", "d_model": D,
+                                               "h_q": h_q, "h_k_teacher": h_k, "h_k_student": h_k // 2, "d": d,
+                                               "inputs": "bf16 random hidden states and projections"},
+                      "by_tokens": res}), flush=True)
+    return 0
+
+
 def decompose(torch, args) -> int:
     """Where the SAGA + Atop-N gain comes from, at the Qwen2.5-1.5B-shaped 128K layer:
     the same library's dense attention and Atop-N step, each with grouped-query heads
@@ -543,6 +615,10 @@ def main() -> int:
                     help="print per-kernel averages of rocprofv3 csv files and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="SAGA vs dense step time over l_kv x N x refresh period (one JSON line)")
+    ap.add_argument("--merge", action="store_true",
+                    help="GQA-to-SAGA key-head merge at the Llama 3.2-1B shape (one JSON line)")
+    ap.add_argument("--merge-tokens", type=int, nargs="+", default=[512, 4096],
+                    help="calibration token counts of --merge")
     ap.add_argument("--decompose", action="store_true",
                     help="dense and Atop-N steps with grouped-query and with SAGA heads (one JSON line)")
     args = ap.parse_args()
@@ -567,6 +643,8 @@ def main() -> int:
         return sweep(torch, args)
     if args.decompose:
         return decompose(torch, args)
+    if args.merge:
+        return merge_bench(torch, args)
 
     from sparse_decode_attention_saga_amd import api
     from sparse_decode_attention_saga_amd import bytemodel

@@ -256,6 +256,56 @@ saga_status saga_decode_layer(const saga_layer* L, int32_t attention, const void
                               int64_t step, float* tau, void* y, int32_t* sel_count, int32_t* flags,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------
+ * GQA-to-SAGA key-head merge, the closed-form initialisation of a SAGA student from
+ * a grouped-query teacher (summary page, section "GQA-to-SAGA Conversion > Stage 1:
+ * Closed-Form Initialization"). Teacher key heads are merged in pairs: h_k teacher
+ * heads become h_k / 2 student heads, and the query heads of both heads of a pair
+ * read the merged head.
+ *   eq. (13): L_ab(M) = sum over the query heads j of head a of
+ *             ||Q^j (X M)^T - Q^j (X W_K^a)^T||_F^2, plus the same over head b;
+ *   Lemma 4.1, eq. (15): the minimiser M_ab = (W_K^a S_a + W_K^b S_b)(S_a + S_b)^+,
+ *             S_r = sum over the query heads j of head r of Q^j^T Q^j, Q^j = X W_Q^j;
+ *   Theorem 4.2, eq. (14): the pairing is the minimum-weight perfect matching of
+ *             the complete graph on the teacher heads with weights L_ab(M_ab).
+ * Query head j belongs to teacher key head floor(j * h_k / h_q). The pseudo-inverse
+ * treats eigenvalues of S_a + S_b below 1e-5 times the largest as zero. Layouts
+ * (row-major, bf16 inputs): x [tokens, d_model] calibration hidden states;
+ * w_q [h_q*d, d_model] and w_k [h_k*d, d_model], the transposed projections (row
+ * f holds output feature f, head-major, as w_qkv of the decode layer).
+ * ------------------------------------------------------------------------------ */
+typedef struct saga_merge_shape {
+  int32_t tokens;    /* calibration tokens T >= 1 (rows of x) */
+  int32_t d_model;   /* hidden size D: a multiple of 32 */
+  int32_t h_q;       /* query heads: a multiple of h_k */
+  int32_t h_k;       /* teacher key heads: even, 2..16 */
+  int32_t d;         /* head dimension: 64 or 128 */
+} saga_merge_shape;
+
+/* Workspace bytes of the merge calls (no zero fill needed); 0 if the shape is invalid. */
+size_t saga_merge_workspace_bytes(const saga_merge_shape* s);
+
+/* Eq. (13) at eq. (15) for every pair of teacher key heads: loss [h_k, h_k] float32
+ * (device), symmetric, zero diagonal. Leaves the coefficients of every pair's merged
+ * projection in the workspace for saga_merge_keys. */
+saga_status saga_merge_losses(const saga_merge_shape* s, const void* x, const void* w_q, const void* w_k,
+                              float* loss, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Theorem 4.2 on the host: the exact minimum-weight perfect matching of n (even,
+ * 2..16) vertices, weights w [n, n] (host, row-major; the diagonal is ignored, the
+ * rest must be finite). partner [n] (host) receives each vertex's partner; total
+ * (host, may be NULL) the matching's weight. Ties go to the matching found first
+ * when every vertex is paired with the lowest free one in increasing partner order.
+ * Pure host code: no device work. */
+saga_status saga_min_weight_pairing(int32_t n, const float* w, int32_t* partner, double* total);
+
+/* Eq. (15) for the pairs of `partner` (host [h_k], partner[partner[a]] == a):
+ * w_out [h_k/2 * d, d_model] float32 (device), merged head i = the i-th pair in
+ * increasing order of its lower head, row i*d + c = column c of its M. Needs the
+ * workspace of a saga_merge_losses call on the same inputs, earlier on `stream`. */
+saga_status saga_merge_keys(const saga_merge_shape* s, const void* w_k, const int32_t* partner, float* w_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

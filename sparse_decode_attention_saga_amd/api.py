@@ -19,7 +19,8 @@ F32, BF16 = 0, 1
 EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "saga_decode_attn",
            "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather",
            "saga_select_gather", "saga_split_combine", "saga_decode_attn_paged", "saga_dense_gqa_attn_paged",
-           "saga_linear", "saga_qkv_append", "saga_layer_workspace_bytes", "saga_decode_layer")
+           "saga_linear", "saga_qkv_append", "saga_layer_workspace_bytes", "saga_decode_layer",
+           "saga_merge_workspace_bytes", "saga_merge_losses", "saga_min_weight_pairing", "saga_merge_keys")
 ATTN_ATOPN, ATTN_DENSE = 0, 1
 FLAG_REFRESHED, FLAG_FORCED = 1, 2
 
@@ -40,6 +41,12 @@ class SagaPages(ctypes.Structure):
 class SagaLayer(ctypes.Structure):
     """Mirror of `saga_layer` in include/saga.h."""
     _fields_ = [("attn", SagaShape), ("d_model", ctypes.c_int32)]
+
+
+class SagaMergeShape(ctypes.Structure):
+    """Mirror of `saga_merge_shape` in include/saga.h."""
+    _fields_ = [("tokens", ctypes.c_int32), ("d_model", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("h_k", ctypes.c_int32), ("d", ctypes.c_int32)]
 
 
 class SagaError(RuntimeError):
@@ -70,6 +77,10 @@ _SIGS = {
     "saga_layer_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "saga_decode_layer": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P,
                                  _SZ, _P]),
+    "saga_merge_workspace_bytes": (_SZ, [_P]),
+    "saga_merge_losses": (_I32, [_P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "saga_min_weight_pairing": (_I32, [_I32, _P, _P, _P]),
+    "saga_merge_keys": (_I32, [_P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -476,3 +487,87 @@ def decode_layer(x, w_qkv, w_o, k_cache, v_cache, l_kv, l_kv_next, *, h_q: int, 
                                  _ptr(flags), _ptr(ws.buf), ws.nbytes, _stream(x.device, stream))
     _check(st, "saga_decode_layer")
     return out
+
+
+# --- GQA-to-SAGA key-head merge (closed-form initialisation) ------------------------
+
+class MergeWorkspace:
+    """Device workspace of the merge calls (no zero fill needed)."""
+
+    def __init__(self, shape: SagaMergeShape, device):
+        n = lib().saga_merge_workspace_bytes(ctypes.byref(shape))
+        if n == 0:
+            raise ValueError("invalid merge shape")
+        self.nbytes = int(n)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+
+def merge_shape(x, w_q, w_k, h_q: int, h_k: int) -> SagaMergeShape:
+    """Shape of x [T, D], w_q [h_q d, D], w_k [h_k d, D] (bfloat16, transposed projections)."""
+    if x.dim() != 2 or w_q.dim() != 2 or w_k.dim() != 2:
+        raise ValueError("x [tokens, d_model], w_q [h_q*d, d_model], w_k [h_k*d, d_model]")
+    T, D = x.shape
+    if w_q.shape[1] != D or w_k.shape[1] != D or w_q.shape[0] % h_q or w_k.shape[0] % h_k:
+        raise ValueError("w_q and w_k must be [heads*d, d_model] matching x")
+    d = w_q.shape[0] // h_q
+    if w_k.shape[0] != h_k * d:
+        raise ValueError("w_q and w_k must share the head dimension")
+    return SagaMergeShape(T, D, h_q, h_k, d)
+
+
+def merge_losses(x, w_q, w_k, *, h_q: int, h_k: int, workspace: Optional[MergeWorkspace] = None, stream=None):
+    """saga_merge_losses: eq. (13) at eq. (15) for every pair of teacher key heads.
+    Returns (loss [h_k, h_k] float32 on the device, the workspace holding the pairs'
+    merge coefficients)."""
+    for name, t in (("x", x), ("w_q", w_q), ("w_k", w_k)):
+        _dev(t, name, torch.bfloat16)
+    shape = merge_shape(x, w_q, w_k, h_q, h_k)
+    ws = workspace or MergeWorkspace(shape, x.device)
+    loss = torch.empty(h_k, h_k, dtype=torch.float32, device=x.device)
+    st = lib().saga_merge_losses(ctypes.byref(shape), _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(loss), _ptr(ws.buf),
+                                 ws.nbytes, _stream(x.device, stream))
+    _check(st, "saga_merge_losses")
+    return loss, ws
+
+
+def min_weight_pairing(weight):
+    """saga_min_weight_pairing (host): weight [n, n] (CPU float32 tensor or array-like).
+    Returns (partner list, total weight)."""
+    w = torch.as_tensor(weight, dtype=torch.float32).contiguous()
+    if w.is_cuda or w.dim() != 2 or w.shape[0] != w.shape[1]:
+        raise ValueError("weight must be a square host matrix")
+    n = w.shape[0]
+    partner = (ctypes.c_int32 * n)()
+    total = ctypes.c_double(0.0)
+    st = lib().saga_min_weight_pairing(n, ctypes.c_void_p(w.data_ptr()), partner, ctypes.byref(total))
+    _check(st, "saga_min_weight_pairing")
+    return list(partner), float(total.value)
+
+
+def merge_keys(x, w_q, w_k, partner, *, h_q: int, h_k: int, workspace: MergeWorkspace, out=None, stream=None):
+    """saga_merge_keys: merged key projections [h_k/2 * d, D] float32 for the pairing
+    `partner` (host list), using the coefficients saga_merge_losses left in `workspace`."""
+    _dev(w_k, "w_k", torch.bfloat16)
+    shape = merge_shape(x, w_q, w_k, h_q, h_k)
+    if len(partner) != h_k:
+        raise ValueError("one partner per teacher key head")
+    part = (ctypes.c_int32 * h_k)(*[int(p) for p in partner])
+    if out is None:
+        out = torch.empty(h_k // 2 * shape.d, shape.d_model, dtype=torch.float32, device=w_k.device)
+    else:
+        _dev(out, "out", torch.float32)
+    st = lib().saga_merge_keys(ctypes.byref(shape), _ptr(w_k), part, _ptr(out), _ptr(workspace.buf),
+                               workspace.nbytes, _stream(w_k.device, stream))
+    _check(st, "saga_merge_keys")
+    return out
+
+
+def merge_key_heads(x, w_q, w_k, *, h_q: int, h_k: int):
+    """The whole closed-form initialisation: pair losses on the device, the pairing on
+    the host (the loss matrix is copied back), the merged projections on the device.
+    Returns (pairs [(a, b), ...], total loss, merged w_k [h_k/2 * d, D] float32, loss)."""
+    loss, ws = merge_losses(x, w_q, w_k, h_q=h_q, h_k=h_k)
+    partner, total = min_weight_pairing(loss.cpu())
+    out = merge_keys(x, w_q, w_k, partner, h_q=h_q, h_k=h_k, workspace=ws)
+    pairs = sorted((a, b) for a, b in enumerate(partner) if a < b)
+    return pairs, total, out, loss

@@ -10,7 +10,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libsaga.so")
-SOURCES = [os.path.join(HERE, "csrc", "saga_api.hip"), os.path.join(HERE, "csrc", "saga_layer.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("saga_api.hip", "saga_layer.hip", "saga_merge.hip")]
 # the decode-attention kernels' sources (what a build of those kernels depends on;
 # the layer's projection kernels are not among them)
 LIB_FILES = [os.path.join(HERE, "csrc", n) for n in ("saga_api.hip", "saga_device.cuh", "saga_kernels.cuh")] + \

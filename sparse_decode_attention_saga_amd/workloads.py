@@ -313,3 +313,32 @@ class DecodeStream:
 
     def inputs(self) -> Inputs:
         return Inputs(self.q, self.k, self.v, self.l_kv.copy())
+
+
+@dataclass
+class MergeInputs:
+    """Calibration hidden states and a teacher's projections for the key-head merge,
+    as CPU bfloat16 tensors in the library's layout (projections transposed: row f
+    holds output feature f, head-major)."""
+
+    x: torch.Tensor     # [T, D]
+    w_q: torch.Tensor   # [h_q * d, D]
+    w_k: torch.Tensor   # [h_k * d, D]
+
+
+def merge_inputs(tokens: int, d_model: int, h_q: int, h_k: int, d: int, seed: int = 0,
+                 twins: Sequence[tuple] = (), twin_noise: float = 0.05) -> MergeInputs:
+    """x ~ N(0, 1); weight entries ~ N(0, 1/D) (random-init weights at the model's
+    shape); all rounded to bfloat16. `twins` lists key-head pairs (a, b) whose
+    projections are made close: head b = head a + twin_noise * N(0, 1/D) (a planted
+    pairing)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x3E5E, seed])))
+    x = rng.standard_normal((tokens, d_model), dtype=np.float32)
+    s = np.float32(1.0 / np.sqrt(d_model))
+    w_q = rng.standard_normal((h_q * d, d_model), dtype=np.float32) * s
+    w_k = rng.standard_normal((h_k * d, d_model), dtype=np.float32) * s
+    for a, b in twins:
+        w_k[b * d:(b + 1) * d] = w_k[a * d:(a + 1) * d] + np.float32(twin_noise) * s * \
+            rng.standard_normal((d, d_model), dtype=np.float32)
+    bf = torch.bfloat16
+    return MergeInputs(to_dtype(x, bf), to_dtype(w_q, bf), to_dtype(w_k, bf))

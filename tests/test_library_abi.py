@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sparse_decode_attention_saga_amd import api
@@ -214,3 +215,52 @@ def test_binding_requires_gpu_tensors(lib):
     k = torch.zeros(1, 1, 16, 64)
     with pytest.raises(ValueError):
         api.decode_attn(q, k, k, torch.zeros(1, dtype=torch.int32), torch.zeros(1, 4), N=4, refresh_period=1, step=0)
+
+
+def merge_shape(**kw):
+    d = dict(tokens=4096, d_model=2048, h_q=32, h_k=8, d=64)
+    d.update(kw)
+    return api.SagaMergeShape(**d)
+
+
+def test_merge_workspace_bytes(lib):
+    s = merge_shape()
+    n = lib.saga_merge_workspace_bytes(ctypes.byref(s))
+    # at least the fp32 queries and keys of every calibration token
+    assert n >= 4096 * (32 + 8) * 64 * 4
+    assert lib.saga_merge_workspace_bytes(ctypes.byref(merge_shape(h_k=7, h_q=28))) == 0   # odd head count
+    assert lib.saga_merge_workspace_bytes(ctypes.byref(merge_shape(h_k=18, h_q=36))) == 0  # more than 16 heads
+    assert lib.saga_merge_workspace_bytes(ctypes.byref(merge_shape(d=96))) == 0
+    assert lib.saga_merge_workspace_bytes(ctypes.byref(merge_shape(d_model=100))) == 0
+    assert lib.saga_merge_workspace_bytes(ctypes.byref(merge_shape(h_q=30))) == 0         # h_k must divide h_q
+    assert lib.saga_merge_workspace_bytes(ctypes.byref(merge_shape(d=128, h_k=2, h_q=12, d_model=1536))) > 0
+    assert lib.saga_merge_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("n,seed", [(2, 0), (4, 1), (6, 2), (8, 3), (8, 4), (10, 5)])
+def test_host_pairing_equals_oracle_matching(lib, n, seed):
+    # Theorem 4.2's matching in the library's host code against the oracle's
+    # enumeration of every perfect matching (no device work is involved)
+    from oracle import convert_oracle as cv
+    rng = np.random.default_rng(seed)
+    w = rng.random((n, n)).astype(np.float32)
+    w = w + w.T
+    partner, total = api.min_weight_pairing(w)
+    pairs, best = cv.min_weight_perfect_matching(w.astype(np.float64))
+    assert sorted((a, b) for a, b in enumerate(partner) if a < b) == pairs
+    assert abs(total - best) <= 1e-6 * best
+    for a in range(n):
+        assert partner[partner[a]] == a and partner[a] != a
+
+
+def test_host_pairing_rejects_bad_input(lib):
+    w = np.ones((4, 4), np.float32)
+    part = (ctypes.c_int32 * 4)()
+    assert lib.saga_min_weight_pairing(3, w.ctypes.data, part, None) == api.ERR_SHAPE
+    assert lib.saga_min_weight_pairing(18, w.ctypes.data, part, None) == api.ERR_SHAPE
+    assert lib.saga_min_weight_pairing(4, None, part, None) == api.ERR_NULL
+    w[1, 2] = np.nan
+    assert lib.saga_min_weight_pairing(4, w.ctypes.data, part, None) == api.ERR_SHAPE
+    w[1, 2] = 1.0
+    w[3, 3] = np.nan          # the diagonal is ignored
+    assert lib.saga_min_weight_pairing(4, w.ctypes.data, part, None) == api.OK
