@@ -940,7 +940,7 @@ struct DenseArgs {
 // value head v: the logits of its g query heads against their key head (h_k divides
 // h_v, so the g heads share one; MFMA), the chunk's softmax numerator relative to the
 // chunk maximum, and its product with the chunk's rows of value head v (VALU). The
-// value and key loads of the chunk are all issued before the first MFMA.
+// key tiles are loaded first; the value tiles follow in two halves (see below).
 template <typename T, int DK, int DV, int GH, bool PAGED>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   constexpr int TPW = StreamCfg<T, DK>::kTPW;
@@ -971,29 +971,40 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   const CacheRows<T, DV, PAGED> vh(vbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vg, h_v, l_max);
   const int wbase = base + wv * 16 * TPW;
 
-  // value tiles: load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
-  uint4 vb[TPW][VL];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int t0 = min(wbase + 16 * t, (L - 1) & ~15);  // a clamped tile lies inside one page
-    const T* vt = PAGED ? vh.tile(t0) : vh.row(0);
-#pragma unroll
-    for (int r = 0; r < VL; ++r) {
-      const int e = r * kWave + lane;
-      if constexpr (PAGED) {
-        const int key = min(t0 + e / G, L - 1);
-        vb[t][r] = ld16(vt + (size_t)(key - t0) * DV + (e % G) * EPL);
-      } else {
-        const int key = min(wbase + 16 * t + e / G, L - 1);
-        vb[t][r] = ld16(vt + (size_t)key * DV + (e % G) * EPL);
-      }
-    }
-  }
-
   QK<T, DK> qk;
   qk.load_q(qbase + (size_t)row0 * DK, gq, lane);
   floatx4 sc[TPW];
   score_tiles<T, DK, TPW>(sc, qk, kh, wbase, L, lane, scale);
+  // The value tiles are loaded once the key tiles are consumed, in two halves: the
+  // first half before the softmax, the second after the first half's products, so
+  // that key tiles, value tiles and the accumulators never all hold registers at
+  // once and four blocks fit on a compute unit. Load latency is covered by the
+  // softmax and by the other resident blocks.
+  constexpr int VH = TPW >= 2 ? 2 : 1;  // value-tile halves
+  constexpr int TPH = TPW / VH;         // tiles per half
+  // load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
+  auto load_values = [&](uint4 (&vb)[TPH][VL], int t_first) {
+#pragma unroll
+    for (int tt = 0; tt < TPH; ++tt) {
+      const int t = t_first + tt;
+      const int t0 = min(wbase + 16 * t, (L - 1) & ~15);  // a clamped tile lies inside one page
+      const T* vt = PAGED ? vh.tile(t0) : vh.row(0);
+#pragma unroll
+      for (int r = 0; r < VL; ++r) {
+        const int e = r * kWave + lane;
+        if constexpr (PAGED) {
+          const int key = min(t0 + e / G, L - 1);
+          vb[tt][r] = ld16(vt + (size_t)(key - t0) * DV + (e % G) * EPL);
+        } else {
+          const int key = min(wbase + 16 * t + e / G, L - 1);
+          vb[tt][r] = ld16(vt + (size_t)key * DV + (e % G) * EPL);
+        }
+      }
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 vb[TPH][VL];
+  load_values(vb, 0);
 
   float mh = -INFINITY;
 #pragma unroll
@@ -1027,20 +1038,28 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int r = 0; r < VL; ++r) {
-      const int e = r * kWave + lane;
-      const int k16 = e / G;
-      float x[EPL];
-      Unpack<T>::run(vb[t][r], x);
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        const float p = s_p[wv][t][k16][h];
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) o[h][q] += p * x[q];
-      }
+  for (int hv = 0; hv < VH; ++hv) {
+    if (hv > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_values(vb, hv * TPH);
     }
+#pragma unroll
+    for (int tt = 0; tt < TPH; ++tt)
+#pragma unroll
+      for (int r = 0; r < VL; ++r) {
+        const int t = hv * TPH + tt;
+        const int e = r * kWave + lane;
+        const int k16 = e / G;
+        float x[EPL];
+        Unpack<T>::run(vb[tt][r], x);
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+          const float p = s_p[wv][t][k16][h];
+#pragma unroll
+          for (int q = 0; q < EPL; ++q) o[h][q] += p * x[q];
+        }
+      }
+  }
   // lanes with the same column group (lane % G) hold partial sums over different keys
 #pragma unroll
   for (int h = 0; h < GH; ++h)
