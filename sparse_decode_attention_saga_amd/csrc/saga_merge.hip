@@ -42,7 +42,7 @@ constexpr double kPinvRcond = 1e-5;      // eigenvalues below rcond * largest co
 constexpr int kJacobiSweeps = 16;        // upper bound; sweeps stop once converged
 constexpr int kGramChunk = 256;          // calibration tokens per partial Gram
 constexpr int kGramTile = 64;            // output tile of one wave in k_gram
-constexpr int kPairScratch = 10;         // d x d fp64 matrices of scratch per pair
+constexpr int kPairScratch = 16;         // d x d fp64 matrices of scratch per pair
 
 // --- workspace layout ------------------------------------------------------------
 
@@ -76,7 +76,7 @@ MergeLayout merge_layout(const saga_merge_shape* s) {
   m.part = take((size_t)m.items * kGramTile * kGramTile * 4);
   m.s = take((size_t)hk * d * d * 4);
   m.h = take((size_t)hk * d * hk * d * 4);
-  // per pair, fp64: V^T, P, A, B, S_a, S_b (d x d), Z^T, (Hab Z)^T (d x 2d)
+  // per pair, fp64: V^T, P, A, B, S_a, S_b (d x d), Z, Z^T, Hab Z (2 d^2 each), Hab (4 d^2)
   m.pair_f64 = take((size_t)m.pairs * (kPairScratch * (size_t)d * d) * 8);
   m.coef = take((size_t)hk * hk * 2 * d * d * 4);  // (A, B) of pair (a, b) at [a][b], fp32
   m.total = off;
@@ -293,48 +293,76 @@ __device__ double block_sum_f64(double v, double* red) {
   return t;
 }
 
-// One pair (a, b), a < b, per block of 256 threads. S_a + S_b (symmetrised, fp64) is
-// diagonalised in LDS by cyclic Jacobi rotations: each round rotates d/2 disjoint
-// index pairs (a round-robin schedule visits every pair once per sweep of d - 1
-// rounds) with the angle that zeroes their off-diagonal entry; eigenvectors
-// accumulate as the rows of V^T. Then P = V diag(1/lambda, 0 below the cut) V^T,
-// A = S_a P, B = S_b P, and L_ab = <Z_a^T Hab Z_a, S_a> + <Z_b^T Hab Z_b, S_b>.
+// C[M x N] = X[M x K] Y[K x N] in fp64, all row-major in global memory, by every
+// thread of the block: 64 x 64 output tiles, each thread a 4 x 4 register tile, K
+// staged through LDS in slices of 16 (`lds`: 64 * 17 + 16 * 64 doubles). M and N
+// are multiples of 64, K of 16.
+constexpr int kGemmLds = 64 * 17 + 16 * 64;
+
+__device__ void block_gemm_f64(double* C, int ldc, const double* X, int ldx, const double* Y, int ldy, int M, int N,
+                               int K, double* lds) {
+  double* xs = lds;            // [64][17]
+  double* ys = lds + 64 * 17;  // [16][64]
+  const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+  for (int mt = 0; mt < M; mt += 64)
+    for (int nt = 0; nt < N; nt += 64) {
+      double acc[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+      for (int k0 = 0; k0 < K; k0 += 16) {
+        double xv[4], yv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = u * kBlock + tid;
+          xv[u] = X[(size_t)(mt + e / 16) * ldx + k0 + e % 16];
+          yv[u] = Y[(size_t)(k0 + e / 64) * ldy + nt + e % 64];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = u * kBlock + tid;
+          xs[(e / 16) * 17 + e % 16] = xv[u];
+          ys[e] = yv[u];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < 16; ++kk) {
+          double xr[4], yr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xr[i] = xs[(tr * 4 + i) * 17 + kk];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yr[j] = ys[kk * 64 + tc * 4 + j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] += xr[i] * yr[j];
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) C[(size_t)(mt + tr * 4 + i) * ldc + nt + tc * 4 + j] = acc[i][j];
+    }
+  __syncthreads();
+}
+
+// Pseudo-inverse of S_a + S_b by its eigendecomposition, with the cut: the sum
+// (symmetrised, fp64) is diagonalised in LDS by cyclic Jacobi rotations. Each round
+// rotates d/2 disjoint index pairs (a round-robin schedule visits every pair once
+// per sweep of d - 1 rounds) with the angle that zeroes their off-diagonal entry;
+// eigenvectors accumulate as the rows of V^T. Then P = V diag(lambda+) V^T. Called by
+// every thread of the block; s_* are the kernel's LDS arrays.
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_pair(const PairArgs a) {
+__device__ void jacobi_pinv(double* s_m, double* vt, int* s_p, int* s_q, double* s_c, double* s_s, double* s_red,
+                            double* s_linv, const double* Ssa, const double* Ssb, double* P) {
   constexpr int HALF = D / 2;
-  constexpr bool kVtLds = D <= 64;         // V^T in LDS too (d = 128: in the scratch)
-  __shared__ double s_m[D * D];
-  __shared__ double s_vt[kVtLds ? D * D : 1];
-  __shared__ int s_p[HALF], s_q[HALF];     // this round's index pairs (p < q)
-  __shared__ double s_c[HALF], s_s[HALF];  // and their rotations
-  __shared__ double s_red[kWaves];
-  __shared__ double s_linv[D];             // 1 / eigenvalue, 0 below the cut
-
-  // pair index -> (a, b) with a < b
-  int pa = 0, rem = blockIdx.x;
-  while (rem >= a.h_k - 1 - pa) {
-    rem -= a.h_k - 1 - pa;
-    ++pa;
-  }
-  const int pb = pa + 1 + rem;
   const int tid = threadIdx.x;
-  const float* Sa = a.S + (size_t)pa * D * D;
-  const float* Sb = a.S + (size_t)pb * D * D;
-  double* const vt_g = a.scratch + (size_t)blockIdx.x * kPairScratch * D * D;
-  double* const vt = kVtLds ? s_vt : vt_g;                    // V^T [D][D]
-  double* const P = vt_g + D * D;
-  double* const Am = P + D * D;
-  double* const Bm = Am + D * D;
-  double* const Ssa = Bm + D * D;    // S_a, S_b symmetrised
-  double* const Ssb = Ssa + D * D;
-  double* const Zt = Ssb + D * D;    // Z^T [D][2D]
-  double* const HZt = Zt + 2 * D * D;  // (Hab Z)^T [D][2D]
-
+  __syncthreads();
   for (int e = tid; e < D * D; e += kBlock) {
     const int i = e / D, k = e - (e / D) * D;
-    const double x = (double)Sa[i * D + k] + (double)Sb[i * D + k];
-    const double y = (double)Sa[k * D + i] + (double)Sb[k * D + i];
-    s_m[e] = 0.5 * (x + y);
+    s_m[e] = Ssa[e] + Ssb[e];
     vt[e] = i == k ? 1.0 : 0.0;
   }
   __syncthreads();
@@ -415,11 +443,6 @@ __global__ __launch_bounds__(kBlock) void k_pair(const PairArgs a) {
     const double l = s_m[tid * D + tid];
     s_linv[tid] = l > kPinvRcond * lmax ? 1.0 / l : 0.0;
   }
-  for (int e = tid; e < D * D; e += kBlock) {
-    const int i = e / D, k = e - (e / D) * D;
-    Ssa[e] = 0.5 * ((double)Sa[i * D + k] + (double)Sa[k * D + i]);
-    Ssb[e] = 0.5 * ((double)Sb[i * D + k] + (double)Sb[k * D + i]);
-  }
   __syncthreads();
   for (int e = tid; e < D * D; e += kBlock) {
     const int m = e / D, n = e - (e / D) * D;
@@ -428,62 +451,135 @@ __global__ __launch_bounds__(kBlock) void k_pair(const PairArgs a) {
     for (int i = 0; i < D; ++i) sum += vt[i * D + m] * vt[i * D + n] * s_linv[i];
     P[e] = sum;
   }
-  __syncthreads();
-  // A = S_a P, B = S_b P (P and the S are symmetric: both operands read along rows)
+}
+
+// One pair (a, b), a < b, per block of 256 threads: P = (S_a + S_b)^+ (the inverse
+// when it is certified to equal the pseudo-inverse with the cut, else jacobi_pinv),
+// A = S_a P, B = S_b P, and L_ab = <Z_a^T Hab Z_a, S_a> + <Z_b^T Hab Z_b, S_b>.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_pair(const PairArgs a) {
+  constexpr int HALF = D / 2;
+  constexpr bool kVtLds = D <= 64;         // V^T in LDS too (d = 128: in the scratch)
+  __shared__ double s_m[D * D];
+  __shared__ double s_vt[kVtLds ? D * D : 1];
+  __shared__ int s_p[HALF], s_q[HALF];     // this round's index pairs (p < q)
+  __shared__ double s_c[HALF], s_s[HALF];  // and their rotations
+  __shared__ double s_red[kWaves];
+  __shared__ double s_linv[D];             // 1 / eigenvalue, 0 below the cut
+  __shared__ double s_gemm[kGemmLds];
+
+  // pair index -> (a, b) with a < b
+  int pa = 0, rem = blockIdx.x;
+  while (rem >= a.h_k - 1 - pa) {
+    rem -= a.h_k - 1 - pa;
+    ++pa;
+  }
+  const int pb = pa + 1 + rem;
+  const int tid = threadIdx.x;
+  const float* Sa = a.S + (size_t)pa * D * D;
+  const float* Sb = a.S + (size_t)pb * D * D;
+  double* const vt_g = a.scratch + (size_t)blockIdx.x * kPairScratch * D * D;
+  double* const vt = kVtLds ? s_vt : vt_g;                    // V^T [D][D]
+  double* const P = vt_g + D * D;
+  double* const Am = P + D * D;
+  double* const Bm = Am + D * D;
+  double* const Ssa = Bm + D * D;    // S_a, S_b symmetrised
+  double* const Ssb = Ssa + D * D;
+  double* const Z = Ssb + D * D;       // [2D][D]
+  double* const Zt = Z + 2 * D * D;    // Z^T [D][2D]
+  double* const HZ = Zt + 2 * D * D;   // Hab Z [2D][D]
+  double* const Hab = HZ + 2 * D * D;  // [2D][2D]
+
   for (int e = tid; e < D * D; e += kBlock) {
-    const int m = e / D, n = e - (e / D) * D;
-    double sa = 0.0, sb = 0.0;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-      const double pk = P[n * D + k];
-      sa += Ssa[m * D + k] * pk;
-      sb += Ssb[m * D + k] * pk;
-    }
-    Am[e] = sa;
-    Bm[e] = sb;
+    const int i = e / D, k = e - (e / D) * D;
+    const double sa = 0.5 * ((double)Sa[i * D + k] + (double)Sa[k * D + i]);
+    const double sb = 0.5 * ((double)Sb[i * D + k] + (double)Sb[k * D + i]);
+    Ssa[e] = sa;
+    Ssb[e] = sb;
+    s_m[e] = sa + sb;
   }
   __syncthreads();
+
+  // Fast path: S_a + S_b inverted in place by Gauss-Jordan elimination (no pivoting
+  // is needed for a positive definite matrix: every pivot is a positive Schur
+  // complement diagonal). The inverse is the pseudo-inverse with the cut whenever no
+  // eigenvalue lies below rcond times the largest, which ||S||_F ||S^-1||_F <
+  // 1 / rcond guarantees (the Frobenius norms bound lambda_max and 1 / lambda_min
+  // from above). Otherwise (a singular or badly conditioned sum, or a non-positive
+  // pivot) the eigendecomposition below applies the cut.
+  double fro_s = 0.0;
+  for (int e = tid; e < D * D; e += kBlock) fro_s += s_m[e] * s_m[e];
+  fro_s = block_sum_f64(fro_s, s_red);
+  bool inverted = true;
+  for (int k = 0; k < D; ++k) {
+    const double piv = s_m[k * D + k];  // the same value in every thread
+    if (!(piv > 0.0)) {
+      inverted = false;
+      break;
+    }
+    const double rp = 1.0 / piv;
+    constexpr int PER = D * D / kBlock;
+    double nv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = u * kBlock + tid;
+      const int i = e / D, j = e - (e / D) * D;
+      const double aij = s_m[e], aik = s_m[i * D + k], akj = s_m[k * D + j];
+      nv[u] = i == k ? (j == k ? rp : akj * rp) : (j == k ? -aik * rp : aij - aik * akj * rp);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) s_m[u * kBlock + tid] = nv[u];
+    __syncthreads();
+  }
+  double fro_p = 0.0;
+  if (inverted) {
+    for (int e = tid; e < D * D; e += kBlock) fro_p += s_m[e] * s_m[e];
+    fro_p = block_sum_f64(fro_p, s_red);
+  }
+  const bool certified = inverted && sqrt(fro_s) * sqrt(fro_p) < 1.0 / kPinvRcond;
+  if (certified) {
+    for (int e = tid; e < D * D; e += kBlock) {
+      const int i = e / D, k = e - (e / D) * D;
+      P[e] = 0.5 * (s_m[e] + s_m[k * D + i]);
+    }
+  } else {
+    jacobi_pinv<D>(s_m, vt, s_p, s_q, s_c, s_s, s_red, s_linv, Ssa, Ssb, P);
+  }
+  __syncthreads();
+  // A = S_a P, B = S_b P
+  block_gemm_f64(Am, D, Ssa, D, P, D, D, D, D, s_gemm);
+  block_gemm_f64(Bm, D, Ssb, D, P, D, D, D, D, s_gemm);
   float* ca = a.coef + ((size_t)(pa * a.h_k + pb) * 2) * D * D;
   for (int e = tid; e < D * D; e += kBlock) {
     ca[e] = (float)Am[e];
     ca[D * D + e] = (float)Bm[e];
   }
-
-  // L = sum over the two heads r of <Z_r^T Hab Z_r, S_r>, Hab = H's blocks (a, b);
-  // Z and Hab Z are kept transposed so that every inner product reads along rows
+  // Hab: the rows and columns of H for heads a and b, in fp64
   const int hd = a.h_k * D;
+  for (int e = tid; e < 4 * D * D; e += kBlock) {
+    const int k = e / (2 * D), t = e - (e / (2 * D)) * (2 * D);
+    Hab[e] = (double)a.H[(size_t)((k < D ? pa : pb) * D + k % D) * hd + (t < D ? pa : pb) * D + t % D];
+  }
+
+  // L = sum over the two heads r of <Z_r^T Hab Z_r, S_r>, Z_a = [A - I; B],
+  // Z_b = [A; B - I]
   double total = 0.0;
   for (int side = 0; side < 2; ++side) {
     for (int e = tid; e < 2 * D * D; e += kBlock) {
-      const int n = e / (2 * D), k = e - (e / (2 * D)) * (2 * D);  // Z^T[n][k] = Z[k][n]
+      const int k = e / D, n = e - (e / D) * D;
       const double id = (side == 0 ? k == n : k - D == n) ? 1.0 : 0.0;
-      Zt[e] = (k < D ? Am[k * D + n] : Bm[(k - D) * D + n]) - id;
+      const double z = (k < D ? Am[k * D + n] : Bm[(k - D) * D + n]) - id;
+      Z[e] = z;
+      Zt[(size_t)n * 2 * D + k] = z;
     }
     __syncthreads();
-    // (Hab Z)^T[n][k] = sum_t Hab[k][t] Z[t][n]; Hab row k = H row (head of k) over
-    // the columns of heads a and b
-    for (int e = tid; e < 2 * D * D; e += kBlock) {
-      const int n = e / (2 * D), k = e - (e / (2 * D)) * (2 * D);
-      const float* hrow = a.H + (size_t)((k < D ? pa : pb) * D + (k % D)) * hd;
-      const double* zc = Zt + (size_t)n * 2 * D;
-      double sum = 0.0;
-#pragma unroll 8
-      for (int t = 0; t < D; ++t) sum += (double)hrow[pa * D + t] * zc[t];
-#pragma unroll 8
-      for (int t = 0; t < D; ++t) sum += (double)hrow[pb * D + t] * zc[D + t];
-      HZt[e] = sum;
-    }
-    __syncthreads();
-    // G = Z^T (Hab Z), then <G, S_r>
+    block_gemm_f64(HZ, D, Hab, 2 * D, Z, D, 2 * D, D, 2 * D, s_gemm);
+    double* const G = P;  // P is no longer needed once A and B are formed
+    block_gemm_f64(G, D, Zt, 2 * D, HZ, D, D, D, 2 * D, s_gemm);
     const double* Sr = side == 0 ? Ssa : Ssb;
     double part = 0.0;
-    for (int e = tid; e < D * D; e += kBlock) {
-      const int m = e / D, n = e - (e / D) * D;
-      double sum = 0.0;
-#pragma unroll 8
-      for (int t = 0; t < 2 * D; ++t) sum += Zt[m * 2 * D + t] * HZt[n * 2 * D + t];
-      part += sum * Sr[n * D + m];
-    }
+    for (int e = tid; e < D * D; e += kBlock) part += G[e] * Sr[e];  // S_r is symmetric
     total += block_sum_f64(part, s_red);
     __syncthreads();
   }
