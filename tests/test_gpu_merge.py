@@ -117,3 +117,20 @@ def test_rank_deficient_gram():
     S = sum(cv.gram_of_queries(X, W_Q, cv.query_heads_of(r, 4, 2), 64) for r in range(2))
     assert np.linalg.matrix_rank(S) == 48
     check_merge(12, 256, 4, 2, 64, seed=30)
+
+
+def test_merge_twelve_heads():
+    # 66 pairs, 10395 pairings
+    check_merge(256, 512, 24, 12, 64, seed=40)
+
+
+def test_merge_one_token():
+    # one calibration token: each S_r has rank at most h_q / h_k, the sum of two at
+    # most 4 < d, so every pair takes the eigendecomposition path with the cut
+    check_merge(1, 256, 8, 4, 64, seed=41)
+
+
+def test_merge_d128_four_heads_planted():
+    twins = [(0, 3), (1, 2)]
+    pairs, ref = check_merge(300, 768, 8, 4, 128, seed=42, twins=twins)
+    assert pairs == sorted(twins)

@@ -264,3 +264,19 @@ def test_host_pairing_rejects_bad_input(lib):
     w[1, 2] = 1.0
     w[3, 3] = np.nan          # the diagonal is ignored
     assert lib.saga_min_weight_pairing(4, w.ctypes.data, part, None) == api.OK
+
+
+def test_host_pairing_sixteen_heads_planted(lib):
+    # 16 heads (the largest merge; 2027025 perfect matchings): a planted matching of
+    # weight 0.01 per pair against weights >= 1 elsewhere is the unique optimum
+    rng = np.random.default_rng(7)
+    n = 16
+    perm = rng.permutation(n)
+    w = (1.0 + rng.random((n, n))).astype(np.float32)
+    w = w + w.T
+    planted = sorted(tuple(sorted((int(perm[2 * i]), int(perm[2 * i + 1])))) for i in range(n // 2))
+    for a, b in planted:
+        w[a, b] = w[b, a] = 0.01
+    partner, total = api.min_weight_pairing(w)
+    assert sorted((a, b) for a, b in enumerate(partner) if a < b) == planted
+    assert abs(total - 0.08) <= 1e-6
