@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kBlock) void k_pair(const PairArgs a) {
   constexpr bool kVtLds = D <= 64;         // V^T in LDS too (d = 128: in the scratch)
   __shared__ double s_m[D * D];
   __shared__ double s_vt[kVtLds ? D * D : 1];
-  __shared__ int s_p[HALF], s_q[HALF];     // this round's index pairs (p < q)
+  __shared__ int s_p[HALF], s_q[HALF];     // the rotation round's index pairs (p < q)
   __shared__ double s_c[HALF], s_s[HALF];  // and their rotations
   __shared__ double s_red[kWaves];
   __shared__ double s_linv[D];             // 1 / eigenvalue, 0 below the cut
