@@ -97,11 +97,11 @@ saga_status launched() { return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA
 
 // --- k_proj: Y[t, n] = sum_x X[t, x] W[n, x] ----------------------------------------
 // W rows n < nq come from w_q, the others from w_k (both [rows, D], D-contiguous: the
-// transposes of the pages' W_Q and W_K). A wave computes a 32 x 64 tile of Y as
-// 2 x 4 MFMA tiles (bf16 16x16x32): X rows as the A operand, W rows as the B
+// transposes of the pages' W_Q and W_K). A wave computes a 64 x 64 tile of Y as
+// 4 x 4 MFMA tiles (bf16 16x16x32): X rows as the A operand, W rows as the B
 // operand, each lane loading its 16-byte K slices straight from memory as the score
-// tiles do. Rows past T are clamped on load and never stored.
-// grid = (ceil(n_cols / 128), ceil(T / 64)), block = 256 (waves 2 x 2 over the tile).
+// tiles do (each load feeds four MFMAs). Rows past T are clamped on load and never
+// stored. grid = (ceil(n_cols / 128), ceil(T / 128)), block = 256 (waves 2 x 2).
 struct ProjArgs {
   const bf16_t* x;
   const bf16_t* wq;
@@ -110,52 +110,45 @@ struct ProjArgs {
   int T, D, nq, n_cols;
 };
 
-constexpr int kProjSteps = 2;  // 32-wide K steps in flight per wave
+constexpr int kProjTile = 64;  // rows and columns of Y per wave
 
 __global__ __launch_bounds__(kBlock) void k_proj(const ProjArgs a) {
+  constexpr int NT = kProjTile / 16;  // MFMA tiles per side
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int m0 = blockIdx.y * 64 + (wv >> 1) * 32;
-  const int n0 = blockIdx.x * 128 + (wv & 1) * 64;
-  const bf16_t* xr[2];
-  const bf16_t* wr[4];
+  const int m0 = blockIdx.y * 2 * kProjTile + (wv >> 1) * kProjTile;
+  const int n0 = blockIdx.x * 2 * kProjTile + (wv & 1) * kProjTile;
+  const bf16_t* xr[NT];
+  const bf16_t* wr[NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) xr[i] = a.x + (size_t)min(m0 + 16 * i + r16, a.T - 1) * a.D + 8 * kq;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NT; ++i) {
+    xr[i] = a.x + (size_t)min(m0 + 16 * i + r16, a.T - 1) * a.D + 8 * kq;
     const int n = min(n0 + 16 * i + r16, a.n_cols - 1);
     wr[i] = (n < a.nq ? a.wq + (size_t)n * a.D : a.wk + (size_t)(n - a.nq) * a.D) + 8 * kq;
   }
-  floatx4 acc[2][4];
+  floatx4 acc[NT][NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[i][k] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.D; k0 += 32 * kProjSteps) {
-    V16 xa[kProjSteps][2], wb[kProjSteps][4];
+    for (int k = 0; k < NT; ++k) acc[i][k] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.D; k0 += 32) {  // D is a multiple of 32
+    V16 xa[NT], wb[NT];
 #pragma unroll
-    for (int u = 0; u < kProjSteps; ++u) {
-      const int k = min(k0 + 32 * u, a.D - 32);  // D is a multiple of 32; a clamped step is masked below
-#pragma unroll
-      for (int i = 0; i < 2; ++i) xa[u][i].u = ld16(xr[i] + k);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wb[u][i].u = ld16(wr[i] + k);
+    for (int i = 0; i < NT; ++i) {
+      xa[i].u = ld16(xr[i] + k0);
+      wb[i].u = ld16(wr[i] + k0);
     }
 #pragma unroll
-    for (int u = 0; u < kProjSteps; ++u) {
-      if (k0 + 32 * u >= a.D) break;  // uniform over the wave
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][i].h, wb[u][k].h, acc[i][k], 0, 0, 0);
-    }
+      for (int k = 0; k < NT; ++k)
+        acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i].h, wb[k].h, acc[i][k], 0, 0, 0);
   }
   // accumulator layout: lane l holds Y[m + 4 (l >> 4) + r][n + (l & 15)]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NT; ++k) {
       const int n = n0 + 16 * k + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -650,7 +643,8 @@ saga_status saga_merge_losses(const saga_merge_shape* s, const void* x, const vo
   pj.D = s->d_model;
   pj.nq = s->h_q * s->d;
   pj.n_cols = m.n_cols;
-  hipLaunchKernelGGL(k_proj, dim3((m.n_cols + 127) / 128, (s->tokens + 63) / 64), dim3(kBlock), 0, hs, pj);
+  hipLaunchKernelGGL(k_proj, dim3((m.n_cols + 2 * kProjTile - 1) / (2 * kProjTile), (s->tokens + 2 * kProjTile - 1) / (2 * kProjTile)),
+                     dim3(kBlock), 0, hs, pj);
 
   GramArgs g{};
   g.y = pj.y;
