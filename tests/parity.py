@@ -138,3 +138,32 @@ def compare(gpu: dict, ref: "orc.DecodeResult", x, dtype: str, check_tau: bool, 
             else:
                 assert err.max() <= tol * scale, f"{where} out rel err {err.max() / scale:.3e} > {tol}"
     return band_rows
+
+
+def check_sampled_rows(x, N: int, rows, gots, dtype: str):
+    """The rules above, row by row, for a sample of (sequence, head) rows of inputs too
+    large for a whole-batch fp64 oracle. Every result in `gots` (steps that share one
+    exact threshold per row: a refresh step and steps reusing its threshold) is
+    checked against the oracle's logits, threshold and eq. (7) output for each row."""
+    h_q, h_k, h_v = x.q.shape[1], x.k.shape[1], x.v.shape[1]
+    scale = 1.0 / np.sqrt(x.q.shape[2])
+    for b, j in rows:
+        L = int(x.l_kv[b])
+        kg, vg = orc.key_head_of(j, h_q, h_k), orc.value_head_of(j, h_q, h_v)
+        a = orc.attention_logits(x.q[b, j].double().numpy(), x.k[b, kg, :L].double().numpy(), scale)
+        t_o = orc.nth_largest(a, N)
+        rs = row_scale(a)
+        s_o = set(orc.threshold_select(a, t_o).tolist())
+        for got in gots:
+            t_g = got["tau"][b, j]
+            assert abs(t_g - t_o) <= BAND * max(abs(t_o), rs), (b, j, t_g, t_o)
+            n = int(got["count"][b, j])
+            s_g = set(got["idx"][b, j, :n].tolist())
+            assert len(s_g) == n
+            for i in s_g ^ s_o:
+                assert in_band(a[i], (t_o, t_g), rs), (b, j, i)
+            sel = np.array(sorted(s_g))
+            V_sel = x.v[b, vg][torch.from_numpy(sel)].double().numpy()
+            o_ref, _ = orc.sparse_softmax_pv(a[sel], V_sel)
+            err = np.abs(got["O"][b, j] - o_ref).max() / np.abs(o_ref).max()
+            assert err <= out_tol(dtype), (b, j, err)

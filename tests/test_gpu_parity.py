@@ -10,7 +10,7 @@ import torch
 from oracle import saga_oracle as orc
 from sparse_decode_attention_saga_amd import api
 from sparse_decode_attention_saga_amd import workloads as wl
-from tests.parity import BAND, GpuCase, compare, in_band, out_tol, row_scale
+from tests.parity import GpuCase, check_sampled_rows, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -152,29 +152,9 @@ def test_batch16_full_size_sampled_rows():
     g = GpuCase(x, w.N)
     got0 = g.step(w.refresh_period, 0)
     got1 = g.step(w.refresh_period, 1)
-    scale = 1.0 / np.sqrt(w.d)
     rows = [(0, 0), (1, 11), (3, 5), (6, 8), (8, 2), (10, 9), (13, 4), (15, 7)]
-    for b, j in rows:
-        L = int(x.l_kv[b])
-        kg, vg = orc.key_head_of(j, w.h_q, w.h_k), orc.value_head_of(j, w.h_q, w.h_v)
-        a = orc.attention_logits(x.q[b, j].double().numpy(), x.k[b, kg, :L].double().numpy(), scale)
-        V = x.v[b, vg, :L].double().numpy()
-        t_o = orc.nth_largest(a, w.N)
-        rs = row_scale(a)
-        for got in (got0, got1):
-            t_g = got["tau"][b, j]
-            assert abs(t_g - t_o) <= BAND * max(abs(t_o), rs), (b, j, t_g, t_o)
-            n = int(got["count"][b, j])
-            s_g = set(got["idx"][b, j, :n].tolist())
-            s_o = set(orc.threshold_select(a, t_o).tolist())
-            assert len(s_g) == n
-            for i in s_g ^ s_o:
-                assert in_band(a[i], (t_o, t_g), rs), (b, j, i)
-            sel = np.array(sorted(s_g))
-            o_ref, _ = orc.sparse_softmax_pv(a[sel], V[sel])
-            err = np.abs(got["O"][b, j] - o_ref).max() / np.abs(o_ref).max()
-            assert err <= out_tol(w.dtype), (b, j, err)
-        assert np.array_equal(got0["count"][b, j], got1["count"][b, j])
+    check_sampled_rows(x, w.N, rows, [got0, got1], w.dtype)
+    assert np.array_equal(got0["count"], got1["count"])
 
 
 # --- multi-step decode: appended rows, drifting query, periodic refresh ----------
