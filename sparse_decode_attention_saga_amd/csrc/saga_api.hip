@@ -12,6 +12,7 @@ using namespace saga;
 namespace {
 
 constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
+constexpr int kMaxWaveKeyBytes = 32768;  // keys one wave of a streaming kernel has in flight
 
 // Runs the statement with P = the page flag as a compile-time constant.
 #define SAGA_PAGED(FLAG, ...)          \
@@ -25,16 +26,21 @@ constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
     }                                  \
   } while (0)
 
-// Runs the statement with W = the chunk width (1 or 2) as a compile-time constant.
-#define SAGA_WIDTH(WIDTH, ...)         \
-  do {                                 \
-    if ((WIDTH) == 2) {                \
-      constexpr int W = 2;             \
-      __VA_ARGS__                      \
-    } else {                           \
-      constexpr int W = 1;             \
-      __VA_ARGS__                      \
-    }                                  \
+// Runs the statement with W = the tiles per wave of the key-streaming kernels (2, 4 or
+// 8) as a compile-time constant. Needs T and DK: forms over kMaxWaveKeyBytes are never
+// chosen (stream_tiles) and are not instantiated.
+#define SAGA_TILES(TILES, ...)                                                        \
+  do {                                                                                \
+    if ((TILES) == 8) {                                                               \
+      constexpr int W = 16 * 8 * DK * (int)sizeof(T) <= kMaxWaveKeyBytes ? 8 : 4;    \
+      __VA_ARGS__                                                                     \
+    } else if ((TILES) == 4) {                                                        \
+      constexpr int W = 4;                                                            \
+      __VA_ARGS__                                                                     \
+    } else {                                                                          \
+      constexpr int W = 2;                                                            \
+      __VA_ARGS__                                                                     \
+    }                                                                                 \
   } while (0)
 
 // Runs the statement with T = the element type, DK and DV = the key and value head
@@ -87,24 +93,34 @@ constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
 int value_dim(const saga_shape* s) { return s->d_v > 0 ? s->d_v : s->d; }
 
 // Keys per chunk of the stream kernels at width W (1 or 2); d is the key head dimension.
-int chunk_keys(int dtype, int d, int W) {
-  int ch = 0;
-  SAGA_DISPATCH(dtype, d, d, ch = W == 2 ? StreamCfg<T, DK, 2>::kChunk : StreamCfg<T, DK, 1>::kChunk;);
-  return ch;
-}
+// Tiles per wave of the key-streaming kernels (8, 4 or 2 tiles of 16 keys). The widest
+// chunks that still give the launch two blocks per compute unit, unless twice as wide
+// chunks give every unit a block and every wave a full 16 KiB of keys. Measured at
+// batch 1: the 32K Llama-shaped layer (2 key heads of 64) takes 13.5 us per step with
+// 128 blocks of 512 keys and 11.6 us with 512 blocks of 128; the 64K Qwen-shaped layer
+// (1 key head of 128) is faster with 256 blocks of 256 keys (16 KiB per wave) than with
+// 512 of 128. Narrower chunks than that only add chunk records. A wave holds at most
+// kMaxWaveKeyBytes of keys in flight (its registers).
+constexpr long long kMinStreamBlocks = 2 * 256;
+constexpr int kFullWaveKeyBytes = 16384;
 
-// Wide chunks (W = 2) when they still give every compute unit of the chip two
-// blocks: measured at 128K keys they are 3-8% faster from two sequences on, and 7%
-// slower for one sequence, whose 256 wide blocks leave one block per unit.
-constexpr int kWideMinBlocks = 2 * 256;
-
-int chunk_width(const saga_shape* s, int max_l_kv) {
-  if (max_l_kv <= 0) return 1;
+int stream_tiles(const saga_shape* s, int max_l_kv) {
+  const int row_bytes = s->d * (s->dtype == SAGA_BF16 ? 2 : 4);
+  int t_max = 8;
+  while (t_max > 2 && 16 * t_max * row_bytes > kMaxWaveKeyBytes) t_max /= 2;
+  if (max_l_kv <= 0) return t_max;
   const int g_k = s->h_q / s->h_k;
   const long long groups = (long long)s->h_k * ((g_k + 15) / 16) * s->batch;
-  const long long ch2 = chunk_keys(s->dtype, s->d, 2);
-  if (ch2 == chunk_keys(s->dtype, s->d, 1)) return 1;
-  return groups * ((max_l_kv + ch2 - 1) / ch2) >= kWideMinBlocks ? 2 : 1;
+  auto blocks = [&](int t) {
+    const long long ch = 16LL * t * kWaves;
+    return groups * ((max_l_kv + ch - 1) / ch);
+  };
+  int t = t_max;
+  while (t > 2 && blocks(t) < kMinStreamBlocks) t /= 2;
+  if (t < t_max && 16 * t * row_bytes < kFullWaveKeyBytes && 16 * 2 * t * row_bytes >= kFullWaveKeyBytes &&
+      blocks(2 * t) >= kMinStreamBlocks / 2)
+    t *= 2;
+  return t;
 }
 
 saga_status check_shape(const saga_shape* s) {
@@ -130,7 +146,7 @@ saga_status check_shape(const saga_shape* s) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  int rows, W, ch, nch, P;  // W: chunk width of the stream kernels; P: threshold-candidate blocks per row
+  int rows, W, ch, nch, P;  // W: tiles per wave of the stream kernels; P: threshold-candidate blocks per row
   int nchd;                 // chunks of the dense kernels (always width 1)
   long long lpad;
   size_t hist, cand_cnt;
@@ -140,10 +156,11 @@ struct Layout {
 Layout layout(const saga_shape* s, int max_l_kv) {
   Layout w{};
   w.rows = s->batch * s->h_q;
-  w.W = chunk_width(s, max_l_kv);
-  w.ch = chunk_keys(s->dtype, s->d, w.W);
+  w.W = stream_tiles(s, max_l_kv);
+  w.ch = 16 * w.W * kWaves;
   w.nch = max_l_kv > 0 ? (max_l_kv + w.ch - 1) / w.ch : 1;
-  const int chd = chunk_keys(s->dtype, s->d, 1);
+  int chd = 0;
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), chd = StreamCfg<T, DK>::kChunk;);
   w.nchd = max_l_kv > 0 ? (max_l_kv + chd - 1) / chd : 1;
   w.lpad = (long long)w.nch * w.ch;
   w.P = max_l_kv > 0 ? (max_l_kv + kSelSlice - 1) / kSelSlice : 1;
@@ -157,12 +174,18 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   // counters first: they must be zero before the first call and every call leaves them at zero
   w.hist = take((size_t)kHistCopies * rows * 256 * 4);
   w.cand_cnt = take(rows * 4);
-  w.scores = take(rows * (size_t)w.lpad * 4);
-  w.surv_idx = take(rows * (size_t)w.lpad * 4);
-  w.surv_val = take(rows * (size_t)w.lpad * 4);
-  w.chunk_hdr = take(rows * (size_t)w.nch * sizeof(ChunkHdr));
+  // sized for every chunk width (the narrowest chunks have the most records; lpad is at
+  // most max_l_kv rounded up to the widest chunk), so that the size only grows with
+  // max_l_kv whatever width a launch takes
+  const int ch_min = 16 * 2 * kWaves, ch_max = 16 * 8 * kWaves;
+  const size_t lpad_max = max_l_kv > 0 ? (size_t)(max_l_kv + ch_max - 1) / ch_max * ch_max : (size_t)ch_max;
+  const size_t nch_max = max_l_kv > 0 ? (size_t)(max_l_kv + ch_min - 1) / ch_min : 1;
+  w.scores = take(rows * lpad_max * 4);
+  w.surv_idx = take(rows * lpad_max * 4);
+  w.surv_val = take(rows * lpad_max * 4);
+  w.chunk_hdr = take(rows * nch_max * sizeof(ChunkHdr));
   // chunk records (sparse: d_v floats, dense: d_v + 4)
-  w.part = take(rows * (size_t)(w.nch > w.nchd ? w.nch : w.nchd) * (value_dim(s) + 4) * 4);
+  w.part = take(rows * (nch_max > (size_t)w.nchd ? nch_max : (size_t)w.nchd) * (value_dim(s) + 4) * 4);
   w.total = off;
   return w;
 }
@@ -266,7 +289,7 @@ dim3 stream_grid(const saga_shape* s, const Layout& w) {
 }
 
 void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, float* tau, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_TILES(w.W, {
     hipLaunchKernelGGL((k_scores_hist<T, DK, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });););
   hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
@@ -276,7 +299,7 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
 // Scores and Atop-N comparison; with `gather` also the chunk records of eq. (7).
 void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, bool gather,
                    hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_TILES(w.W, {
     dim3 grid = stream_grid(s, w);
     grid.y *= a.hsplit;
     if (!gather)
@@ -292,13 +315,13 @@ void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bo
 
 // Chunk records from the kept lists (only for the separate gather stage).
 void launch_chunk_gather(const saga_shape* s, const Layout& w, const StreamArgs& a, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_WIDTH(w.W, {
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_TILES(w.W, {
     hipLaunchKernelGGL((k_chunk_gather<T, DK, DV, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });););
 }
 
 void launch_combine(const saga_shape* s, const Layout& w, const GatherArgs& g, hipStream_t st) {
-  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(g.s.ptab != nullptr, SAGA_WIDTH(w.W, {
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(g.s.ptab != nullptr, SAGA_TILES(w.W, {
     hipLaunchKernelGGL((k_split_combine<T, DK, DV, P, W>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
   });););
 }

@@ -21,18 +21,15 @@
 
 namespace saga {
 
-// Keys per block of the key-streaming kernels: 4 waves x TPW tiles x 16 keys.
-// W = 2 is the wide form for launches with many blocks: twice the tiles per wave
-// (at most 8: the kept mask of a lane holds 32 entries), so each resident block
-// keeps twice the keys in flight and a step has half the chunk records.
-#ifndef SAGA_KEY_BYTES_PER_WAVE
-#define SAGA_KEY_BYTES_PER_WAVE 16384  // K bytes one wave has in flight per chunk
-#endif
-template <typename T, int D, int W = 1> struct StreamCfg {
+// Keys per block of the key-streaming kernels: 4 waves x TPW tiles x 16 keys. The
+// launch picks W = TPW from 2, 4 and 8 (the kept mask of a lane holds 32 entries);
+// W = 0 is the base form used by the dense kernels and the exact row pass: 16 KiB of
+// keys per wave, at most 8 tiles.
+template <typename T, int D, int W = 0> struct StreamCfg {
   static constexpr int kRowBytes = D * (int)sizeof(T);
-  static constexpr int kBase = SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) > 0 ? SAGA_KEY_BYTES_PER_WAVE / (16 * kRowBytes) : 1;
-  static constexpr int kTPW = kBase * W > 8 ? 8 : kBase * W;  // 16-key tiles per wave
-  static_assert(kTPW >= 1, "at least one tile per wave");
+  static constexpr int kBase = 16384 / (16 * kRowBytes) > 0 ? 16384 / (16 * kRowBytes) : 1;
+  static constexpr int kTPW = W > 0 ? W : (kBase > 8 ? 8 : kBase);  // 16-key tiles per wave
+  static_assert(kTPW >= 1 && kTPW <= 8, "one to eight tiles per wave");
   static constexpr int kChunk = 16 * kTPW * kWaves;
 };
 

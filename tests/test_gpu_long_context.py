@@ -1,9 +1,8 @@
 """A context of 2^20 keys, eight times the pages' longest (needs an MI355X).
 
 The Qwen2.5-1.5B-shaped layer (h_q=12, h_k=1, h_v=4, d=128, bf16, N=512) at
-l_kv = 1,048,576: 2048 wide chunks of 512 keys in one sequence, which takes the
-wide key-streaming kernels with speculative key loads and a combine over 2048
-chunk records per row. The oracle is evaluated row by row (every one of the 12
+l_kv = 1,048,576: 2048 chunks of 512 keys (8 tiles per wave) in one sequence, with
+speculative key loads and a combine over 2048 chunk records per row. The oracle is evaluated row by row (every one of the 12
 rows) for the decode step and for the dense kernels (SAGA with full attention
 over all 2^20 keys).
 """

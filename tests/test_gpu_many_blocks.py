@@ -2,8 +2,8 @@
 
 Each case gives the select kernel at least 2048 chunk blocks (chunks x key heads x
 head splits x sequences; the comments give the count) at a size the oracle finishes
-in seconds: many key heads, heads split over many blocks per chunk, fp32 wide
-chunks. The lengths are ragged so that some blocks hold no keys (an empty sequence,
+in seconds: many key heads, heads split over many blocks per chunk, fp32 chunks
+of 512 keys. The lengths are ragged so that some blocks hold no keys (an empty sequence,
 a sequence of one key) and the last chunk of a sequence is partly past its length.
 Stale, forced and mixed thresholds are checked, and paged caches against the
 contiguous ones.
@@ -41,7 +41,7 @@ CASES = [
     (4, 12, 1, 4, 128, [16384, 9000, 1, 16000], 16384, "bf16", 8192),
     # 16 chunks of 512 keys x 32 key heads x 4 sequences = 2048 blocks
     (4, 64, 32, 32, 64, [8192, 0, 5000, 8191], 8192, "bf16", 64),
-    # fp32 in wide chunks of 512 keys: 16 chunks x 64 key heads x 2 sequences = 2048 blocks
+    # fp32 in chunks of 512 keys: 16 chunks x 64 key heads x 2 sequences = 2048 blocks
     (2, 64, 64, 64, 64, [8192, 3001], 8192, "f32", 32),
 ]
 

@@ -80,21 +80,23 @@ def test_small_shapes_refresh_and_stale(case):
     assert np.array_equal(got1["count"], got["count"])
 
 
-# launches with many blocks take the wide chunks (twice the keys per block); these
-# shapes reach them at sizes the oracle finishes quickly
-WIDE = [
-    # B, h_q, h_k, h_v, d, lens, dtype, N
+# The chunk width follows the launch: the widest chunks (8, 4 or 2 tiles of 16 keys
+# per wave) that still give two blocks per compute unit. The small shapes above take
+# 2 tiles; these reach the wider forms at sizes the oracle finishes quickly.
+CHUNK_FORMS = [
+    # B, h_q, h_k, h_v, d, lens, dtype, N                                  tiles per wave
     (16, 12, 1, 4, 128, [16384, 1, 9000, 16383, 256, 511, 12000, 16384, 700, 16000, 3, 8192, 8193, 15000, 4097,
-                         16384], "bf16", 64),
-    (8, 32, 2, 8, 128, [16384, 16000, 9000, 16384, 2049, 16384, 12345, 16384], "bf16", 2048),
-    (16, 16, 1, 2, 128, [16384] * 16, "f32", 32),
+                         16384], "bf16", 64),                                # 8
+    (8, 32, 2, 8, 128, [16384, 16000, 9000, 16384, 2049, 16384, 12345, 16384], "bf16", 2048),  # 8
+    (16, 16, 1, 2, 128, [16384] * 16, "f32", 32),                          # 4 (32 KiB per wave)
+    (4, 32, 2, 8, 64, [16384, 9000, 16383, 1], "bf16", 256),               # 4
 ]
 
 
-@pytest.mark.parametrize("case", range(len(WIDE)))
-def test_wide_chunks_refresh_and_stale(case):
-    B, h_q, h_k, h_v, d, lens, dtype, N = WIDE[case]
-    say(f"wide case {case}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} N={N} {dtype}")
+@pytest.mark.parametrize("case", range(len(CHUNK_FORMS)))
+def test_chunk_widths_refresh_and_stale(case):
+    B, h_q, h_k, h_v, d, lens, dtype, N = CHUNK_FORMS[case]
+    say(f"chunk form {case}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} N={N} {dtype}")
     w, x = small(B, h_q, h_k, h_v, d, lens, dtype, seed=50 + case)
     g = GpuCase(x, N, sel_cap=min(max(lens), 4 * N))
     got = g.step(4, 0)

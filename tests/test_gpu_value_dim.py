@@ -72,10 +72,10 @@ def test_reduced_key_dim_refresh_stale_forced(case):
 
 
 def test_reduced_key_dim_wide_chunks():
-    # 16 sequences: the launch takes the wide chunks (twice the keys per block)
+    # 16 sequences: the launch takes chunks of 512 keys (8 tiles per wave)
     lens = [16384, 1, 9000, 16383, 256, 511, 12000, 16384, 700, 16000, 3, 8192, 8193, 15000, 4097, 16384]
     x = small(16, 12, 2, 4, 64, 128, lens, "bf16", seed=20)
-    say("wide chunks, (d_k, d_v) = (64, 128), B=16")
+    say("chunks of 512 keys, (d_k, d_v) = (64, 128), B=16")
     g = GpuCase(x, 64, sel_cap=256)
     got = g.step(4, 0)
     ref = oracle_step(x, 64, 4, 0)

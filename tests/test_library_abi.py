@@ -58,6 +58,19 @@ def test_workspace_bytes(lib):
     assert lib.saga_workspace_bytes(ctypes.byref(shape(d=96)), 512, 1024) == 0
     assert lib.saga_workspace_bytes(ctypes.byref(s), 0, 1024) == 0
     assert lib.saga_workspace_bytes(ctypes.byref(s), 8, 131073) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(batch=3), dict(h_q=32, h_k=2, h_v=8, d=64), dict(dtype=api.F32, out_dtype=api.F32),
+                                dict(h_q=32, h_k=4, h_v=8, d=32, d_v=64)])
+def test_workspace_grows_with_context(lib, kw):
+    # the launch picks its chunk width from max_l_kv (narrower chunks, more records
+    # below some lengths); a workspace sized for a length serves every shorter one
+    s = shape(**kw)
+    lengths = sorted({1, 127, 128, 129, 4095, 4096, 16384, 32767, 32768, 65535, 65536, 65537, 98304, 130816,
+                      131071, 131072} | {131072 * i // 97 for i in range(1, 97)})
+    sizes = [lib.saga_workspace_bytes(ctypes.byref(s), 512, L) for L in lengths]
+    assert all(n > 0 for n in sizes)
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])), list(zip(lengths, sizes))
     assert lib.saga_workspace_bytes(None, 8, 16) == 0
 
 
