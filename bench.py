@@ -655,17 +655,19 @@ def main() -> int:
         w = w.with_(batch=args.batch)
     dev = torch.device("cuda:0")
     api.lib()
-    L = w.l_kv
     es = 2 if w.dtype == "bf16" else 4
-    bytes_k = bytemodel.key_bytes(w.h_k, w.d, [L] * w.batch, es)
-    R = rotating_sets(bytes_k, w.refresh_period, args.sets)
-    dims = f"d={w.d}" if w.dv == w.d else f"d_k={w.d} d_v={w.dv}"
-    log(f"workload {w.name}: B={w.batch} h_q={w.h_q} h_k={w.h_k} h_v={w.h_v} {dims} l_kv={L} "
-        f"N={w.N} n={w.refresh_period}; {R} rotating sets")
-
     t0 = time.perf_counter()
     x = wl.generate(w, seed=0)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    L = int(x.k.shape[2])              # cache capacity: the longest sequence
+    lens = [int(n) for n in x.l_kv]
+    ragged = len(set(lens)) > 1
+    bytes_k = bytemodel.key_bytes(w.h_k, w.d, lens, es)
+    R = rotating_sets(bytes_k, w.refresh_period, args.sets)
+    dims = f"d={w.d}" if w.dv == w.d else f"d_k={w.d} d_v={w.dv}"
+    ctx = f"l_kv={min(lens)}..{max(lens)} (mean {np.mean(lens):.0f})" if ragged else f"l_kv={L}"
+    log(f"workload {w.name}: B={w.batch} h_q={w.h_q} h_k={w.h_k} h_v={w.h_v} {dims} {ctx} "
+        f"N={w.N} n={w.refresh_period}; {R} rotating sets")
     q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     l_kv = torch.from_numpy(x.l_kv).to(dev)
     qs = [q0] + [q0.clone() for _ in range(R - 1)]
@@ -748,8 +750,8 @@ def main() -> int:
     dense = {}
     if w.dense_h_kv and args.only in ("all", "dense"):
         wd = w.with_(h_k=w.dense_h_kv, h_v=w.dense_h_kv, workload_id=w.workload_id + 100)
-        xd = wl.generate(wd, seed=0)
-        bytes_d = bytemodel.dense_bytes(wd.h_k, wd.d, [L] * wd.batch, es)
+        xd = wl.generate(wd, seed=0, lengths=lens, l_max=L)
+        bytes_d = bytemodel.dense_bytes(wd.h_k, wd.d, lens, es)
         Rd = rotating_sets(bytes_d, 1, 0)
         qd = xd.q.to(dev)
         kd = [xd.k.to(dev)]
@@ -771,7 +773,7 @@ def main() -> int:
         log(f"dense GQA (h_kv={wd.h_k}): {dense['us']:.2f} us/step")
         del kd, vd
 
-    if not args.no_layer and args.only in ("all", "layer") and w.dv == w.d:
+    if not args.no_layer and args.only in ("all", "layer") and w.dv == w.d and not ragged:
         res["layer"] = layer_timing(torch, api, wl, w, ks, vs, L, args)
 
     if "paged" in res and "saga_us" in res:
@@ -812,7 +814,9 @@ def main() -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_k": w.h_k, "h_v": w.h_v,
-                   "d": w.d, "d_v": w.dv, "l_kv": L, "N": w.N, "refresh_period": w.refresh_period,
+                   "d": w.d, "d_v": w.dv, "l_kv": L if not ragged else {"min": min(lens), "max": max(lens),
+                                                                         "mean": float(np.mean(lens))},
+                   "N": w.N, "refresh_period": w.refresh_period,
                    "accumulate": "f32", "rotating_sets": R, "dense_h_kv": w.dense_h_kv},
         "us_per_step": us,
         "us_per_step_p10": pct(res["saga_us"], 10),
