@@ -462,6 +462,80 @@ def decompose(torch, args) -> int:
     return 0
 
 
+def stages(torch, args) -> int:
+    """The stages of the decode step as separate launches, at a workload (default: the
+    Qwen2.5-1.5B-shaped 128K layer), each timed alone from a graph of launches over
+    rotating input sets: the key stream with the Atop-N comparison (saga_qk_select,
+    algorithmic bytes = the keys), the value gather into chunk records followed by the
+    combine (saga_sparse_gather over the kept lists of one saga_qk_select call,
+    algorithmic bytes = the selected value rows), and the step's fused select kernel
+    and combine (saga_select_gather, saga_split_combine). Under rocprofv3 the same
+    command gives each kernel's duration and counters."""
+    from sparse_decode_attention_saga_amd import api
+    from sparse_decode_attention_saga_amd import bytemodel
+    from sparse_decode_attention_saga_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    api.lib()
+    w = wl.WORKLOADS[args.workload]
+    es = 2 if w.dtype == "bf16" else 4
+    x = wl.generate(w, seed=0)
+    L = int(x.k.shape[2])
+    lens = [int(n) for n in x.l_kv]
+    bytes_k = bytemodel.key_bytes(w.h_k, w.d, lens, es)
+    R = rotating_sets(bytes_k, w.refresh_period, args.sets)
+    q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    l_kv = torch.from_numpy(x.l_kv).to(dev)
+    ks = [k0] + [k0.clone() for _ in range(R - 1)]
+    vs = [v0] + [v0.clone() for _ in range(R - 1)]
+    tau = torch.zeros(w.batch, w.h_q, dtype=torch.float32, device=dev)
+    out = torch.empty(w.batch, w.h_q, w.dv, dtype=q0.dtype, device=dev)
+    ws = api.Workspace(api.make_shape(q0, k0, v0), w.N, L, dev)
+    api.refresh_threshold(q0, k0, l_kv, tau, N=w.N, max_l_kv=L, workspace=ws, d_v=w.dv)
+    # the selected value rows of the threshold (the union over each value head's query heads)
+    cap = 8 * w.N
+    sel_count = torch.zeros(w.batch, w.h_q, dtype=torch.int32, device=dev)
+    sel_idx = torch.full((w.batch, w.h_q, cap), -1, dtype=torch.int32, device=dev)
+    api.decode_attn(q0, k0, v0, l_kv, tau, N=w.N, refresh_period=1 << 30, step=1, max_l_kv=L, out=out,
+                    sel_count=sel_count, sel_idx=sel_idx, workspace=ws)
+    torch.cuda.synchronize()
+    counts, idx = sel_count.cpu().numpy(), sel_idx.cpu().numpy()
+    union_rows = []
+    for b in range(w.batch):
+        for vh in range(w.h_v):
+            rows = set()
+            for j in range(w.h_q):
+                if (j * w.h_v) // w.h_q == vh:
+                    rows.update(idx[b, j, : min(counts[b, j], cap)].tolist())
+            union_rows.append(len(rows))
+    bytes_v = bytemodel.selected_value_bytes(union_rows, w.dv, es)
+    K = args.steps
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        return pct([1e3 * m / K for m in time_graph(torch, lambda: [fn(t) for t in range(K)], args.reps)], 50)
+
+    res = {}
+    res["qk_select"] = timed(lambda t: api.qk_select(q0, ks[t % R], l_kv, tau, max_l_kv=L, workspace=ws, d_v=w.dv))
+    api.qk_select(q0, k0, l_kv, tau, max_l_kv=L, workspace=ws, d_v=w.dv)  # the kept lists the gather reads
+    res["sparse_gather"] = timed(lambda t: api.sparse_gather(q0, ks[t % R], vs[t % R], l_kv, tau, N=w.N, max_l_kv=L,
+                                                             out=out, workspace=ws))
+    res["select_gather"] = timed(lambda t: api.select_gather(q0, ks[t % R], vs[t % R], l_kv, tau, max_l_kv=L,
+                                                             workspace=ws))
+    res["split_combine"] = timed(lambda t: api.split_combine(q0, ks[t % R], vs[t % R], l_kv, tau, N=w.N, max_l_kv=L,
+                                                             out=out, workspace=ws))
+    for k, v in res.items():
+        log(f"{k}: {v:.2f} us/launch")
+    line = {"stages": w.name, "rotating_sets": R, "steps": K, "us": res,
+            "bytes": {"keys": bytes_k, "selected_value_rows": bytes_v},
+            "gbs": {"qk_select_keys": bytes_k / res["qk_select"] / 1e3,
+                    "sparse_gather_value_rows": bytes_v / res["sparse_gather"] / 1e3,
+                    "select_gather_keys_and_rows": (bytes_k + bytes_v) / res["select_gather"] / 1e3}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def device_pages(torch, k, v, page_tokens: int, seed: int):
     """Paged copies of contiguous caches k [B, h_k, L, d], v [B, h_v, L, d_v] (L a
     multiple of the page size) on the device, pages in a seeded random order:
@@ -619,6 +693,8 @@ def main() -> int:
                     help="GQA-to-SAGA key-head merge at the Llama 3.2-1B shape (one JSON line)")
     ap.add_argument("--merge-tokens", type=int, nargs="+", default=[512, 4096],
                     help="calibration token counts of --merge")
+    ap.add_argument("--stages", action="store_true",
+                    help="time the stages of the step as separate launches (key stream, value gather, combine)")
     ap.add_argument("--decompose", action="store_true",
                     help="dense and Atop-N steps with grouped-query and with SAGA heads (one JSON line)")
     args = ap.parse_args()
@@ -643,6 +719,8 @@ def main() -> int:
         return sweep(torch, args)
     if args.decompose:
         return decompose(torch, args)
+    if args.stages:
+        return stages(torch, args)
     if args.merge:
         return merge_bench(torch, args)
 
