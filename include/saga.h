@@ -75,7 +75,9 @@ typedef struct saga_shape {
 const char* saga_status_str(int32_t status);
 
 /* Bytes of workspace the calls below need for `s`, top-N size N and contexts up to
- * max_l_kv tokens. 0 if the shape is invalid. Pure host arithmetic. */
+ * max_l_kv tokens. 0 if the shape is invalid. Pure host arithmetic. The size never
+ * decreases with max_l_kv, so a workspace sized for a context serves every call with
+ * a smaller max_l_kv (a growing decode context allocates once). */
 size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv);
 
 /* Enqueue a zero fill of `bytes` bytes of `workspace` (first-use initialisation). */
