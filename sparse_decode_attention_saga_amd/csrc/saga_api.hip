@@ -92,7 +92,6 @@ constexpr int kMaxWaveKeyBytes = 32768;  // keys one wave of a streaming kernel 
 // Value head dimension of a shape (0 in the struct means d).
 int value_dim(const saga_shape* s) { return s->d_v > 0 ? s->d_v : s->d; }
 
-// Keys per chunk of the stream kernels at width W (1 or 2); d is the key head dimension.
 // Tiles per wave of the key-streaming kernels (8, 4 or 2 tiles of 16 keys). The widest
 // chunks that still give the launch two blocks per compute unit, unless twice as wide
 // chunks give every unit a block and every wave a full 16 KiB of keys. Measured at
@@ -147,7 +146,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int rows, W, ch, nch, P;  // W: tiles per wave of the stream kernels; P: threshold-candidate blocks per row
-  int nchd;                 // chunks of the dense kernels (always width 1)
+  int nchd;                 // chunks of the dense kernels (their base chunk: 16 KiB of keys per wave)
   long long lpad;
   size_t hist, cand_cnt;
   size_t scores, surv_idx, surv_val, chunk_hdr, part, total;
