@@ -269,6 +269,23 @@ def test_ties_keep_every_equal_logit():
         assert np.abs(got["O"][0, j] - mean).max() <= 2e-3 * np.abs(mean).max()
 
 
+def test_zero_query_keeps_every_key():
+    # a query head of zeros: every logit is 0 (the threshold is 0 and every key ties
+    # with it), so the head keeps the whole row and averages its value rows; the
+    # other heads of the same key head are unaffected
+    w, x = small(2, 8, 2, 4, 64, [700, 1500], "bf16", seed=35)
+    x.q[1, 3] = 0
+    g = GpuCase(x, 16, sel_cap=1500)
+    got = g.step(4, 0)
+    ref = oracle_step(x, 16, 4, 0)
+    compare(got, ref, x, "bf16", check_tau=True)
+    assert got["tau"][1, 3] == 0 and got["count"][1, 3] == 1500
+    mean = x.v[1, 3 // 2, :1500].double().numpy().mean(axis=0)
+    assert np.abs(got["O"][1, 3] - mean).max() <= 2e-3 * np.abs(mean).max()
+    got1 = g.step(4, 1)                           # the stale zero threshold keeps them again
+    assert got1["count"][1, 3] == 1500 and got1["flags"][1, 3] == 0
+
+
 # --- the other entry points --------------------------------------------------------
 
 def test_refresh_threshold_entry_point():
