@@ -286,6 +286,38 @@ def test_zero_query_keeps_every_key():
     assert got1["count"][1, 3] == 1500 and got1["flags"][1, 3] == 0
 
 
+@pytest.mark.parametrize("scale", [0.05, 2.5])
+def test_given_logit_scale(scale):
+    # a logit scale other than 1/sqrt(d) (saga_shape.scale): the decode step (refresh
+    # and stale) and the dense kernel against the oracle with the same scale
+    w, x = small(2, 12, 1, 4, 128, [3000, 777], "bf16", seed=36)
+    N = 32
+    dev = torch.device("cuda:0")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    l_kv = torch.from_numpy(x.l_kv).to(dev)
+    tau = torch.zeros(2, 12, dtype=torch.float32, device=dev)
+    cnt = torch.zeros(2, 12, dtype=torch.int32, device=dev)
+    idx = torch.full((2, 12, 4 * N), -1, dtype=torch.int32, device=dev)
+    q64, k64, v64 = x.f64()
+    tau_o = None
+    for step in (0, 1):
+        out = api.decode_attn(q, k, v, l_kv, tau, N=N, refresh_period=4, step=step, out_dtype=torch.float32,
+                              sel_count=cnt, sel_idx=idx, scale=scale)
+        torch.cuda.synchronize()
+        got = dict(O=out.double().cpu().numpy(), tau=tau.double().cpu().numpy(), count=cnt.cpu().numpy(),
+                   idx=idx.cpu().numpy())
+        ref = orc.saga_decode_step(q64, k64, v64, x.l_kv, N, 4, step, tau_in=tau_o, scale=scale)
+        compare(got, ref, x, "bf16", check_tau=(step == 0))
+        tau_o = ref.tau
+    dense = api.dense_gqa_attn(q, k, v, l_kv, out_dtype=torch.float32, scale=scale)
+    torch.cuda.synchronize()
+    ref_d = orc.dense_gqa(q64, k64, v64, x.l_kv, scale=scale)
+    got_d = dense.double().cpu().numpy()
+    for b in range(2):
+        for j in range(12):
+            assert np.abs(got_d[b, j] - ref_d[b, j]).max() <= 2e-3 * np.abs(ref_d[b, j]).max(), (b, j)
+
+
 # --- the other entry points --------------------------------------------------------
 
 def test_refresh_threshold_entry_point():

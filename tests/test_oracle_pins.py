@@ -63,6 +63,32 @@ def test_dense_limit_equals_library_attention(h_k, h_v):
             assert r.tau[b, j] == -np.inf
 
 
+@pytest.mark.parametrize("scale", [0.05, 1.0, 2.5])
+def test_given_scale_equals_library_attention(scale):
+    # eq. (2) with a logit scale other than 1/sqrt(d): torch's attention with the same scale
+    q, K, V, lens = rand_case(2, h_q=4, h_k=1, h_v=2)
+    r = orc.saga_decode_step(q, K, V, lens, N=10 ** 6, refresh_period=1, step=0, scale=scale)
+    d = orc.dense_gqa(q, K, V, lens, scale=scale)
+    for b in range(q.shape[0]):
+        L = lens[b]
+        for j in range(4):
+            qt = torch.from_numpy(q[b, j])[None, None, None, :]
+            kt = torch.from_numpy(np.ascontiguousarray(K[b, 0, :L]))[None, None]
+            vt = torch.from_numpy(np.ascontiguousarray(V[b, j * 2 // 4, :L]))[None, None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, 0, 0].numpy()
+            np.testing.assert_allclose(r.O[b, j], ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(d[b, j], ref, rtol=0, atol=1e-12)
+    # and the selection is made on the scaled logits: with N = 1 the largest entry is
+    # kept whatever the (positive) scale
+    r1 = orc.saga_decode_step(q, K, V, lens, N=1, refresh_period=1, step=0, scale=scale)
+    for b in range(q.shape[0]):
+        L = lens[b]
+        for j in range(4):
+            a = K[b, 0, :L] @ q[b, j]
+            assert r1.sel[b][j].tolist() == [int(np.argmax(a))]
+            assert abs(r1.tau[b, j] - scale * a.max()) <= 1e-12 * abs(scale * a.max())
+
+
 def test_equal_heads_is_grouped_query_attention():
     # h_k == h_v: the library's own grouped-query attention (enable_gqa) fixes the
     # head grouping independently of the oracle's head maps.
