@@ -318,6 +318,22 @@ def test_given_logit_scale(scale):
             assert np.abs(got_d[b, j] - ref_d[b, j]).max() <= 2e-3 * np.abs(ref_d[b, j]).max(), (b, j)
 
 
+def test_kept_index_export_capacity():
+    # sel_cap below the kept count: sel_count is still the whole count, the export holds
+    # sel_cap distinct kept indices (any of them), and the output is the whole set's
+    w, x = small(2, 12, 1, 4, 128, [4000, 1300], "bf16", seed=37)
+    N = 64
+    g = GpuCase(x, N, sel_cap=20)
+    got = g.step(4, 0)
+    ref = oracle_step(x, N, 4, 0)
+    compare(got, ref, x, "bf16", check_tau=True, cap_ok=False)
+    for b in range(2):
+        for j in range(12):
+            assert got["count"][b, j] == len(ref.sel[b][j]) >= 20
+            e = got["idx"][b, j]
+            assert len(set(e.tolist())) == 20 and set(e.tolist()) <= set(ref.sel[b][j].tolist()), (b, j)
+
+
 # --- the other entry points --------------------------------------------------------
 
 def test_refresh_threshold_entry_point():
