@@ -123,9 +123,16 @@ def cpu_baseline(w, x, seconds: float):
 
     steps, el = run(seconds)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     with threadpool_limits(limits=1):
         steps1, el1 = run(seconds / 5)
     return {"value": steps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()},
             "sample": f"{steps} consecutive oracle decode steps (steps 0..{steps - 1}, exact threshold at "
                       f"step % {w.refresh_period} == 0) of the full {w.name} workload, {el:.1f} s of host time; "
                       f"float64 numpy, BLAS threads = cores",
