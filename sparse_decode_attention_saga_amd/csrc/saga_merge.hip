@@ -20,9 +20,10 @@
 //   k_proj    Y = X [W_Q W_K] (bf16 MFMA, fp32 out): all queries and keys;
 //   k_gram    partial Grams of the query groups (S_a) and of the keys (H) over
 //             token chunks (fp32 MFMA), k_gram_sum adds the chunks;
-//   k_pair    per pair (a, b): P by a cyclic Jacobi eigendecomposition of
-//             S_a + S_b (fp64), A, B, and L_ab = <Z_a^T Hab Z_a, S_a> +
-//             <Z_b^T Hab Z_b, S_b>;
+//   k_pair    per pair (a, b): P = (S_a + S_b)^+ (fp64: a Gauss-Jordan inverse when
+//             it is certified to equal the pseudo-inverse with the cut, else a
+//             cyclic Jacobi eigendecomposition), A, B, and
+//             L_ab = <Z_a^T Hab Z_a, S_a> + <Z_b^T Hab Z_b, S_b>;
 //   (host)    the minimum-weight perfect matching of the h_k heads;
 //   k_merge   the merged projections of the chosen pairs.
 #include "saga.h"
@@ -40,7 +41,11 @@ namespace {
 constexpr int kMaxMergeHeads = 16;       // teacher key heads (even)
 constexpr double kPinvRcond = 1e-5;      // eigenvalues below rcond * largest count as zero
 constexpr int kJacobiSweeps = 16;        // upper bound; sweeps stop once converged
-constexpr int kGramChunk = 256;          // calibration tokens per partial Gram
+constexpr int kGramSteps = 16;      // 4-token MFMA steps per load round of k_gram
+constexpr int kGramRound = 4 * kGramSteps;  // tokens per load round (all loads of a round in flight)
+constexpr int kGramChunk = 64;      // calibration tokens per partial Gram, at least
+constexpr int kGramMaxChunks = 64;  // partial Grams per output tile, at most
+static_assert(kGramChunk % kGramRound == 0, "whole load rounds per chunk");
 constexpr int kGramTile = 64;            // output tile of one wave in k_gram
 constexpr int kPairScratch = 16;         // d x d fp64 matrices of scratch per pair
 
@@ -50,6 +55,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct MergeLayout {
   int n_cols;          // columns of Y: (h_q + h_k) d
+  int chunk_tokens;    // calibration tokens per partial Gram (whole load rounds)
   int chunks;          // token chunks of the partial Grams
   int s_tiles, h_tiles;  // 64 x 64 output tiles of one S_a and of H
   int items;           // partial Gram work items (one wave each)
@@ -61,7 +67,11 @@ MergeLayout merge_layout(const saga_merge_shape* s) {
   MergeLayout m{};
   const int d = s->d, hk = s->h_k;
   m.n_cols = (s->h_q + hk) * d;
-  m.chunks = (s->tokens + kGramChunk - 1) / kGramChunk;
+  // chunks of kGramChunk tokens (many short serial loops in parallel), longer ones
+  // past kGramMaxChunks chunks so that the partials stay a bounded multiple of the Grams
+  const int per = (s->tokens + kGramMaxChunks - 1) / kGramMaxChunks;
+  m.chunk_tokens = per > kGramChunk ? (per + kGramRound - 1) / kGramRound * kGramRound : kGramChunk;
+  m.chunks = (s->tokens + m.chunk_tokens - 1) / m.chunk_tokens;
   m.s_tiles = (d / kGramTile) * (d / kGramTile);
   m.h_tiles = (hk * d / kGramTile) * (hk * d / kGramTile);
   m.items = (hk * m.s_tiles + m.h_tiles) * m.chunks;
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void k_proj(const ProjArgs a) {
 
 // --- k_gram: partial Grams over one chunk of tokens ---------------------------------
 // Work item w (one wave): an output o (S_a for o < h_k, else H), a 64 x 64 tile of it
-// and a chunk of kGramChunk tokens. S_a tile (i, k) sums Y[t, jd + 64i + m] *
+// and a chunk of a.chunk_tokens tokens. S_a tile (i, k) sums Y[t, jd + 64i + m] *
 // Y[t, jd + 64k + n] over the chunk's tokens t and the query heads j of key head a;
 // H tile (i, k) sums Y[t, c0 + 64i + m] Y[t, c0 + 64k + n] with c0 = h_q d (the key
 // columns). fp32 MFMA 16x16x4 (lane l supplies row/column l & 15 at token l >> 4 of
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void k_proj(const ProjArgs a) {
 struct GramArgs {
   const float* y;
   float* part;     // [items, 64, 64]
-  int T, n_cols, h_q, h_k, d, chunks, s_tiles, h_tiles, items;
+  int T, n_cols, h_q, h_k, d, chunks, s_tiles, h_tiles, items, chunk_tokens;
 };
 
 __global__ __launch_bounds__(kBlock) void k_gram(const GramArgs a) {
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(kBlock) void k_gram(const GramArgs a) {
     head_stride = 0;
   }
   const int ti = tile / tiles_per_row, tk = tile - ti * tiles_per_row;
-  const int t_lo = chunk * kGramChunk, t_hi = min(t_lo + kGramChunk, a.T);
+  const int t_lo = chunk * a.chunk_tokens, t_hi = min(t_lo + a.chunk_tokens, a.T);
   floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -202,10 +212,10 @@ __global__ __launch_bounds__(kBlock) void k_gram(const GramArgs a) {
   for (int h = 0; h < heads; ++h) {
     const float* ya = a.y + col_base + h * head_stride + ti * kGramTile + r16;
     const float* yb = a.y + col_base + h * head_stride + tk * kGramTile + r16;
-    for (int t0 = t_lo; t0 < t_hi; t0 += 16) {
-      float va[4][4], vb[4][4];  // [token step][subtile]
+    for (int t0 = t_lo; t0 < t_hi; t0 += kGramRound) {
+      float va[kGramSteps][4], vb[kGramSteps][4];  // [token step][subtile]
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kGramSteps; ++u) {
         const int t = t0 + 4 * u + kq;
         const bool ok = t < t_hi;
         const size_t row = (size_t)min(t, a.T - 1) * a.n_cols;
@@ -216,7 +226,7 @@ __global__ __launch_bounds__(kBlock) void k_gram(const GramArgs a) {
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kGramSteps; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -655,6 +665,7 @@ saga_status saga_merge_losses(const saga_merge_shape* s, const void* x, const vo
   g.h_k = s->h_k;
   g.d = s->d;
   g.chunks = m.chunks;
+  g.chunk_tokens = m.chunk_tokens;
   g.s_tiles = m.s_tiles;
   g.h_tiles = m.h_tiles;
   g.items = m.items;

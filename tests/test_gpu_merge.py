@@ -134,3 +134,29 @@ def test_merge_d128_four_heads_planted():
     twins = [(0, 3), (1, 2)]
     pairs, ref = check_merge(300, 768, 8, 4, 128, seed=42, twins=twins)
     assert pairs == sorted(twins)
+
+
+def test_many_calibration_tokens_scale_the_losses():
+    # past 16384 calibration tokens the partial Grams take longer token chunks. A
+    # property that holds at any size: repeating every calibration token once
+    # doubles the queries and keys, so every logit matrix appears four times, every
+    # loss of eq. (13) is 4x the loss of the original tokens, and the merged
+    # projections of eq. (15) (a ratio of Grams) are unchanged.
+    T, D, h_q, h_k, d = 9000, 256, 8, 4, 64
+    inp = wl.merge_inputs(T, D, h_q, h_k, d, seed=7)
+    x = inp.x.to(DEV)
+    x2 = torch.cat([x, x], dim=0)          # 18000 tokens
+    wq, wk = inp.w_q.to(DEV), inp.w_k.to(DEV)
+    say(f"T={T} and its doubled set {2 * T}")
+    l1, ws1 = api.merge_losses(x, wq, wk, h_q=h_q, h_k=h_k)
+    l2, ws2 = api.merge_losses(x2, wq, wk, h_q=h_q, h_k=h_k)
+    a, b = l1.double().cpu().numpy(), l2.double().cpu().numpy()
+    off = ~np.eye(h_k, dtype=bool)
+    assert np.all(np.abs(b[off] - 4 * a[off]) <= 1e-4 * 4 * a[off])
+    partner = list(api.min_weight_pairing(l1.cpu())[0])
+    assert list(api.min_weight_pairing(l2.cpu())[0]) == partner
+    m1 = api.merge_keys(x, wq, wk, partner, h_q=h_q, h_k=h_k, workspace=ws1)
+    m2 = api.merge_keys(x2, wq, wk, partner, h_q=h_q, h_k=h_k, workspace=ws2)
+    torch.cuda.synchronize()
+    m1, m2 = m1.double().cpu().numpy(), m2.double().cpu().numpy()
+    assert np.abs(m2 - m1).max() <= 1e-5 * np.abs(m1).max()
