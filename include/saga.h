@@ -46,7 +46,8 @@ typedef enum saga_status {
   SAGA_OK = 0,
   SAGA_ERR_NULL = 1,        /* a required pointer is NULL */
   SAGA_ERR_SHAPE = 2,       /* inconsistent sizes: heads not divisible, N < 1, period < 1, ... */
-  SAGA_ERR_UNSUPPORTED = 3, /* valid but not built: (d, d_v) not built, unknown dtype, too long */
+  SAGA_ERR_UNSUPPORTED = 3, /* valid but not built: (d, d_v) not built, unknown dtype, too long,
+                               too many (sequence, head) rows */
   SAGA_ERR_WORKSPACE = 4,   /* workspace smaller than saga_workspace_bytes() */
   SAGA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
 } saga_status;
@@ -56,8 +57,8 @@ typedef enum saga_dtype { SAGA_F32 = 0, SAGA_BF16 = 1 } saga_dtype;
 /* Head counts and sizes, named as on the pages (section "Attention Mechanism
  * Formalization": h heads of dimension d; section "SAGA Architecture": h_k, h_v). */
 typedef struct saga_shape {
-  int32_t batch;      /* B >= 1 sequences, one decode token each */
-  int32_t h_q;        /* query heads; multiple of h_k and of h_v */
+  int32_t batch;      /* B >= 1 sequences, one decode token each; B <= 65535 */
+  int32_t h_q;        /* query heads; multiple of h_k and of h_v; h_q <= 65535, B h_q <= 2^24 */
   int32_t h_k;        /* key heads */
   int32_t h_v;        /* value heads */
   int32_t d;          /* head dimension of q and K (d_k): 32, 64 or 128, see d_v */
@@ -65,7 +66,7 @@ typedef struct saga_shape {
                        * and the reduced key dimensions (d, d_v) = (32, 64), and (64, 128)
                        * for bf16 (section "Training from Scratch": a key head dimension
                        * below the value head dimension). The logit scale is 1/sqrt(d). */
-  int32_t l_max;      /* cache capacity: row stride (in tokens) of K and V */
+  int32_t l_max;      /* cache capacity: row stride (in tokens) of K and V; at most 2^24 */
   int32_t dtype;      /* saga_dtype of q, K and V */
   int32_t out_dtype;  /* saga_dtype of out (bf16 output is rounded to nearest even) */
   float scale;        /* logit scale; 0 selects 1/sqrt(d) as in eq. (2) */

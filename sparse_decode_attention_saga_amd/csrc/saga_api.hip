@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kMaxContext = 1 << 24;   // longest supported l_kv
 constexpr int kMaxWaveKeyBytes = 32768;  // keys one wave of a streaming kernel has in flight
+constexpr long long kMaxRows = 1 << 24;  // most (sequence, query head) rows of one call
 
 // Runs the statement with P = the page flag as a compile-time constant.
 #define SAGA_PAGED(FLAG, ...)          \
@@ -139,6 +140,8 @@ saga_status check_shape(const saga_shape* s) {
   const bool reduced = (s->d == 32 && dv == 64) || (s->d == 64 && dv == 128 && s->dtype == SAGA_BF16);
   if (!same && !reduced) return SAGA_ERR_UNSUPPORTED;
   if (s->batch > 65535 || s->h_q > 65535 || s->l_max > kMaxContext) return SAGA_ERR_UNSUPPORTED;
+  // rows (sequence, query head) are indexed with 32-bit integers in the kernels
+  if ((long long)s->batch * s->h_q > kMaxRows) return SAGA_ERR_UNSUPPORTED;
   return SAGA_OK;
 }
 

@@ -111,6 +111,9 @@ def test_decode_rejects_bad_arguments(lib):
     assert decode(lib, shape(d=96)) == api.ERR_UNSUPPORTED
     assert decode(lib, shape(dtype=7)) == api.ERR_UNSUPPORTED
     assert decode(lib, shape(out_dtype=2)) == api.ERR_UNSUPPORTED
+    # more (sequence, query head) rows than the kernels index: refused before any work
+    assert decode(lib, shape(batch=65535, h_q=512, h_k=1, h_v=1)) == api.ERR_UNSUPPORTED
+    assert lib.saga_workspace_bytes(ctypes.byref(shape(batch=65535, h_q=512, h_k=1, h_v=1)), 8, 1024) == 0
     assert decode(lib, shape(), ws_bytes=1024) == api.ERR_WORKSPACE
 
 
