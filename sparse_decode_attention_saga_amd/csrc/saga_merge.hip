@@ -298,8 +298,9 @@ __device__ double block_sum_f64(double v, double* red) {
 
 // C[M x N] = X[M x K] Y[K x N] in fp64, all row-major in global memory, by every
 // thread of the block: 64 x 64 output tiles, each thread a 4 x 4 register tile, K
-// staged through LDS in slices of 16 (`lds`: 64 * 17 + 16 * 64 doubles). M and N
-// are multiples of 64, K of 16.
+// staged through LDS in slices of 16 (`lds`: 64 * 17 + 16 * 64 doubles), the next
+// slice's loads in flight while the current one is multiplied. M and N are multiples
+// of 64, K of 16.
 constexpr int kGemmLds = 64 * 17 + 16 * 64;
 
 __device__ void block_gemm_f64(double* C, int ldc, const double* X, int ldx, const double* Y, int ldy, int M, int N,
@@ -314,14 +315,18 @@ __device__ void block_gemm_f64(double* C, int ldc, const double* X, int ldx, con
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-      for (int k0 = 0; k0 < K; k0 += 16) {
-        double xv[4], yv[4];
+      // the next K slice is loaded into registers while the current one is used
+      double xv[4], yv[4];
+      auto load = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = u * kBlock + tid;
           xv[u] = X[(size_t)(mt + e / 16) * ldx + k0 + e % 16];
           yv[u] = Y[(size_t)(k0 + e / 64) * ldy + nt + e % 64];
         }
+      };
+      load(0);
+      for (int k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = u * kBlock + tid;
@@ -329,6 +334,7 @@ __device__ void block_gemm_f64(double* C, int ldc, const double* X, int ldx, con
           ys[e] = yv[u];
         }
         __syncthreads();
+        if (k0 + 16 < K) load(k0 + 16);
 #pragma unroll 4
         for (int kk = 0; kk < 16; ++kk) {
           double xr[4], yr[4];
