@@ -3,15 +3,23 @@
 
 One step = one saga_decode_attn call (one layer, one decode token) on the
 Qwen2.5-1.5B-shaped workload at 128K context, batch 1 (h_q=12, h_k=1, h_v=4, d=128,
-N=512, exact threshold every 32 steps), bf16 inputs, seeded synthetic data. Refresh
-steps occur at their natural rate (one in refresh_period) inside the timed region.
+N=512, exact threshold every 32 steps), bf16 inputs, seeded synthetic data.
+
+The exact threshold refresh is part of the method's cost: one step in every n
+(n = refresh_period) recomputes it. Two graphs of exactly K steps each are timed:
+K steps that reuse the threshold (t_steady per step) and K steps that each refresh
+it (t_refresh per step). The reported step time is the amortized one,
+t_step = ((n - 1) t_steady + t_refresh) / n, whatever K is. A third graph of K
+consecutive steps starting at a multiple of n (refreshes at their natural rate,
+ceil(K / n) of them) is timed as a cross-check and reported beside it.
 
 Inputs are resident in HBM before timing. R rotating copies of q/K/V/tau (R*bytes(K)
 >= 1 GiB, R coprime with the refresh period) keep the 256 MB Infinity Cache from
 serving repeated reads, as a model's per-layer caches would. Timed steps are
 replayed from a HIP graph and timed with HIP events on the launch stream.
 
-Prints one JSON line. `value` = SAGA decode steps/s (refresh steps included).
+Prints one JSON line. `value` = SAGA decode steps/s = 1 / t_step (refresh cost
+amortized as above).
 `roofline` is for the dominant kernel, the select kernel of a step that reuses the
 threshold (saga_select_gather: K stream, comparison, value gather): a graph of K
 launches of it alone is timed with HIP events on its stream; its algorithmic bytes
@@ -33,6 +41,7 @@ import math
 import os
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -100,9 +109,9 @@ def pct(xs, p):
     return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
 
-def cpu_baseline(w, x, seconds: float):
+def cpu_baseline(w, x, seconds: float, one_thread_seconds: Optional[float] = None):
     """The oracle as it stands, on the same inputs, for about `seconds` of host time
-    with every host core, then for a fifth of that on one thread."""
+    with every host core, then (default: a fifth of that) on one thread."""
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import saga_oracle as orc
 
@@ -130,7 +139,7 @@ def cpu_baseline(w, x, seconds: float):
     except OSError:
         pass
     with threadpool_limits(limits=1):
-        steps1, el1 = run(seconds / 5)
+        steps1, el1 = run(seconds / 5 if one_thread_seconds is None else one_thread_seconds)
     return {"value": steps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()},
             "sample": f"{steps} consecutive oracle decode steps (steps 0..{steps - 1}, exact threshold at "
@@ -138,6 +147,28 @@ def cpu_baseline(w, x, seconds: float):
                       f"float64 numpy, BLAS threads = cores",
             "single_thread": {"value": steps1 / el1, "unit": "steps/s", "cores": 1,
                               "sample": f"{steps1} steps, {el1:.1f} s, BLAS limited to one thread"}}
+
+
+def cpu_baselines(args) -> int:
+    """The CPU oracle timed on this host, with every core and on one thread, for the
+    tiny fp32 case, the Llama- and Qwen-shaped layers and both ends of the sweep's
+    context range (4K and 128K keys): one JSON line. Bounded: about
+    --cpu-seconds with every core and a third of that on one thread per workload."""
+    from sparse_decode_attention_saga_amd import workloads as wl
+
+    cases = [(wl.TINY, None), (wl.LLAMA_32K, None), (wl.QWEN_128K, None),
+             (wl.SWEEP, wl.SWEEP_L[0]), (wl.SWEEP, wl.SWEEP_L[-1])]
+    rows = []
+    for w, L in cases:
+        x = wl.generate(w, seed=0) if L is None else wl.generate(w, seed=0, lengths=[L], l_max=L)
+        name = w.name if L is None else f"{w.name} at l_kv={L}"
+        r = cpu_baseline(w, x, args.cpu_seconds, args.cpu_seconds / 3)
+        log(f"cpu oracle {name}: {r['value']:.1f} steps/s on {r['cores']} threads, "
+            f"{r['single_thread']['value']:.1f} steps/s on one")
+        rows.append({"workload": name, "l_kv": int(x.l_kv.max()), "N": w.N, "refresh_period": w.refresh_period,
+                     "dtype": w.dtype, **r})
+    print(json.dumps({"cpu_baselines": rows}), flush=True)
+    return 0
 
 
 def copy_probe(torch, reps: int) -> int:
@@ -585,12 +616,16 @@ def paged_timing(torch, api, w, qs, ks, vs, taus, l_kv, L, args) -> list:
         for t in range(W):
             step(t, w.refresh_period)
         torch.cuda.synchronize()
-        ms = time_graph(torch, lambda: [step(t, w.refresh_period) for t in range(W, W + K)], args.reps)
-        us = pct([1e3 * m / K for m in ms], 50)
+        n = w.refresh_period
         ms = time_graph(torch, lambda: [step(1 + t, 1 << 30) for t in range(W, W + K)], args.reps)
         us_steady = pct([1e3 * m / K for m in ms], 50)
-        log(f"paged ({P}-token pages): {us:.2f} us/step, steady {us_steady:.2f} us/step")
-        out.append({"page_tokens": P, "us_per_step": us, "us_steady_step": us_steady})
+        ms = time_graph(torch, lambda: [step(t, 1) for t in range(W, W + K)], args.reps)
+        us_refresh = pct([1e3 * m / K for m in ms], 50)
+        us = ((n - 1) * us_steady + us_refresh) / n
+        log(f"paged ({P}-token pages): {us:.2f} us/step amortized (steady {us_steady:.2f}, refresh "
+            f"{us_refresh:.2f} us/step)")
+        out.append({"page_tokens": P, "us_per_step": us, "us_steady_step": us_steady,
+                    "us_refresh_step": us_refresh})
         del sets
     return out
 
@@ -624,10 +659,10 @@ def layer_timing(torch, api, wl, w, ks, vs, L, args) -> dict:
         desc = api.layer_desc(xs[0], kset[0], vset[0], w.h_q, bf)
         lws = api.LayerWorkspace(desc, w.N, L, dev)
 
-        def step(t):
+        def step(t, period=w.refresh_period):
             r = t % n
             api.decode_layer(xs[r], wq[r], wo[r], kset[r], vset[r], l_kv, l_next, h_q=w.h_q, attention=mode,
-                             N=w.N, refresh_period=w.refresh_period, step=t, tau=taus[r], max_l_kv=L, out=y,
+                             N=w.N, refresh_period=period, step=t, tau=taus[r], max_l_kv=L, out=y,
                              workspace=lws)
 
         def proj(t):
@@ -642,8 +677,14 @@ def layer_timing(torch, api, wl, w, ks, vs, L, args) -> dict:
         for t in range(W):
             step(t)
         torch.cuda.synchronize()
-        ms = time_graph(torch, lambda: [step(t) for t in range(W, W + K)], args.reps)
+        # steps that reuse the threshold, and (Atop-N) steps that refresh it, amortized
+        # over the refresh period as the attention step is
+        ms = time_graph(torch, lambda: [step(1 + t, 1 << 30) for t in range(W, W + K)], args.reps)
         us = pct([1e3 * m / K for m in ms], 50)
+        if mode == api.ATTN_ATOPN:
+            p = w.refresh_period
+            ms = time_graph(torch, lambda: [step(t, 1) for t in range(W, W + K)], args.reps)
+            us = ((p - 1) * us + pct([1e3 * m / K for m in ms], 50)) / p
         ms = time_graph(torch, lambda: [proj(t) for t in range(W, W + K)], args.reps)
         us_proj = pct([1e3 * m / K for m in ms], 50)
         wbytes = (wq[0].numel() + wo[0].numel()) * 2
@@ -688,7 +729,8 @@ def main() -> int:
     ap.add_argument("--paged", type=int, nargs="*", default=[16, 256], metavar="P",
                     help="also time the step over paged caches with P-token pages (none: skip)")
     ap.add_argument("--no-layer", action="store_true", help="skip the decode-layer timing")
-    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady", "paged", "layer"], default="all",
+    ap.add_argument("--only", choices=["all", "saga", "dense", "select", "steady", "refresh", "paged", "layer"],
+                    default="all",
                     help="time only one part (for profiler runs)")
     ap.add_argument("--probe", choices=["none", "copy", "read"], default="none",
                     help="copy: a plain device copy of 256 MiB (counter calibration); read: read ceilings")
@@ -702,12 +744,17 @@ def main() -> int:
                     help="calibration token counts of --merge")
     ap.add_argument("--stages", action="store_true",
                     help="time the stages of the step as separate launches (key stream, value gather, combine)")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="time the CPU oracle (all cores, one thread) on the tiny, Llama- and Qwen-shaped "
+                         "workloads and the sweep's 4K and 128K ends (one JSON line)")
     ap.add_argument("--decompose", action="store_true",
                     help="dense and Atop-N steps with grouped-query and with SAGA heads (one JSON line)")
     args = ap.parse_args()
 
     if args.rocprof_summary:
         return rocprof_summary(args.rocprof_summary)
+    if args.cpu_baselines:
+        return cpu_baselines(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -784,20 +831,43 @@ def main() -> int:
         r = t % R
         api.split_combine(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, max_l_kv=L, out=out, workspace=ws)
 
+    def refresh_step(t):
+        r = t % R
+        api.decode_attn(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, refresh_period=1, step=t,
+                        max_l_kv=L, out=out, workspace=ws)
+
     K, W = args.steps, args.warmup
+    n = w.refresh_period
     res = {}
     if args.only in ("all", "saga"):
         for t in range(W):
             saga_step(t)
         torch.cuda.synchronize()
-        ms = time_graph(torch, lambda: [saga_step(t) for t in range(W, W + K)], args.reps)
-        res["saga_us"] = [1e3 * m / K for m in ms]
-        res["refresh_steps"] = sum(1 for t in range(W, W + K) if t % w.refresh_period == 0)
-        log(f"saga: {pct(res['saga_us'], 50):.2f} us/step over {K} steps ({res['refresh_steps']} refresh)")
-    if args.only in ("all", "steady"):
+        # K steps that reuse the threshold and K steps that each refresh it
+        ms = time_graph(torch, lambda: [steady_step(t) for t in range(W, W + K)], args.reps)
+        steady = [1e3 * m / K for m in ms]
+        ms = time_graph(torch, lambda: [refresh_step(t) for t in range(W, W + K)], args.reps)
+        refresh = [1e3 * m / K for m in ms]
+        res["steady_us"] = pct(steady, 50)
+        res["refresh_us"] = pct(refresh, 50)
+        # amortized step per replay pair: (n - 1) steady steps and one refresh step
+        res["saga_us"] = [((n - 1) * a + b) / n for a, b in zip(sorted(steady), sorted(refresh))]
+        log(f"steady step (threshold reused): {res['steady_us']:.2f} us/step; refresh step: "
+            f"{res['refresh_us']:.2f} us/step; amortized over n={n}: {pct(res['saga_us'], 50):.2f} us/step")
+        # cross-check: K consecutive steps from a multiple of n, refreshes at their natural rate
+        t0 = -(-W // n) * n
+        ms = time_graph(torch, lambda: [saga_step(t) for t in range(t0, t0 + K)], args.reps)
+        res["natural_us"] = pct([1e3 * m / K for m in ms], 50)
+        res["refresh_steps"] = sum(1 for t in range(t0, t0 + K) if t % n == 0)
+        log(f"natural rate: {res['natural_us']:.2f} us/step over {K} steps ({res['refresh_steps']} refresh)")
+    if args.only == "steady":
         ms = time_graph(torch, lambda: [steady_step(t) for t in range(W, W + K)], args.reps)
         res["steady_us"] = pct([1e3 * m / K for m in ms], 50)
         log(f"steady step (threshold reused): {res['steady_us']:.2f} us/step")
+    if args.only == "refresh":
+        ms = time_graph(torch, lambda: [refresh_step(t) for t in range(W, W + K)], args.reps)
+        res["refresh_us"] = pct([1e3 * m / K for m in ms], 50)
+        log(f"refresh step: {res['refresh_us']:.2f} us/step")
     if args.only in ("all", "select"):
         ms = time_graph(torch, lambda: [select_only(t) for t in range(W, W + K)], args.reps)
         res["select_us"] = pct([1e3 * m / K for m in ms], 50)
@@ -907,6 +977,9 @@ def main() -> int:
         "us_per_step_p10": pct(res["saga_us"], 10),
         "us_per_step_p90": pct(res["saga_us"], 90),
         "us_steady_step": res.get("steady_us"),
+        "us_refresh_step": res.get("refresh_us"),
+        "step_time": "((n-1) * us_steady_step + us_refresh_step) / n, n = refresh_period",
+        "us_per_step_natural_rate": res.get("natural_us"),
         "us_select_kernel": res.get("select_us"),
         "us_combine_kernel": res.get("combine_us"),
         "bytes_per_step": bytes_step,
@@ -915,7 +988,7 @@ def main() -> int:
         "bytes_selected_v_per_query_head": bytes_v_per_head,
         "step_gbs": step_gbs,
         "step_roofline_frac": step_gbs / HBM_PEAK_GBS,
-        "refresh_steps_timed": res["refresh_steps"],
+        "refresh_steps_timed_natural_rate": res["refresh_steps"],
         "survivors_mean": float(counts.mean()),
         "survivors_max": int(counts.max()),
         "forced_refresh_rows": forced,

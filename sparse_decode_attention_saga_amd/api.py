@@ -200,6 +200,8 @@ def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale, d_v=0, need_out=T
         _dev(tau, "tau", torch.float32)
         if tau.numel() != shape.batch * shape.h_q:
             raise ValueError("tau must be [B, h_q]")
+    if l_kv.device != q.device or (tau is not None and tau.device != q.device):
+        raise ValueError("every tensor of a call must be on one device")
     if max_l_kv is None:
         max_l_kv = shape.l_max
     out_shape = (shape.batch, shape.h_q, value_dim(shape))
@@ -212,6 +214,24 @@ def _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale, d_v=0, need_out=T
         if tuple(out.shape) != out_shape or dtype_code(out.dtype) != shape.out_dtype:
             raise ValueError("out must be [B, h_q, d_v] in the output dtype")
     return shape, int(max_l_kv), out
+
+
+def _row_outputs(B: int, h_q: int, sel_count, sel_idx, flags) -> int:
+    """Checks the optional per-(sequence, query head) outputs: sel_count and flags
+    [B, h_q] int32, sel_idx [B, h_q, cap] int32. Returns cap (0 without sel_idx).
+    The kernels write B*h_q counts and flags and cap indices per row, so a smaller
+    tensor is refused here rather than written past its end."""
+    for name, t in (("sel_count", sel_count), ("flags", flags)):
+        if t is not None:
+            _dev(t, name, torch.int32)
+            if t.numel() != B * h_q:
+                raise ValueError(f"{name} must be [B, h_q] = [{B}, {h_q}]")
+    if sel_idx is None:
+        return 0
+    _dev(sel_idx, "sel_idx", torch.int32)
+    if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (B, h_q) or sel_idx.shape[2] < 1:
+        raise ValueError(f"sel_idx must be [B, h_q, cap] = [{B}, {h_q}, cap >= 1]")
+    return int(sel_idx.shape[2])
 
 
 def _ws(ws: Optional[Workspace], shape, N, max_l_kv, device):
@@ -227,10 +247,7 @@ def decode_attn(q, k, v, l_kv, tau, *, N: int, refresh_period: int, step: int,
     """saga_decode_attn: one SAGA + Atop-N decode step. `tau` [B, h_q] float32 is
     read and updated in place. Returns `out`."""
     shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
-    for name, t in (("sel_count", sel_count), ("sel_idx", sel_idx), ("flags", flags)):
-        if t is not None:
-            _dev(t, name, torch.int32)
-    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    cap = _row_outputs(shape.batch, shape.h_q, sel_count, sel_idx, flags)
     ws = _ws(workspace, shape, N, max_l_kv, q.device)
     st = lib().saga_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
                                 int(refresh_period), int(step), _ptr(tau), _ptr(out), _ptr(sel_count),
@@ -268,7 +285,7 @@ def sparse_gather(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
                   scale: float = 0.0, stream=None):
     """saga_sparse_gather: softmax and value gather over what saga_qk_select kept."""
     shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
-    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    cap = _row_outputs(shape.batch, shape.h_q, sel_count, sel_idx, flags)
     ws = _ws(workspace, shape, N, max_l_kv, q.device)
     st = lib().saga_sparse_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
                                   _ptr(tau), _ptr(out), _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags),
@@ -293,7 +310,7 @@ def split_combine(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
                   scale: float = 0.0, stream=None):
     """saga_split_combine: merges the chunk parts left by saga_select_gather into `out`."""
     shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
-    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    cap = _row_outputs(shape.batch, shape.h_q, sel_count, sel_idx, flags)
     ws = _ws(workspace, shape, N, max_l_kv, q.device)
     st = lib().saga_split_combine(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
                                   _ptr(tau), _ptr(out), _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags),
@@ -360,10 +377,7 @@ def decode_attn_paged(q, k_pages, v_pages, table, l_kv, tau, *, N: int, refresh_
     tokens found through `table`). Returns `out`."""
     shape, pages, max_l_kv, out = _prep_paged(q, k_pages, v_pages, table, l_kv, tau, out, out_dtype, max_l_kv,
                                               scale)
-    for name, t in (("sel_count", sel_count), ("sel_idx", sel_idx), ("flags", flags)):
-        if t is not None:
-            _dev(t, name, torch.int32)
-    cap = 0 if sel_idx is None else sel_idx.shape[-1]
+    cap = _row_outputs(shape.batch, shape.h_q, sel_count, sel_idx, flags)
     ws = _ws(workspace, shape, N, max_l_kv, q.device)
     st = lib().saga_decode_attn_paged(ctypes.byref(shape), ctypes.byref(pages), _ptr(q), _ptr(k_pages),
                                       _ptr(v_pages), _ptr(l_kv), max_l_kv, int(N), int(refresh_period), int(step),
@@ -431,8 +445,14 @@ def qkv_append(x, w_qkv, k_cache, v_cache, l_kv, l_kv_next, *, h_q: int, q=None,
     L = layer_desc(x, k_cache, v_cache, h_q)
     if tuple(w_qkv.shape) != ((h_q + L.attn.h_k + L.attn.h_v) * L.attn.d, L.d_model):
         raise ValueError("w_qkv must be [(h_q + h_k + h_v) * d, d_model]")
+    if l_kv.numel() != x.shape[0] or l_kv_next.numel() != x.shape[0]:
+        raise ValueError("l_kv and l_kv_next need one entry per sequence")
     if q is None:
         q = torch.empty(x.shape[0], h_q, L.attn.d, dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(q, "q", torch.bfloat16)
+        if tuple(q.shape) != (x.shape[0], h_q, L.attn.d):
+            raise ValueError("q must be [B, h_q, d]")
     st = lib().saga_qkv_append(ctypes.byref(L), _ptr(x), _ptr(w_qkv), _ptr(k_cache), _ptr(v_cache), _ptr(l_kv),
                                _ptr(l_kv_next), _ptr(q), _stream(x.device, stream))
     _check(st, "saga_qkv_append")
@@ -468,17 +488,24 @@ def decode_layer(x, w_qkv, w_o, k_cache, v_cache, l_kv, l_kv_next, *, h_q: int, 
         raise ValueError("w_qkv must be [(h_q + h_k + h_v) * d, d_model]")
     if tuple(w_o.shape) != (L.d_model, h_q * L.attn.d):
         raise ValueError("w_o must be [d_model, h_q * d]")
+    B = x.shape[0]
+    if l_kv.numel() != B or l_kv_next.numel() != B:
+        raise ValueError("l_kv and l_kv_next need one entry per sequence")
+    if attention == ATTN_ATOPN and tau is None:
+        raise ValueError("the Atop-N layer needs the threshold state tau [B, h_q]")
     if tau is not None:
         _dev(tau, "tau", torch.float32)
-    for name, t in (("sel_count", sel_count), ("flags", flags)):
-        if t is not None:
-            _dev(t, name, torch.int32)
+        if tau.numel() != B * h_q:
+            raise ValueError("tau must be [B, h_q]")
+    _row_outputs(B, h_q, sel_count, None, flags)
     if max_l_kv is None:
         max_l_kv = L.attn.l_max
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or torch.bfloat16, device=x.device)
     else:
         _dev(out, "out")
+        if tuple(out.shape) != tuple(x.shape) or dtype_code(out.dtype) != L.attn.out_dtype:
+            raise ValueError("out must be [B, d_model] in the output dtype")
     n = N if attention == ATTN_ATOPN else 1
     ws = workspace or LayerWorkspace(L, n, max_l_kv, x.device)
     st = lib().saga_decode_layer(ctypes.byref(L), int(attention), _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(k_cache),
@@ -556,6 +583,8 @@ def merge_keys(x, w_q, w_k, partner, *, h_q: int, h_k: int, workspace: MergeWork
         out = torch.empty(h_k // 2 * shape.d, shape.d_model, dtype=torch.float32, device=w_k.device)
     else:
         _dev(out, "out", torch.float32)
+        if tuple(out.shape) != (h_k // 2 * shape.d, shape.d_model):
+            raise ValueError("out must be [h_k/2 * d, d_model]")
     st = lib().saga_merge_keys(ctypes.byref(shape), _ptr(w_k), part, _ptr(out), _ptr(workspace.buf),
                                workspace.nbytes, _stream(w_k.device, stream))
     _check(st, "saga_merge_keys")

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libsaga.so")
 SOURCES = [os.path.join(HERE, "csrc", n) for n in ("saga_api.hip", "saga_layer.hip", "saga_merge.hip")]
 # the decode-attention kernels' sources (what a build of those kernels depends on;
 # the layer's projection kernels are not among them)
-LIB_FILES = [os.path.join(HERE, "csrc", n) for n in ("saga_api.hip", "saga_device.cuh", "saga_kernels.cuh")] + \
+LIB_FILES = [os.path.join(HERE, "csrc", n) for n in ("saga_api.hip", "saga_device.hpp", "saga_kernels.hpp")] + \
     [os.path.join(ROOT, "include", "saga.h")]
 # streaming-read probe used by the benchmark (not part of the decode library)
 PROBE_PATH = os.path.join(HERE, "libsaga_probe.so")

@@ -5,7 +5,7 @@
 #include <cmath>
 #include <cstddef>
 
-#include "saga_kernels.cuh"
+#include "saga_kernels.hpp"
 
 using namespace saga;
 

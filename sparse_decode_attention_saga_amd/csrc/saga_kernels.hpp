@@ -17,7 +17,7 @@
 // Architecture" (h_k key heads, h_v value heads).
 #pragma once
 
-#include "saga_device.cuh"
+#include "saga_device.hpp"
 
 namespace saga {
 

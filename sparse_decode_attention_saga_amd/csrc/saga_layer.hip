@@ -16,7 +16,7 @@
 
 #include <cstddef>
 
-#include "saga_device.cuh"
+#include "saga_device.hpp"
 
 using namespace saga;
 

@@ -32,7 +32,7 @@
 #include <cstddef>
 #include <vector>
 
-#include "saga_device.cuh"
+#include "saga_device.hpp"
 
 using namespace saga;
 

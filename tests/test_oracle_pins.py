@@ -175,6 +175,53 @@ def test_refresh_equals_bruteforce_topn(N):
                 assert len(want) == N
 
 
+# Key head of each of 8 query heads, written out per key-head count (contiguous
+# groups of h_q / h_k query heads, as in grouped-query attention).
+KEY_HEAD_OF_8 = {1: [0] * 8, 2: [0, 0, 0, 0, 1, 1, 1, 1], 4: [0, 0, 1, 1, 2, 2, 3, 3]}
+
+
+@pytest.mark.parametrize("h_k", [1, 2, 4])
+@pytest.mark.parametrize("scale", [None, 0.3])
+def test_refresh_threshold_equals_bruteforce_sort(h_k, scale):
+    # The exact threshold of a refresh step (section "Top-N Attention", eq. (6); the
+    # Atop-N threshold is the N-th largest logit of the row): pure-Python logits of
+    # each row against its key head, then the N-th entry of a full descending sort,
+    # counting repeats. Rows cover an empty sequence (no threshold: NaN), N >= l_kv
+    # (-inf: everything kept), N = l_kv - 1, and keys repeated to force ties.
+    h_q, d, L_max = 8, 6, 24
+    rng = np.random.default_rng(40 + h_k)
+    q = rng.standard_normal((4, h_q, d))
+    K = rng.standard_normal((4, h_k, L_max, d))
+    K[:, :, 5] = K[:, :, 2]           # repeated keys: tied logits around the threshold
+    K[:, :, 9] = K[:, :, 2]
+    lens = np.array([24, 0, 7, 13])
+    s = (1.0 / math.sqrt(d)) if scale is None else scale
+    for N in (1, 3, 6, 7, 12, 30):
+        got = orc.refresh_threshold(q, K, lens, N, scale=scale)
+        for b in range(4):
+            L = int(lens[b])
+            for j in range(h_q):
+                g = KEY_HEAD_OF_8[h_k][j]
+                if L == 0:
+                    assert math.isnan(got[b, j])
+                    continue
+                scores = [sum(float(q[b, j, c]) * float(K[b, g, i, c]) for c in range(d)) * s for i in range(L)]
+                want = -math.inf if N >= L else sorted(scores, reverse=True)[N - 1]
+                if want == -math.inf:
+                    assert got[b, j] == -math.inf, (b, j, N)
+                else:
+                    assert math.isclose(got[b, j], want, rel_tol=1e-12, abs_tol=1e-14), (b, j, N)
+    # the tie: with N = 2 or 3 the three repeated keys of a row whose repeated key is
+    # the largest give one threshold value, that key's logit
+    Kt = K.copy()
+    Kt[0, :, 2] = 50.0 * np.sign(q[0, 0]) / math.sqrt(d)   # largest logit of head 0's key head
+    Kt[0, :, 5] = Kt[0, :, 2]
+    Kt[0, :, 9] = Kt[0, :, 2]
+    top = sum(float(q[0, 0, c]) * float(Kt[0, 0, 2, c]) for c in range(d)) * s
+    for N in (1, 2, 3):
+        assert math.isclose(orc.refresh_threshold(q, Kt, lens, N, scale=scale)[0, 0], top, rel_tol=1e-12)
+
+
 def test_nth_largest_matches_partition_with_repeats():
     rng = np.random.default_rng(5)
     for _ in range(200):
