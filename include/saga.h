@@ -111,6 +111,32 @@ saga_status saga_decode_attn(const saga_shape* s, const void* q, const void* k, 
                              int32_t* flags, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): saga_decode_attn with its workspace
+ * in a scratch array inside the library instead of a caller's buffer. Arguments,
+ * results and errors are those of saga_decode_attn, plus:
+ *   - Scratch: SAGA_NOALLOC_SCRATCH_BYTES of device memory per GPU, set up by the HIP
+ *     runtime when the library's code is loaded on that GPU and held until the process
+ *     ends. The call uses the copy of the current device (hipGetDevice); `stream` must
+ *     belong to that device. The first call on a device looks up the copy's address
+ *     (SAGA_ERR_HIP if that fails); nothing is ever allocated or freed (no hipMalloc,
+ *     no hipFree, no allocating library call).
+ *   - SAGA_ERR_WORKSPACE when the step needs more than the scratch holds, i.e. when
+ *     saga_workspace_bytes(s, N, max_l_kv) > SAGA_NOALLOC_SCRATCH_BYTES (one sequence
+ *     of 128K tokens with 12 query heads of 128 needs about 25 MiB; a batch of 16
+ *     such sequences does not fit). Checked before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *     contents: calls that overlap on one GPU (concurrent streams, or host threads
+ *     enqueueing at once) race and give undefined results; order them on one stream.
+ *     A refresh step first clears the scratch's threshold counters with a fill kernel
+ *     (one extra launch, no memset node), so no earlier contents are relied on. */
+#define SAGA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+saga_status saga_decode_attn_noalloc(const saga_shape* s, const void* q, const void* k, const void* v,
+                                     const int32_t* l_kv, int32_t max_l_kv, int32_t N,
+                                     int32_t refresh_period, int64_t step, float* tau, void* out,
+                                     int32_t* sel_count, int32_t* sel_idx, int32_t sel_cap,
+                                     int32_t* flags, void* stream);
+
 /* The exact threshold alone (section "Methodology > Atop-N Attention", refresh step):
  * tau[b,j] = N-th largest fp32 logit of row (b,j), counting repeats; -inf when
  * N >= l_kv[b]; unchanged when l_kv[b] == 0. */

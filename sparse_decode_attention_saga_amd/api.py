@@ -20,7 +20,9 @@ EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "sa
            "saga_refresh_threshold", "saga_dense_gqa_attn", "saga_qk_select", "saga_sparse_gather",
            "saga_select_gather", "saga_split_combine", "saga_decode_attn_paged", "saga_dense_gqa_attn_paged",
            "saga_linear", "saga_qkv_append", "saga_layer_workspace_bytes", "saga_decode_layer",
-           "saga_merge_workspace_bytes", "saga_merge_losses", "saga_min_weight_pairing", "saga_merge_keys")
+           "saga_merge_workspace_bytes", "saga_merge_losses", "saga_min_weight_pairing", "saga_merge_keys",
+           "saga_decode_attn_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SAGA_NOALLOC_SCRATCH_BYTES of include/saga.h
 ATTN_ATOPN, ATTN_DENSE = 0, 1
 FLAG_REFRESHED, FLAG_FORCED = 1, 2
 
@@ -63,6 +65,7 @@ _SIGS = {
     "saga_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "saga_workspace_init": (_I32, [_P, _SZ, _P]),
     "saga_decode_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_decode_attn_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P]),
     "saga_refresh_threshold": (_I32, [_P, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "saga_dense_gqa_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_qk_select": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
@@ -254,6 +257,23 @@ def decode_attn(q, k, v, l_kv, tau, *, N: int, refresh_period: int, step: int,
                                 _ptr(sel_idx), cap, _ptr(flags), _ptr(ws.buf), ws.nbytes,
                                 _stream(q.device, stream))
     _check(st, "saga_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(q, k, v, l_kv, tau, *, N: int, refresh_period: int, step: int,
+                        max_l_kv: Optional[int] = None, out=None, sel_count=None, sel_idx=None, flags=None,
+                        scale: float = 0.0, stream=None):
+    """saga_decode_attn_noalloc: decode_attn with the library's own per-GPU scratch
+    instead of a workspace (nothing is allocated by the library). `out` must be given,
+    so that the call allocates nothing here either. Returns `out`."""
+    if out is None:
+        raise ValueError("decode_attn_noalloc needs a preallocated out [B, h_q, d_v]")
+    shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, None, max_l_kv, scale)
+    cap = _row_outputs(shape.batch, shape.h_q, sel_count, sel_idx, flags)
+    st = lib().saga_decode_attn_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv,
+                                        int(N), int(refresh_period), int(step), _ptr(tau), _ptr(out),
+                                        _ptr(sel_count), _ptr(sel_idx), cap, _ptr(flags), _stream(q.device, stream))
+    _check(st, "saga_decode_attn_noalloc")
     return out
 
 

@@ -4,10 +4,19 @@
 
 #include <cmath>
 #include <cstddef>
+#include <mutex>
 
 #include "saga_kernels.hpp"
 
 using namespace saga;
+
+// Scratch of saga_decode_attn_noalloc: the decode step's workspace for callers that
+// cannot allocate. One copy per GPU, set up by the runtime when the library's code
+// is loaded on that GPU and held until the process ends. Host code never passes
+// this name to a kernel or a copy: on the host it is only a stand-in for the
+// symbol; the device address of a GPU's copy comes from hipGetSymbolAddress
+// (noalloc_scratch below) and only that address is used.
+static __device__ __align__(256) uint8_t scratch[SAGA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -364,6 +373,24 @@ saga_status decode_impl(const saga_shape* s, const saga_pages* pg, const void* q
   return launched();
 }
 
+// Device address of the current GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept; null if the lookup fails.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 saga_status dense_impl(const saga_shape* s, const saga_pages* pg, const void* q, const void* k, const void* v,
                        const int32_t* l_kv, int32_t max_l_kv, void* out, void* workspace, size_t workspace_bytes,
                        void* stream) {
@@ -465,6 +492,32 @@ saga_status saga_decode_attn_paged(const saga_shape* s, const saga_pages* pages,
   if (st != SAGA_OK) return st;
   return decode_impl(s, pages, q, k_pages, v_pages, l_kv, max_l_kv, N, refresh_period, step, tau, out, sel_count,
                      sel_idx, sel_cap, flags, workspace, workspace_bytes, stream);
+}
+
+saga_status saga_decode_attn_noalloc(const saga_shape* s, const void* q, const void* k, const void* v,
+                                     const int32_t* l_kv, int32_t max_l_kv, int32_t N, int32_t refresh_period,
+                                     int64_t step, float* tau, void* out, int32_t* sel_count, int32_t* sel_idx,
+                                     int32_t sel_cap, int32_t* flags, void* stream) {
+  // every argument check of saga_decode_attn, before the scratch is touched
+  if (!s || !q || !k || !v || !l_kv || !tau || !out) return SAGA_ERR_NULL;
+  saga_status st = check_shape(s);
+  if (st != SAGA_OK) return st;
+  if (max_l_kv < 0 || max_l_kv > s->l_max || N < 1) return SAGA_ERR_SHAPE;
+  if (refresh_period < 1 || step < 0 || (sel_idx && sel_cap < 1)) return SAGA_ERR_SHAPE;
+  const Layout w = layout(s, max_l_kv);
+  if (w.total > (size_t)SAGA_NOALLOC_SCRATCH_BYTES) return SAGA_ERR_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return SAGA_ERR_HIP;
+  const hipStream_t hs = (hipStream_t)stream;
+  (void)hipGetLastError();
+  // The threshold counters must be zero when a refresh starts. Every refresh leaves
+  // them at zero, but the scratch is shared by every call on this GPU and its first
+  // contents are not the library's, so each refresh step clears them first (a fill
+  // kernel, which a graph capture records as an ordinary kernel node).
+  if (max_l_kv > 0 && step % refresh_period == 0)
+    hipLaunchKernelGGL(k_zero_fill, dim3(32), dim3(kBlock), 0, hs, reinterpret_cast<uint8_t*>(ws), w.scores);
+  return decode_impl(s, nullptr, q, k, v, l_kv, max_l_kv, N, refresh_period, step, tau, out, sel_count, sel_idx,
+                     sel_cap, flags, ws, (size_t)SAGA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const void* k, const int32_t* l_kv,

@@ -95,6 +95,33 @@ def decode(lib, s, N=8, period=4, step=1, ws_bytes=1 << 40, max_l=1024, tau=FAKE
                                 period, step, tau, FAKE, None, sel_idx, cap, None, FAKE, ws_bytes, None)
 
 
+def decode_noalloc(lib, s, N=8, period=4, step=1, max_l=1024, tau=FAKE, sel_idx=None, cap=0):
+    return lib.saga_decode_attn_noalloc(None if s is None else ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, max_l, N,
+                                        period, step, tau, FAKE, None, sel_idx, cap, None, None)
+
+
+def test_noalloc_rejects_bad_arguments_before_touching_the_gpu(lib):
+    # the same checks as saga_decode_attn, and a step that needs more scratch than
+    # SAGA_NOALLOC_SCRATCH_BYTES is refused with SAGA_ERR_WORKSPACE
+    assert decode_noalloc(lib, None) == api.ERR_NULL
+    assert decode_noalloc(lib, shape(), tau=None) == api.ERR_NULL
+    assert decode_noalloc(lib, shape(h_k=5)) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(batch=0)) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(), N=0) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(), period=0) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(), step=-1) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(), max_l=131073) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(), sel_idx=FAKE, cap=0) == api.ERR_SHAPE
+    assert decode_noalloc(lib, shape(d=96)) == api.ERR_UNSUPPORTED
+    big = shape(batch=4)
+    assert lib.saga_workspace_bytes(ctypes.byref(big), 512, 131072) > api.NOALLOC_SCRATCH_BYTES
+    assert decode_noalloc(lib, big, N=512, max_l=131072) == api.ERR_WORKSPACE
+    # the header's scratch size and the binding's agree
+    text = open(HEADER).read()
+    m = re.search(r"#define SAGA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == api.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_rejects_bad_arguments(lib):
     assert decode(lib, None) == api.ERR_NULL
     assert decode(lib, shape(), tau=None) == api.ERR_NULL
