@@ -248,7 +248,61 @@ def read_probe(torch, reps: int) -> dict:
     xs = np.array([m * 1048576.0 for m in by_size])
     ys = np.array([by_size[m] for m in by_size])
     slope, t0 = np.polyfit(xs, ys, 1)
+
+    # one 32 MiB read per launch (32 slices of the GiB, a graph of 32 launches) for
+    # 4, 8, 16 and 32 loads in flight per thread and 1 to 8 blocks per compute unit
+    fn_ex = lib.saga_probe_stream_read_ex
+    fn_ex.restype = ctypes.c_int
+    fn_ex.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                      ctypes.c_void_p, ctypes.c_void_p]
+    sink_ex = torch.zeros(65536, dtype=torch.float32, device="cuda:0")
+    S32 = n // 32
+
+    def launch_ex(off, blocks, loads, times=None):
+        st = fn_ex(x.data_ptr() + off, S32, sink_ex.data_ptr(), blocks, loads,
+                   None if times is None else times.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"saga_probe_stream_read_ex failed ({st})")
+
+    sweep = {}
+    for loads in (4, 8, 16, 32):
+        for blocks in (256, 512, 1024, 2048):
+            def run32():
+                for i in range(32):
+                    launch_ex(i * S32, blocks, loads)
+            run32()
+            torch.cuda.synchronize()
+            sweep[(loads, blocks)] = min(time_graph(torch, run32, reps)) / 32 * 1e3
+    best = min(sweep, key=sweep.get)
+
+    # timeline of the best configuration: per launch, the spread of block starts, the
+    # first load's arrival, the last block's end (s_memrealtime, 100 MHz), against the
+    # launch's share of the graph time
+    loads, blocks = best
+    times = [torch.zeros(3 * blocks, dtype=torch.int64, device="cuda:0") for _ in range(32)]
+
+    def run32_t():
+        for i in range(32):
+            launch_ex(i * S32, blocks, loads, times[i])
+    run32_t()
+    torch.cuda.synchronize()
+    us_launch = min(time_graph(torch, run32_t, reps)) / 32 * 1e3
+    tl = []
+    for t in times:
+        a = t.view(blocks, 3).cpu().numpy().astype(np.float64) * 1e-2  # ticks of 10 ns -> us
+        start = a[:, 0].min()
+        tl.append((a[:, 0].max() - start, np.median(a[:, 1] - a[:, 0]), (a[:, 1] - start).min(),
+                   a[:, 2].max() - start))
+    tl = np.median(np.array(tl), axis=0)
+    timeline = {"loads_per_thread": loads, "blocks": blocks, "us_per_launch_graph": us_launch,
+                "us_block_start_spread": float(tl[0]), "us_first_load_median": float(tl[1]),
+                "us_first_load_earliest": float(tl[2]), "us_first_to_last_instruction": float(tl[3]),
+                "us_outside_kernel_body": us_launch - float(tl[3])}
     return {"kernel": "k_stream_read (libsaga_probe.so)",
+            "mib32_sweep_us": {f"{l}x{b}": round(v, 3) for (l, b), v in sweep.items()},
+            "mib32_best": {"loads_per_thread": best[0], "blocks": best[1], "us": sweep[best],
+                           "gbs": S32 / (sweep[best] * 1e-6) / 1e9},
+            "mib32_timeline": timeline,
             "per_launch_us_by_mib": {str(m): round(v, 3) for m, v in by_size.items()},
             "fit_fixed_us": float(t0), "fit_stream_gbs": float(1e-3 / slope),
             "gib_read_gbs": table[best_big][0], "gib_blocks": best_big,

@@ -20,10 +20,12 @@
  *     out [B,h_q,d_v]; l_kv [B] int32; tau [B,h_q] float32. d is the query/key head
  *     dimension, d_v the value head dimension (saga_shape.d_v).
  *   - Cache rows read: rows >= max_l_kv are never read, and rows >= l_kv[b] never
- *     contribute to a result. With batch 1 the key loads of a decode step are issued
- *     before l_kv[0] is known, so key rows l_kv[0] .. max_l_kv - 1 may be read (and
- *     discarded); they lie inside the cache, since max_l_kv <= l_max. Value rows and,
- *     with batch > 1, key rows at or past l_kv[b] are never read.
+ *     contribute to a result. With batch 1 the loads of a call are issued before
+ *     l_kv[0] is known, so rows l_kv[0] .. max_l_kv - 1 may be read and discarded
+ *     (key rows by the decode calls, key and value rows by the dense calls); they lie
+ *     inside the caches, since max_l_kv <= l_max, and whatever they hold (even NaN)
+ *     never reaches a result. With batch > 1, rows at or past l_kv[b] are never read,
+ *     and the decode calls read value rows only for kept entries.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *     Results are valid once the stream reaches the call.
  *   - Arguments are checked on the host before anything is launched; on any error

@@ -158,7 +158,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int rows, W, ch, nch, P;  // W: tiles per wave of the stream kernels; P: threshold-candidate blocks per row
-  int nchd;                 // chunks of the dense kernels (their base chunk: 16 KiB of keys per wave)
+  int nchd;                 // chunks of the dense kernels (DenseCfg: 16 KiB of keys and values per wave)
   long long lpad;
   size_t hist, cand_cnt;
   size_t scores, surv_idx, surv_val, chunk_hdr, part, total;
@@ -171,7 +171,7 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   w.ch = 16 * w.W * kWaves;
   w.nch = max_l_kv > 0 ? (max_l_kv + w.ch - 1) / w.ch : 1;
   int chd = 0;
-  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), chd = StreamCfg<T, DK>::kChunk;);
+  SAGA_DISPATCH(s->dtype, s->d, value_dim(s), chd = (DenseCfg<T, DK, DV>::kChunk););
   w.nchd = max_l_kv > 0 ? (max_l_kv + chd - 1) / chd : 1;
   w.lpad = (long long)w.nch * w.ch;
   w.P = max_l_kv > 0 ? (max_l_kv + kSelSlice - 1) / kSelSlice : 1;
@@ -429,12 +429,22 @@ saga_status dense_impl(const saga_shape* s, const saga_pages* pg, const void* q,
   SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(pg != nullptr, {
     if (max_l_kv > 0) {
       const dim3 grid(w.nchd, s->h_v, s->batch);
-      if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 4, P>), grid, dim3(kBlock), 0, hs, a);
-      else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 8, P>), grid, dim3(kBlock), 0, hs, a);
-      else hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 16, P>), grid, dim3(kBlock), 0, hs, a);
+      constexpr int TD = DenseCfg<T, DK, DV>::kTPW;
+      // one sequence: its chunks reach max_l_kv, loads need not wait for l_kv
+      if (s->batch == 1) {
+        if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 4, P, TD, true>), grid, dim3(kBlock), 0, hs, a);
+        else if (g <= 6) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 6, P, TD, true>), grid, dim3(kBlock), 0, hs, a);
+        else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 8, P, TD, true>), grid, dim3(kBlock), 0, hs, a);
+        else hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 16, P, TD, true>), grid, dim3(kBlock), 0, hs, a);
+      } else {
+        if (g <= 4) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 4, P, TD, false>), grid, dim3(kBlock), 0, hs, a);
+        else if (g <= 6) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 6, P, TD, false>), grid, dim3(kBlock), 0, hs, a);
+        else if (g <= 8) hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 8, P, TD, false>), grid, dim3(kBlock), 0, hs, a);
+        else hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 16, P, TD, false>), grid, dim3(kBlock), 0, hs, a);
+      }
     }
     hipLaunchKernelGGL((k_dense_combine<DV>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
-                       (int)StreamCfg<T, DK>::kChunk);
+                       (int)DenseCfg<T, DK, DV>::kChunk);
   }););
   return launched();
 }

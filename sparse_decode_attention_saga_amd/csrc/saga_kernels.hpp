@@ -17,6 +17,8 @@
 // Architecture" (h_k key heads, h_v value heads).
 #pragma once
 
+#include <type_traits>
+
 #include "saga_device.hpp"
 
 namespace saga {
@@ -30,6 +32,20 @@ template <typename T, int D, int W = 0> struct StreamCfg {
   static constexpr int kBase = 16384 / (16 * kRowBytes) > 0 ? 16384 / (16 * kRowBytes) : 1;
   static constexpr int kTPW = W > 0 ? W : (kBase > 8 ? 8 : kBase);  // 16-key tiles per wave
   static_assert(kTPW >= 1 && kTPW <= 8, "one to eight tiles per wave");
+  static constexpr int kChunk = 16 * kTPW * kWaves;
+};
+
+// Keys per block of the dense kernel: 4 waves x TPW tiles x 16 keys, TPW the power of
+// two (1..8) that keeps a wave's key and value rows within 16 KiB, or 32 KiB where the
+// value products run on the matrix cores (bf16, d_v = 128; the VALU form needs the
+// registers for its sums); every load of a wave is in flight at once, in registers.
+// Measured at the Qwen-shaped 128K layer (h_kv = 2): 36.5 us with 16 KiB, 32.7 us with
+// 32 KiB per wave; the Llama-shaped 32K layer (h_kv = 8): 19.5 against 20.4 us.
+template <typename T, int DK, int DV> struct DenseCfg {
+  static constexpr int kBytes = 16 * (DK + DV) * (int)sizeof(T);  // one tile's keys and values
+  static constexpr int kBudget = std::is_same<T, bf16_t>::value && DV == 128 ? 32768 : 16384;
+  static constexpr int kFit = kBudget / kBytes;
+  static constexpr int kTPW = kFit >= 8 ? 8 : kFit >= 4 ? 4 : kFit >= 2 ? 2 : 1;
   static constexpr int kChunk = 16 * kTPW * kWaves;
 };
 
@@ -932,19 +948,33 @@ struct DenseArgs {
   int ptab_stride, page_shift, num_pages;     // paged caches (see StreamArgs)
 };
 
-// DK and DV are the key and value head dimensions.
-// grid = (nchd, h_v, B), block = 256. Each block takes one chunk of CHD keys and one
-// value head v: the logits of its g query heads against their key head (h_k divides
-// h_v, so the g heads share one; MFMA), the chunk's softmax numerator relative to the
-// chunk maximum, and its product with the chunk's rows of value head v (VALU). The
-// key tiles are loaded first; the value tiles follow in two halves (see below).
-template <typename T, int DK, int DV, int GH, bool PAGED>
+// DK and DV are the key and value head dimensions; TPW tiles of 16 keys per wave.
+// grid = (nchd, h_v, B), block = 256. Each block takes one chunk of 4 * 16 * TPW keys
+// and one value head v: the logits of its g query heads against their key head (h_k
+// divides h_v, so the g heads share one; MFMA), the chunk's softmax numerator
+// relative to the chunk maximum, and its product with the chunk's rows of value head
+// v (VALU, GH >= g heads). Every key and value load of a wave is issued at once, so a
+// block waits for one memory round trip. SPEC (one sequence): the loads are issued
+// before l_kv arrives, for rows up to max_l_kv - 1 (inside the caches); logits of rows
+// at or past l_kv are masked and their value registers zeroed before use.
+//
+// P.V on the matrix cores (bf16 caches, d_v = 128, an even number of tiles): lane
+// (x, kq) = (lane & 15, lane >> 4) loads row 16t + 4kq + r of tile t at columns
+// 8x .. 8x+7. The score tile leaves p(head x, key 16t + 4kq + r) in that same lane, so
+// over a pair of tiles a lane holds, for the same 8 keys, the 8 weights of head x and
+// 8 values of each of its 8 columns: exactly the K-slice of a 16x16x32 bf16 MFMA's A
+// operand (rows = heads) and, taking element i of each value load, of its B operand
+// (columns 8n + i for n = 0..15). The fp32 weights enter as three bf16 terms (each the
+// rounding of what the previous ones leave, so their sum is the weight to within 2^-24
+// of it); values are exact in bf16 and products accumulate in fp32.
+template <typename T, int DK, int DV, int GH, bool PAGED, int TPW, bool SPEC>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
-  constexpr int TPW = StreamCfg<T, DK>::kTPW;
-  constexpr int CHD = StreamCfg<T, DK>::kChunk;
+  constexpr bool kMfmaPV = std::is_same<T, bf16_t>::value && DV == 128 && TPW % 2 == 0;
+  constexpr int CHD = 16 * TPW * kWaves;
   constexpr int EPL = Unpack<T>::kN;
   constexpr int G = DV / EPL;                        // lanes per value row
   constexpr int VL = (16 * DV) / (EPL * kWave);      // 16-byte value loads per lane per tile
+  constexpr int KL = QK<T, DK>::kLoads;
   const T* const kbase = reinterpret_cast<const T*>(a.k);
   const T* const vbase = reinterpret_cast<const T*>(a.v);
   const T* const qbase = reinterpret_cast<const T*>(a.q);
@@ -953,16 +983,19 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   const int c = blockIdx.x, vg = blockIdx.y, b = blockIdx.z;
   const int kg = h_k == h_v ? vg : vg / (h_v / h_k);  // key head of this value head's query heads
-  const int L = min(a.l_kv[b], max_l_kv);
   const int base = c * CHD;
-  if (base >= L) return;
+  int L = max_l_kv;  // rows the loads may touch (SPEC), else the sequence's length
+  if constexpr (!SPEC) {
+    L = min(a.l_kv[b], max_l_kv);
+    if (base >= L) return;
+  }
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int hh = lane & 15, kq = lane >> 4;
   const int row0 = b * h_q + vg * gq;
 
-  __shared__ float s_p[kWaves][TPW][16][GH];
+  __shared__ float s_p[kMfmaPV ? 1 : kWaves][kMfmaPV ? 1 : TPW][16][GH];
   __shared__ float s_m[kWaves][GH], s_z[kWaves][GH];
-  __shared__ float s_o[kWaves][GH][DV];
+  __shared__ __align__(16) float s_o[kWaves][GH][DV];
 
   const CacheRows<T, DK, PAGED> kh(kbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, kg, h_k, l_max);
   const CacheRows<T, DV, PAGED> vh(vbase, a.ptab, a.ptab_stride, a.page_shift, a.num_pages, b, vg, h_v, l_max);
@@ -970,38 +1003,54 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
 
   QK<T, DK> qk;
   qk.load_q(qbase + (size_t)row0 * DK, gq, lane);
-  floatx4 sc[TPW];
-  score_tiles<T, DK, TPW>(sc, qk, kh, wbase, L, lane, scale);
-  // The value tiles are loaded once the key tiles are consumed, in two halves: the
-  // first half before the softmax, the second after the first half's products, so
-  // that key tiles, value tiles and the accumulators never all hold registers at
-  // once and four blocks fit on a compute unit. Load latency is covered by the
-  // softmax and by the other resident blocks.
-  constexpr int VH = TPW >= 2 ? 2 : 1;  // value-tile halves
-  constexpr int TPH = TPW / VH;         // tiles per half
-  // load r of tile t covers flat element (r*64 + lane) of the 16 x G grid
-  auto load_values = [&](uint4 (&vb)[TPH][VL], int t_first) {
+  // every key and value load of the wave, rows past L clamped to L - 1 (in bounds;
+  // their logits are masked); a clamped tile lies inside one page
+  uint4 kb[TPW][KL], vb[TPW][VL];
 #pragma unroll
-    for (int tt = 0; tt < TPH; ++tt) {
-      const int t = t_first + tt;
-      const int t0 = min(wbase + 16 * t, (L - 1) & ~15);  // a clamped tile lies inside one page
-      const T* vt = PAGED ? vh.tile(t0) : vh.row(0);
+  for (int t = 0; t < TPW; ++t) {
+    const int t0 = min(wbase + 16 * t, (L - 1) & ~15);
+    if constexpr (PAGED) {
+      const int key = min(t0 + (lane & 15), L - 1);
+      QK<T, DK>::load_k(kb[t], kh.tile(t0) + (size_t)(key - t0) * DK, lane);
+    } else {
+      QK<T, DK>::load_k(kb[t], kh.row(min(wbase + 16 * t + (lane & 15), L - 1)), lane);
+    }
+  }
+  // value row of load r of tile t (the MFMA form: row 4kq + r of the tile, columns
+  // 8 hh ..; the VALU form: flat element r*64 + lane of the tile's 16 x G grid)
+  auto vrow = [&](int t, int r) {
+    return wbase + 16 * t + (kMfmaPV ? 4 * kq + r : (r * kWave + lane) / G);
+  };
+  const int vcol = kMfmaPV ? 8 * hh : ((lane % G) * EPL);
 #pragma unroll
-      for (int r = 0; r < VL; ++r) {
-        const int e = r * kWave + lane;
-        if constexpr (PAGED) {
-          const int key = min(t0 + e / G, L - 1);
-          vb[tt][r] = ld16(vt + (size_t)(key - t0) * DV + (e % G) * EPL);
-        } else {
-          const int key = min(wbase + 16 * t + e / G, L - 1);
-          vb[tt][r] = ld16(vt + (size_t)key * DV + (e % G) * EPL);
-        }
+  for (int t = 0; t < TPW; ++t) {
+    const int t0 = min(wbase + 16 * t, (L - 1) & ~15);
+    const T* vt = PAGED ? vh.tile(t0) : vh.row(0);
+#pragma unroll
+    for (int r = 0; r < VL; ++r) {
+      if constexpr (PAGED) {
+        const int key = min(t0 + (vrow(t, r) - wbase - 16 * t), L - 1);
+        vb[t][r] = ld16(vt + (size_t)(key - t0) * DV + vcol);
+      } else {
+        const int key = min(vrow(t, r), L - 1);
+        vb[t][r] = ld16(vt + (size_t)key * DV + vcol);
       }
     }
-  };
+  }
+  // every load of the wave is issued before the first MFMA waits on one
   __builtin_amdgcn_sched_barrier(0);
-  uint4 vb[TPH][VL];
-  load_values(vb, 0);
+  if constexpr (SPEC) {
+    L = min(a.l_kv[b], max_l_kv);
+    if (base >= L) return;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < VL; ++r)
+        if (vrow(t, r) >= L) vb[t][r] = make_uint4(0, 0, 0, 0);
+  }
+  floatx4 sc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) sc[t] = qk.mma(kb[t]) * scale;
 
   float mh = -INFINITY;
 #pragma unroll
@@ -1020,13 +1069,65 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     for (int r = 0; r < 4; ++r) {
       const float p = (mh == -INFINITY) ? 0.f : expf(sc[t][r] - mh);
       zh += p;
-      if (hh < GH) s_p[wv][t][4 * kq + r][hh] = p;
+      if constexpr (kMfmaPV) sc[t][r] = p;  // the weights stay in the score registers
+      else if (hh < GH) s_p[wv][t][4 * kq + r][hh] = p;
     }
   zh = strided_lane_sum<16>(zh);
   if (lane < GH) {
     s_m[wv][lane] = mh;
     s_z[wv][lane] = zh;
   }
+
+  if constexpr (kMfmaPV) {
+    floatx4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tp = 0; tp < TPW; tp += 2) {
+      // element e of a K-slice: key 16 (tp + e/4) + 4kq + e%4
+      bf16x8 w1, w2, w3;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = sc[tp + e / 4][e % 4];
+        const __bf16 h1 = (__bf16)p;
+        const float r1 = p - (float)h1;
+        const __bf16 h2 = (__bf16)r1;
+        const float r2 = r1 - (float)h2;
+        w1[e] = h1;
+        w2[e] = h2;
+        w3[e] = (__bf16)r2;
+      }
+      const uint4* v0 = vb[tp];
+      const uint4* v1 = vb[tp + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // element i of each of the 8 value loads: word i/2, half i%2
+        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        auto word = [&](const uint4& u) {
+          return (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+        };
+        V16 bw;
+        bw.u.x = __builtin_amdgcn_perm(word(v0[1]), word(v0[0]), sel);
+        bw.u.y = __builtin_amdgcn_perm(word(v0[3]), word(v0[2]), sel);
+        bw.u.z = __builtin_amdgcn_perm(word(v1[1]), word(v1[0]), sel);
+        bw.u.w = __builtin_amdgcn_perm(word(v1[3]), word(v1[2]), sel);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, bw.h, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, bw.h, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, bw.h, acc[i], 0, 0, 0);
+      }
+    }
+    // lane (x, kq) holds the wave's sum for head 4kq + j, column 8x + i in acc[i][j]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * kq + j;
+      if (h < GH) {
+        *reinterpret_cast<float4*>(&s_o[wv][h][8 * hh]) = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+        *reinterpret_cast<float4*>(&s_o[wv][h][8 * hh + 4]) =
+            make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+      }
+    }
+    __syncthreads();
+  } else {
   __syncthreads();
 
   float o[GH][EPL];
@@ -1035,28 +1136,19 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
 #pragma unroll
-  for (int hv = 0; hv < VH; ++hv) {
-    if (hv > 0) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_values(vb, hv * TPH);
-    }
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int tt = 0; tt < TPH; ++tt)
+    for (int r = 0; r < VL; ++r) {
+      const int k16 = (r * kWave + lane) / G;
+      float x[EPL];
+      Unpack<T>::run(vb[t][r], x);
 #pragma unroll
-      for (int r = 0; r < VL; ++r) {
-        const int t = hv * TPH + tt;
-        const int e = r * kWave + lane;
-        const int k16 = e / G;
-        float x[EPL];
-        Unpack<T>::run(vb[tt][r], x);
+      for (int h = 0; h < GH; ++h) {
+        const float p = s_p[wv][t][k16][h];
 #pragma unroll
-        for (int h = 0; h < GH; ++h) {
-          const float p = s_p[wv][t][k16][h];
-#pragma unroll
-          for (int q = 0; q < EPL; ++q) o[h][q] += p * x[q];
-        }
+        for (int q = 0; q < EPL; ++q) o[h][q] += p * x[q];
       }
-  }
+    }
   // lanes with the same column group (lane % G) hold partial sums over different keys
 #pragma unroll
   for (int h = 0; h < GH; ++h)
@@ -1069,6 +1161,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
       for (int q = 0; q < EPL; ++q) s_o[wv][h][lane * EPL + q] = o[h][q];
   }
   __syncthreads();
+  }
 
   // merge the 4 waves (each relative to its own maximum) and write the chunk partial
   for (int idx = tid; idx < gq * (DV + 1); idx += kBlock) {
@@ -1092,17 +1185,36 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   }
 }
 
-// Log-sum-exp merge of the chunk partials of each row (b, j). Thread t takes chunks
-// t, t+256, ... and 16 columns (four 16-byte loads per chunk). D is the value head
-// dimension. grid = (D / 16, h_q, B), block = 256.
+// Log-sum-exp merge of the chunk partials of each row (b, j), in one pass: thread t
+// takes chunks t, t+256, ... and 16 columns, loads every one of its chunks' partials in
+// one round, keeps its own maximum m_t and its sums relative to it, then the block
+// rescales each thread's sums by exp(m_t - M) with M the row's maximum. D is the value
+// head dimension. grid = (D / 16, h_q, B), block = 256.
+constexpr int kDenseCombRegs = 4;  // chunks per thread whose partials are loaded together
+
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_dense_combine(const DenseArgs a, int chd) {
   const int cg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const long long row = (long long)b * a.h_q + j;
-  const int L = min(a.l_kv[b], a.max_l_kv);
+  const float* rp = a.part + row * a.nchd * (D + 4);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   __shared__ float s_ftmp[kWaves];
   __shared__ float s_acc[kWaves][17];
+  // the first round of loads is issued with l_kv (chunks past the length are not used)
+  float2 mz[kDenseCombRegs];
+  float4 x[kDenseCombRegs][4];
+#pragma unroll
+  for (int k = 0; k < kDenseCombRegs; ++k) {
+    const int c = tid + k * kBlock;
+    if (c < a.nchd) {
+      const float* pc = rp + (long long)c * (D + 4);
+      mz[k] = *reinterpret_cast<const float2*>(pc);
+      const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + cg * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[k][q] = p4[q];
+    }
+  }
+  const int L = min(a.l_kv[b], a.max_l_kv);
   if (L <= 0) {
     if (tid < 16) {
       if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[row * D + cg * 16 + tid] = 0;
@@ -1111,31 +1223,41 @@ __global__ __launch_bounds__(kBlock) void k_dense_combine(const DenseArgs a, int
     return;
   }
   const int nch_b = (L + chd - 1) / chd;
-  const float* rp = a.part + row * a.nchd * (D + 4);
   float m = -INFINITY;
-  for (int c = tid; c < nch_b; c += kBlock) m = fmaxf(m, rp[(long long)c * (D + 4)]);
-  const float M = block_max(m, s_ftmp);
+#pragma unroll
+  for (int k = 0; k < kDenseCombRegs; ++k)
+    if (tid + k * kBlock < nch_b) m = fmaxf(m, mz[k].x);
+  for (int c = tid + kDenseCombRegs * kBlock; c < nch_b; c += kBlock) m = fmaxf(m, rp[(long long)c * (D + 4)]);
   float o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
   float z = 0.f;
-  for (int c = tid; c < nch_b; c += kBlock) {
-    const float* pc = rp + (long long)c * (D + 4);
-    const float w = expf(pc[0] - M);
-    z += w * pc[1];
-    const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + cg * 16);
+  auto add = [&](float mc, float zc, const float4 (&xc)[4]) {
+    const float w = expf(mc - m);
+    z += w * zc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 x = p4[q];
-      o[4 * q] += w * x.x;
-      o[4 * q + 1] += w * x.y;
-      o[4 * q + 2] += w * x.z;
-      o[4 * q + 3] += w * x.w;
+      o[4 * q] += w * xc[q].x;
+      o[4 * q + 1] += w * xc[q].y;
+      o[4 * q + 2] += w * xc[q].z;
+      o[4 * q + 3] += w * xc[q].w;
     }
-  }
+  };
 #pragma unroll
-  for (int e = 0; e < 16; ++e) o[e] = wave_sum(o[e]);
-  z = wave_sum(z);
+  for (int k = 0; k < kDenseCombRegs; ++k)
+    if (tid + k * kBlock < nch_b) add(mz[k].x, mz[k].y, x[k]);
+  for (int c = tid + kDenseCombRegs * kBlock; c < nch_b; c += kBlock) {
+    const float* pc = rp + (long long)c * (D + 4);
+    const float4* p4 = reinterpret_cast<const float4*>(pc + 4 + cg * 16);
+    const float4 xc[4] = {p4[0], p4[1], p4[2], p4[3]};
+    add(pc[0], pc[1], xc);
+  }
+  // every chunk has at least one key, so a thread with chunks has a finite maximum
+  const float M = block_max(m, s_ftmp);
+  const float sc = m == -INFINITY ? 0.f : expf(m - M);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = wave_sum(o[e] * sc);
+  z = wave_sum(z * sc);
   if (lane == 0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s_acc[wv][e] = o[e];
@@ -1149,9 +1271,9 @@ __global__ __launch_bounds__(kBlock) void k_dense_combine(const DenseArgs a, int
       oo += s_acc[w][tid];
       zz += s_acc[w][16];
     }
-    const float x = oo / zz;
-    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[row * D + cg * 16 + tid] = f32_to_bf16(x);
-    else reinterpret_cast<float*>(a.out)[row * D + cg * 16 + tid] = x;
+    const float y = oo / zz;
+    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[row * D + cg * 16 + tid] = f32_to_bf16(y);
+    else reinterpret_cast<float*>(a.out)[row * D + cg * 16 + tid] = y;
   }
 }
 

@@ -9,10 +9,19 @@ Rules (tolerances fixed here, derived in the design notes):
   * kept index sets: equal except for indices whose oracle logit lies within
     1e-5 * s of either threshold (several selections are then correct);
   * outputs: normwise max|O_gpu - O_ref| / max|O_ref| <= 1e-5 (fp32 inputs) or 2e-3
-    (bf16 inputs), O_ref = the oracle's eq. (7) output on its own selection; when
-    the selections differ inside the band, the GPU's selection has been checked
-    valid above and O_ref is eq. (7) evaluated by the oracle on that selection.
-    A bf16 output adds the bf16 rounding of each element (2^-8 relative).
+    (bf16 inputs, the bar stated for bf16 caches), O_ref = the oracle's eq. (7)
+    output on its own selection; when the selections differ inside the band, the
+    GPU's selection has been checked valid above and O_ref is eq. (7) evaluated by
+    the oracle on that selection. A bf16 output adds the bf16 rounding of each
+    element (unit roundoff 2^-8 relative);
+  * and, for every input type, the bound the arithmetic gives, DERIVED = 1e-5
+    normwise: bf16 and fp32 inputs are exact in fp32 and in the oracle's float64,
+    bf16 x bf16 products are exact in fp32, so the only errors are the fp32
+    roundings of the d-term logit sums (each about sqrt(d) 2^-24 of the sum of
+    |q_c K_ic|, a few 1e-7 of a logit here), of exp (a few ulp), and of the sums
+    of up to |S| weighted value rows and weights (about sqrt(|S|) 2^-24 relative);
+    their effect on a softmax-weighted mean stays below 1e-5 of the row's largest
+    output. A bf16 output adds its rounding as above.
 """
 from __future__ import annotations
 
@@ -25,8 +34,17 @@ from sparse_decode_attention_saga_amd import api
 BAND = 1e-5
 
 
+DERIVED = 1e-5
+
+
 def out_tol(dtype: str) -> float:
+    """The stated bar: 1e-5 for fp32 inputs, 2e-3 for bf16 caches."""
     return 1e-5 if dtype == "f32" else 2e-3
+
+
+def out_bound(dtype: str) -> float:
+    """The bar asserted: the stated one and the arithmetic's DERIVED, whichever is tighter."""
+    return min(out_tol(dtype), DERIVED)
 
 
 class GpuCase:
@@ -93,7 +111,7 @@ def compare(gpu: dict, ref: "orc.DecodeResult", x, dtype: str, check_tau: bool, 
     q64, k64, v64 = x.f64()
     B, h_q, _ = q64.shape
     h_v = v64.shape[1]
-    tol = out_tol(dtype)
+    tol = out_bound(dtype)
     band_rows = 0
     for b in range(B):
         for j in range(h_q):
@@ -134,13 +152,14 @@ def compare(gpu: dict, ref: "orc.DecodeResult", x, dtype: str, check_tau: bool, 
             scale = np.abs(o_ref).max()
             err = np.abs(gpu["O"][b, j] - o_ref)
             if out_bf16:
-                assert np.all(err <= tol * scale + 2.0 ** -8 * np.abs(o_ref)), f"{where} bf16 out err {err.max()}"
+                assert np.all(err <= tol * scale + 2.0 ** -8 * np.abs(o_ref) * (1 + tol)), \
+                    f"{where} bf16 out err {err.max()}"
             else:
                 assert err.max() <= tol * scale, f"{where} out rel err {err.max() / scale:.3e} > {tol}"
     return band_rows
 
 
-def check_sampled_rows(x, N: int, rows, gots, dtype: str):
+def check_sampled_rows(x, N: int, rows, gots, dtype: str, out_bf16: bool = False):
     """The rules above, row by row, for a sample of (sequence, head) rows of inputs too
     large for a whole-batch fp64 oracle. Every result in `gots` (steps that share one
     exact threshold per row: a refresh step and steps reusing its threshold) is
@@ -165,5 +184,9 @@ def check_sampled_rows(x, N: int, rows, gots, dtype: str):
             sel = np.array(sorted(s_g))
             V_sel = x.v[b, vg][torch.from_numpy(sel)].double().numpy()
             o_ref, _ = orc.sparse_softmax_pv(a[sel], V_sel)
-            err = np.abs(got["O"][b, j] - o_ref).max() / np.abs(o_ref).max()
-            assert err <= out_tol(dtype), (b, j, err)
+            err = np.abs(got["O"][b, j] - o_ref)
+            tol = out_bound(dtype) * np.abs(o_ref).max()
+            if out_bf16:
+                assert np.all(err <= tol + 2.0 ** -8 * np.abs(o_ref) * (1 + out_bound(dtype))), (b, j, err.max())
+            else:
+                assert err.max() <= tol, (b, j, err.max() / np.abs(o_ref).max())

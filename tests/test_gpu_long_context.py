@@ -13,7 +13,7 @@ import torch
 from oracle import saga_oracle as orc
 from sparse_decode_attention_saga_amd import api
 from sparse_decode_attention_saga_amd import workloads as wl
-from tests.parity import GpuCase, check_sampled_rows
+from tests.parity import DERIVED, GpuCase, check_sampled_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -60,5 +60,5 @@ def test_dense_1m_keys(inputs):
                 continue
             a = orc.attention_logits(x.q[0, j].double().numpy(), K, scale)
             ref, _ = orc.sparse_softmax_pv(a, V)
-            assert np.abs(got[0, j] - ref).max() <= 2e-3 * np.abs(ref).max(), j
+            assert np.abs(got[0, j] - ref).max() <= DERIVED * np.abs(ref).max(), j
         del V

@@ -10,7 +10,7 @@ import torch
 from oracle import saga_oracle as orc
 from sparse_decode_attention_saga_amd import api
 from sparse_decode_attention_saga_amd import workloads as wl
-from tests.parity import GpuCase, check_sampled_rows, compare
+from tests.parity import DERIVED, GpuCase, check_sampled_rows, compare, out_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -266,7 +266,7 @@ def test_ties_keep_every_equal_logit():
     v = x.v.double().numpy()
     for j in range(4):
         mean = v[0, j // 2, :600].mean(axis=0)
-        assert np.abs(got["O"][0, j] - mean).max() <= 2e-3 * np.abs(mean).max()
+        assert np.abs(got["O"][0, j] - mean).max() <= DERIVED * np.abs(mean).max()
 
 
 def test_zero_query_keeps_every_key():
@@ -281,7 +281,7 @@ def test_zero_query_keeps_every_key():
     compare(got, ref, x, "bf16", check_tau=True)
     assert got["tau"][1, 3] == 0 and got["count"][1, 3] == 1500
     mean = x.v[1, 3 // 2, :1500].double().numpy().mean(axis=0)
-    assert np.abs(got["O"][1, 3] - mean).max() <= 2e-3 * np.abs(mean).max()
+    assert np.abs(got["O"][1, 3] - mean).max() <= DERIVED * np.abs(mean).max()
     got1 = g.step(4, 1)                           # the stale zero threshold keeps them again
     assert got1["count"][1, 3] == 1500 and got1["flags"][1, 3] == 0
 
@@ -315,7 +315,7 @@ def test_given_logit_scale(scale):
     got_d = dense.double().cpu().numpy()
     for b in range(2):
         for j in range(12):
-            assert np.abs(got_d[b, j] - ref_d[b, j]).max() <= 2e-3 * np.abs(ref_d[b, j]).max(), (b, j)
+            assert np.abs(got_d[b, j] - ref_d[b, j]).max() <= DERIVED * np.abs(ref_d[b, j]).max(), (b, j)
 
 
 def test_kept_index_export_capacity():
@@ -398,7 +398,7 @@ def test_dense_gqa(case):
     q64, k64, v64 = x.f64()
     ref = orc.dense_gqa(q64, k64, v64, x.l_kv)
     got = out.double().cpu().numpy()
-    tol = 1e-5 if dtype == "f32" else 2e-3
+    tol = out_bound(dtype)
     for b in range(B):
         if x.l_kv[b] == 0:
             assert np.all(got[b] == 0)
@@ -437,3 +437,30 @@ def test_dense_gqa_full_size(name):
     got = out.double().cpu().numpy()
     err = np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)
     assert err.max() <= 2e-3, err.max()
+
+
+@pytest.mark.parametrize("case", [
+    # B, h_q, h_k, h_v, d, lens, N (a long row with about one kept entry per chunk; a
+    # short row whose heads are split over several blocks per chunk; fp32 caches)
+    (1, 12, 1, 4, 128, [65536], 256, "bf16"),
+    (1, 12, 1, 4, 128, [4096], 2048, "bf16"),
+    (2, 8, 2, 4, 64, [3000, 1234], 100, "f32"),
+])
+@pytest.mark.skip(reason="needs fixed slots for kept entries; the wavefront-ballot compaction that gave them "
+                         "faulted the GPU on its first run with no cause found, so it is not built")
+def test_repeated_steps_are_bitwise_identical(case):
+    # kept entries take fixed slots (wavefront ballots) and every sum runs in a fixed
+    # order, so the same step on the same inputs gives the same bits every time
+    B, h_q, h_k, h_v, d, lens, N, dtype = case
+    w, x = small(B, h_q, h_k, h_v, d, lens, dtype, seed=50)
+    g = GpuCase(x, N)
+    runs = []
+    for _ in range(3):
+        r0 = g.step(8, 0)
+        r1 = g.step(8, 3)
+        runs.append((r0, r1))
+    for r0, r1 in runs[1:]:
+        for got, ref in ((r0, runs[0][0]), (r1, runs[0][1])):
+            for key in ("O", "tau", "count", "idx", "flags"):
+                assert np.array_equal(got[key], ref[key]), key
+    compare(runs[0][0], oracle_step(x, N, 8, 0), x, dtype, check_tau=True)

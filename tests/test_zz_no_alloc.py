@@ -6,9 +6,10 @@ Two inputs in a row on one GPU, the second smaller than the first, each with a
 refresh step and a step that reuses the threshold, so the second call runs on
 scratch that still holds the first call's contents. Thresholds, kept counts, flags
 and kept index sets must be identical (the same kernels on the same inputs, the
-threshold select is exact); outputs within 1e-5 of the row's largest output (fp32
-outputs; the only difference is the order of fp32 sums inside a chunk). The first
-input is also checked against the CPU oracle with the bar of the parity tests.
+threshold select is exact); outputs within 1e-6 of the row's largest output (fp32
+outputs; kept entries of a chunk take their slots in the order the lanes reach
+them, so the order of the fp32 sums inside a chunk can differ). The first input is
+also checked against the CPU oracle with the bar of the parity tests.
 """
 import numpy as np
 import pytest
@@ -58,7 +59,7 @@ def run_pair(w, steps):
         assert torch.equal(torch.sort(ref.idx, dim=-1).values, torch.sort(na.idx, dim=-1).values), t
         o_ref, o_na = ref.out.double(), na.out.double()
         err = ((o_ref - o_na).abs().amax(dim=-1) / o_ref.abs().amax(dim=-1)).max().item()
-        assert err <= 1e-5, (t, err)
+        assert err <= 1e-6, (t, err)
         results.append((x, t, na.out.double().cpu().numpy(), na.tau.double().cpu().numpy(),
                         na.count.cpu().numpy(), na.flags.cpu().numpy()))
     return results
@@ -75,7 +76,7 @@ def test_noalloc_matches_workspace_entry_point_twice_second_smaller():
     s = np.maximum(np.abs(r.tau), 1.0)
     assert np.all(np.abs(tau - r.tau) <= 1e-5 * s)
     err = (np.abs(out - r.O).max(axis=-1) / np.abs(r.O).max(axis=-1)).max()
-    assert err <= 2e-3, err  # bf16 caches
+    assert err <= 1e-5, err  # exact bf16 inputs, fp32 arithmetic and outputs
     assert np.all(flags == 1)
     # both inputs: every row kept at least N entries at its refresh step
     for res, w in ((first, FIRST), (second, SECOND)):
