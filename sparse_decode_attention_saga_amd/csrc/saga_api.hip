@@ -184,7 +184,7 @@ Layout layout(const saga_shape* s, int max_l_kv) {
   };
   // counters first: they must be zero before the first call and every call leaves them at zero
   w.hist = take((size_t)kHistCopies * rows * 256 * 4);
-  w.cand_cnt = take(rows * 4);
+  w.cand_cnt = take(rows * (size_t)w.P * 4);
   // sized for every chunk width (the narrowest chunks have the most records; lpad is at
   // most max_l_kv rounded up to the widest chunk), so that the size only grows with
   // max_l_kv whatever width a launch takes
@@ -267,6 +267,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.chunk_hdr = at<ChunkHdr>(ws, w.chunk_hdr);
   a.hist = at<unsigned>(ws, w.hist);
   a.cand_cnt = at<unsigned>(ws, w.cand_cnt);
+  a.nsel = w.P;
   a.h_q = s->h_q;
   a.h_k = s->h_k;
   a.g_k = s->h_q / s->h_k;

@@ -76,13 +76,14 @@ struct StreamArgs {
   ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
   float* part;             // [B*h_q, DV/16, nch, 16] chunk records: sum w*v, 16 columns per slice
   unsigned* hist;          // [8, B*h_q, 256] top-digit histogram copies (zero between calls)
-  unsigned* cand_cnt;      // [B*h_q] candidates of the threshold select (zero between calls)
+  unsigned* cand_cnt;      // [B*h_q, nsel] threshold candidates of each slice of kSelSlice logits
   const int32_t* ptab;     // paged caches: [B, ptab_stride] page ids (the kernels' PAGED form)
   long long lpad;
   int h_q, h_k, h_v, g_k, g_v, htiles, l_max, nch, N;  // g_k = h_q/h_k, g_v = h_q/h_v
   int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   int hsplit;              // blocks sharing one chunk in k_qk_select (heads split among them)
   float scale;
+  int nsel;                // slices of kSelSlice logits per row (the candidate pass's blocks)
   int ptab_stride, page_shift;  // paged caches: page table row stride, log2(tokens per page)
   int num_pages;           // paged caches: pages per pool (page ids are clamped below it)
 };
@@ -491,8 +492,10 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
 // ----------------------------------------------------------------------------
 // Refresh, pass 2: candidates for the exact threshold. The sum of the row's
 // histogram copies gives the 8-bit bin that holds its N-th largest logit; each block
-// copies the logits of its slice that fall in that bin to the row's candidate list
-// (stored in the row's kept-logit buffer, free at this point of a refresh step).
+// copies the logits of its slice that fall in that bin to the slice's own segment of
+// the row's kept-logit buffer (free at this point of a refresh step; a slice's
+// candidates fit in the slice's kSelSlice places) and their number to
+// cand_cnt[row, slice]. No block waits on another and there are no device atomics.
 // grid = (P, h_q, B) with P = ceil(max_l_kv / kSelSlice), block = 256.
 constexpr int kSelSlice = 4096;   // logits scanned per block
 constexpr int kCandLds = 8192;    // candidates the finishing block stages in LDS
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
   __shared__ int s_itmp[kWaves];
   __shared__ unsigned s_res[2];
   __shared__ float s_cand[kSelSlice];
-  __shared__ int s_cc, s_base;
+  __shared__ int s_cc;
 
   // the slice's logits are loaded with the histogram, before the bin is known
   const int hi = min(lo + kSelSlice, L);
@@ -551,17 +554,22 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
   }
   __syncthreads();
   const int cnt = s_cc;
-  if (tid == 0 && cnt > 0) s_base = (int)atomicAdd(&a.cand_cnt[row], (unsigned)cnt);
-  __syncthreads();
-  for (int i = tid; i < cnt; i += kBlock) a.surv_val[rbase + s_base + i] = s_cand[i];
+  if (tid == 0) a.cand_cnt[row * a.nsel + p] = (unsigned)cnt;
+  for (int i = tid; i < cnt; i += kBlock) a.surv_val[rbase + lo + i] = s_cand[i];
 }
 
 // Refresh, pass 3: the remaining 24 bits of the N-th largest logit resolved on the
-// candidates (counting repeats); writes tau (-inf when N >= l_kv, unchanged when
-// l_kv == 0) and returns the row's histogram copies and candidate count to zero.
-// grid = (h_q, B), block = 1024.
+// candidates (counting repeats). The slices' candidate counts give each slice's
+// place in the row's candidate list (a block scan); every candidate is then loaded
+// in one round (each index finds its slice by a binary search of the places) into
+// LDS, or, past kCandLds candidates, into the row's kept-index buffer. Writes tau
+// (-inf when N >= l_kv, unchanged when l_kv == 0) and returns the row's histogram
+// copies to zero. grid = (h_q, B), block = 1024.
+constexpr int kMaxSel = 4096;  // slices of a row of the longest supported context
+
 __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs a, float* tau_out) {
   constexpr int NT = kRowThreads;
+  constexpr int PER = kMaxSel / NT;
   const int j = blockIdx.x, b = blockIdx.y;
   const long long rows = (long long)gridDim.y * a.h_q;
   const long long row = (long long)b * a.h_q + j;
@@ -574,42 +582,77 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
   __shared__ int s_itmp[NT / kWave];
   __shared__ unsigned s_res[2];
   __shared__ float s_cand[kCandLds];
+  __shared__ int s_off[kMaxSel + 1];
 
-  const unsigned C = a.cand_cnt[row];
+  const int nsl = (L + kSelSlice - 1) / kSelSlice;  // slices holding candidates
+  int c[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int sl = tid * PER + u;
+    c[u] = (N < L && sl < nsl) ? (int)a.cand_cnt[row * a.nsel + sl] : 0;
+  }
   if (tid < 256) s_hist[tid] = hist_sum(a.hist, rows, row, tid, true);
   if (N >= L) {
     if (tid == 0) tau_out[row] = -INFINITY;
     return;
   }
+  // places of the slices in the candidate list: thread t holds slices t*PER ..
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) mine += c[u];
+  int C;
+  int off = block_excl_scan<NT>(mine, s_itmp, C);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int sl = tid * PER + u;
+    if (sl < nsl) s_off[sl] = off;
+    off += c[u];
+  }
+  if (tid == 0) s_off[nsl] = C;
   __syncthreads();
   digit_of_kth_largest<NT>(s_hist, (unsigned)N, s_itmp, s_res);
   const unsigned d1 = s_res[0], k1 = s_res[1];
-  const float* cand = a.surv_val + row * a.lpad;
-  if (C <= (unsigned)kCandLds) {
-    for (int i0 = 0; i0 < (int)C; i0 += 4 * NT) {
-      float t4[4];
+  const float* seg = a.surv_val + row * a.lpad;
+  float* gcand = reinterpret_cast<float*>(a.surv_idx) + row * a.lpad;  // free at this point
+  // where candidate i lies: the slice sl with s_off[sl] <= i < s_off[sl + 1]
+  auto where = [&](int i) {
+    int lo = 0, hi = nsl;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    return (long long)lo * kSelSlice + (i - s_off[lo]);
+  };
+  if (C <= kCandLds && nsl <= NT) {
+    // a group of NT / nsl threads per slice copies the slice's candidates to their
+    // place, four loads of a thread in flight at once
+    const int tps = NT / nsl;
+    const int sl = tid / tps, sub = tid - sl * tps;
+    if (sl < nsl) {
+      const int o = s_off[sl], n = s_off[sl + 1] - o;
+      const float* src = seg + (long long)sl * kSelSlice;
+      for (int i0 = sub; i0 < n; i0 += 4 * tps) {
+        float v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * NT + tid;
-        t4[u] = (i < (int)C) ? cand[i] : 0.f;
-      }
+        for (int u = 0; u < 4; ++u) v[u] = i0 + u * tps < n ? src[i0 + u * tps] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * NT + tid;
-        if (i < (int)C) s_cand[i] = t4[u];
+        for (int u = 0; u < 4; ++u)
+          if (i0 + u * tps < n) s_cand[o + i0 + u * tps] = v[u];
       }
     }
-    __syncthreads();
+  } else if (C <= kCandLds) {
+    for (int i = tid; i < C; i += NT) s_cand[i] = seg[where(i)];
+  } else {
+    for (int i = tid; i < C; i += NT) gcand[i] = seg[where(i)];
   }
+  __syncthreads();
   // one call per source, so that each reads through a pointer of known kind (LDS or global)
   const uint32_t key =
-      C <= (unsigned)kCandLds
+      C <= kCandLds
           ? radix_select_block<NT>(s_cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res)
-          : radix_select_block<NT>(cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
-  if (tid == 0) {
-    tau_out[row] = order_key_to_f32(key);
-    a.cand_cnt[row] = 0u;
-  }
+          : radix_select_block<NT>(gcand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
+  if (tid == 0) tau_out[row] = order_key_to_f32(key);
 }
 
 // ----------------------------------------------------------------------------
