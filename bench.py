@@ -354,6 +354,81 @@ def rocprof_summary(paths) -> int:
     return 0
 
 
+def counter_averages(path):
+    """{(kernel, counter): (average value per dispatch, dispatches)} of a rocprofv3
+    counter_collection csv."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            a = acc.setdefault(key, [0.0, 0])
+            a[0] += float(r["Counter_Value"])
+            a[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in acc.items()}
+
+
+def traffic_record(args) -> int:
+    """Writes the HBM-traffic record of the dominant kernel from four rocprofv3
+    counter_collection csv files: FETCH_SIZE and WRITE_SIZE of a
+    `--only select` run, and FETCH_SIZE and WRITE_SIZE of a `--probe copy` run (a
+    256 MiB device copy: 262144 KiB read and written per dispatch, which calibrates the
+    two counters to bytes). The record names the kernel sources it was taken on."""
+    from sparse_decode_attention_saga_amd import build
+    f_sel, w_sel, f_copy, w_copy = args.traffic_record
+    copy_kib = 262144.0
+    cf = counter_averages(f_copy)
+    cw = counter_averages(w_copy)
+    cf_copy = next(v for (k, c), v in cf.items() if "copyBuffer" in k and c == "FETCH_SIZE")
+    cw_copy = next(v for (k, c), v in cw.items() if "copyBuffer" in k and c == "WRITE_SIZE")
+    fetch_scale, write_scale = copy_kib / cf_copy[0], copy_kib / cw_copy[0]
+    name = "k_qk_select<unsigned short, 128, 128, 1, true, false"  # speculative keys, gather, contiguous
+    fs = counter_averages(f_sel)
+    ws = counter_averages(w_sel)
+    f_k = next(v for (k, c), v in fs.items() if name in k and c == "FETCH_SIZE")
+    w_k = next(v for (k, c), v in ws.items() if name in k and c == "WRITE_SIZE")
+    traffic = f_k[0] * 1024 * fetch_scale + w_k[0] * 1024 * write_scale
+    alg = args.alg_bytes
+    lines = [
+        "# HBM traffic of k_qk_select<bf16, d=128, speculative keys, gather> (saga_select_gather) on the",
+        "# Qwen2.5-1.5B-shaped layer at l_kv=128K (rotating input sets, so K and V come from HBM).",
+        "#",
+        "# counter passes (repository root), one counter per run:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_sel_f -o p --output-format csv -- \\",
+        "#       python3 -u bench.py --only select --steps 256 --warmup 8 --reps 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_sel_w -o p --output-format csv -- (the same)",
+        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_copy_f -o p --output-format csv -- \\",
+        "#       python3 -u bench.py --probe copy --steps 8",
+        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_copy_w -o p --output-format csv -- (the same)",
+        "#   python3 bench.py --traffic-record <the four counter_collection.csv> --alg-bytes <B>",
+        "# calibration: a 256 MiB device copy reads and writes 262144 KiB per dispatch;",
+        f"#   FETCH_SIZE reads {cf_copy[0]:.1f} KiB (scale {fetch_scale:.5f}), "
+        f"WRITE_SIZE reads {cw_copy[0]:.1f} KiB (scale {write_scale:.5f})",
+        "# traffic = FETCH_SIZE * 1024 * fetch_scale + WRITE_SIZE * 1024 * write_scale",
+    ]
+    if alg:
+        lines.append(f"# algorithmic bytes per launch (K stream + union of selected V rows) = {alg}")
+        lines.append(f"#   -> traffic / algorithmic = {traffic / alg:.3f}; reads alone = "
+                     f"{f_k[0] * 1024 * fetch_scale / alg:.3f}")
+    lines += [
+        f"fetch_kib_per_dispatch: {f_k[0]:.1f}",
+        f"write_kib_per_dispatch: {w_k[0]:.1f}",
+        f"dispatches: {f_k[1]}",
+        f"fetch_scale: {fetch_scale:.6f}",
+        f"write_scale: {write_scale:.6f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"source_sha256: {build.source_digest()}",
+        "#",
+        "# averages per dispatch of every kernel of the select runs (KiB):",
+    ]
+    for (k, c), (v, n) in sorted(list(fs.items()) + list(ws.items())):
+        lines.append(f"#   {k[:90]:90s} {c:10s} {n:6d} {v:12.1f}")
+    text = "\n".join(lines) + "\n"
+    with open(args.out or TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text, end="")
+    return 0
+
+
 def sweep(torch, args) -> int:
     """Decode step time of SAGA + Atop-N and of the dense GQA kernel over the sweep grid
     (Qwen2.5-1.5B-shaped heads, l_kv in 4K..128K, N in {128, 512, 2048}, refresh period
@@ -790,6 +865,10 @@ def main() -> int:
                     help="copy: a plain device copy of 256 MiB (counter calibration); read: read ceilings")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="CSV",
                     help="print per-kernel averages of rocprofv3 csv files and exit")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("SEL_FETCH", "SEL_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the dominant kernel's traffic record from four counter_collection csv files")
+    ap.add_argument("--alg-bytes", type=int, default=0, help="algorithmic bytes per launch (--traffic-record)")
+    ap.add_argument("--out", default=None, help="output file of --traffic-record (default: the profiles record)")
     ap.add_argument("--sweep", action="store_true",
                     help="SAGA vs dense step time over l_kv x N x refresh period (one JSON line)")
     ap.add_argument("--merge", action="store_true",
@@ -807,6 +886,8 @@ def main() -> int:
 
     if args.rocprof_summary:
         return rocprof_summary(args.rocprof_summary)
+    if args.traffic_record:
+        return traffic_record(args)
     if args.cpu_baselines:
         return cpu_baselines(args)
 
@@ -890,6 +971,17 @@ def main() -> int:
         api.decode_attn(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, refresh_period=1, step=t,
                         max_l_kv=L, out=out, workspace=ws)
 
+    # a refresh reads the threshold passed in as a guess of the new one's top-digit bin
+    # (two octaves wide); alternating q and 4 q (exact in bf16: every logit times 4) on
+    # one shared threshold makes every guess miss, the refresh's slowest path
+    q4 = [qs[0], qs[0] * 4]
+    tau_miss = taus[0].clone()
+
+    def refresh_miss_step(t):
+        r = t % R
+        api.decode_attn(q4[t % 2], ks[r], vs[r], l_kv, tau_miss, N=w.N, refresh_period=1, step=t,
+                        max_l_kv=L, out=out, workspace=ws)
+
     K, W = args.steps, args.warmup
     n = w.refresh_period
     res = {}
@@ -914,6 +1006,11 @@ def main() -> int:
         res["natural_us"] = pct([1e3 * m / K for m in ms], 50)
         res["refresh_steps"] = sum(1 for t in range(t0, t0 + K) if t % n == 0)
         log(f"natural rate: {res['natural_us']:.2f} us/step over {K} steps ({res['refresh_steps']} refresh)")
+    if args.only in ("all", "saga", "refresh"):
+        Km = min(K, 512)
+        ms = time_graph(torch, lambda: [refresh_miss_step(t) for t in range(W, W + Km)], args.reps)
+        res["refresh_miss_us"] = pct([1e3 * m / Km for m in ms], 50)
+        log(f"refresh step whose guessed bin misses: {res['refresh_miss_us']:.2f} us/step")
     if args.only == "steady":
         ms = time_graph(torch, lambda: [steady_step(t) for t in range(W, W + K)], args.reps)
         res["steady_us"] = pct([1e3 * m / K for m in ms], 50)
@@ -1032,6 +1129,7 @@ def main() -> int:
         "us_per_step_p90": pct(res["saga_us"], 90),
         "us_steady_step": res.get("steady_us"),
         "us_refresh_step": res.get("refresh_us"),
+        "us_refresh_step_guess_missed": res.get("refresh_miss_us"),
         "step_time": "((n-1) * us_steady_step + us_refresh_step) / n, n = refresh_period",
         "us_per_step_natural_rate": res.get("natural_us"),
         "us_select_kernel": res.get("select_us"),

@@ -158,6 +158,8 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int rows, W, ch, nch, P;  // W: tiles per wave of the stream kernels; P: threshold-candidate blocks per row
+  bool cand_chunk;          // threshold candidates per chunk (k_scores_hist), else per slice (k_cand_collect)
+  int nsel;                 // candidate slices per row
   int nchd;                 // chunks of the dense kernels (DenseCfg: 16 KiB of keys and values per wave)
   long long lpad;
   size_t hist, cand_cnt;
@@ -182,15 +184,20 @@ Layout layout(const saga_shape* s, int max_l_kv) {
     off = align_up(off + bytes);
     return at;
   };
-  // counters first: they must be zero before the first call and every call leaves them at zero
-  w.hist = take((size_t)kHistCopies * rows * 256 * 4);
-  w.cand_cnt = take(rows * (size_t)w.P * 4);
   // sized for every chunk width (the narrowest chunks have the most records; lpad is at
   // most max_l_kv rounded up to the widest chunk), so that the size only grows with
   // max_l_kv whatever width a launch takes
   const int ch_min = 16 * 2 * kWaves, ch_max = 16 * 8 * kWaves;
   const size_t lpad_max = max_l_kv > 0 ? (size_t)(max_l_kv + ch_max - 1) / ch_max * ch_max : (size_t)ch_max;
   const size_t nch_max = max_l_kv > 0 ? (size_t)(max_l_kv + ch_min - 1) / ch_min : 1;
+  // threshold candidates per chunk while a row has at most kMaxSel chunks, else per
+  // slice of kSelSlice logits (collected by k_cand_collect)
+  w.cand_chunk = w.nch <= kMaxSel;
+  w.nsel = w.cand_chunk ? w.nch : w.P;
+  const size_t nsel_max = nch_max < (size_t)kMaxSel ? nch_max : (size_t)kMaxSel;  // >= nch here, >= P
+  // counters first: they must be zero before the first call and every call leaves them at zero
+  w.hist = take((size_t)kHistCopies * rows * 256 * 4);
+  w.cand_cnt = take(rows * nsel_max * 4);
   w.scores = take(rows * lpad_max * 4);
   w.surv_idx = take(rows * lpad_max * 4);
   w.surv_val = take(rows * lpad_max * 4);
@@ -267,7 +274,9 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.chunk_hdr = at<ChunkHdr>(ws, w.chunk_hdr);
   a.hist = at<unsigned>(ws, w.hist);
   a.cand_cnt = at<unsigned>(ws, w.cand_cnt);
-  a.nsel = w.P;
+  a.nsel = w.nsel;
+  a.cand_slice = w.cand_chunk ? w.ch : kSelSlice;
+  a.cand_chunk = w.cand_chunk ? 1 : 0;
   a.h_q = s->h_q;
   a.h_k = s->h_k;
   a.g_k = s->h_q / s->h_k;
@@ -304,7 +313,7 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
   SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_TILES(w.W, {
     hipLaunchKernelGGL((k_scores_hist<T, DK, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });););
-  hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
+  if (!a.cand_chunk) hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
   hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);
 }
 

@@ -377,21 +377,36 @@ __device__ __forceinline__ int block_sum_i(int x, int* tmp) {
 // Given a 256-bin histogram `hist` (shared), find the digit whose bin holds the k-th
 // largest element counting from the top bin; res[0] = digit, res[1] = rank of the
 // element inside that bin. If the bins hold fewer than k elements res is left at
-// (0, 1). itmp: int[NT/64].
+// (0, 1). The first wave does the search (four bins per lane from the top, a prefix
+// sum over the lanes); one barrier follows. itmp is unused.
 template <int NT = kBlock>
-__device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsigned k, int* itmp,
+__device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsigned k, int* /*itmp*/,
                                                      unsigned* res) {
+  static_assert(NT >= kWave, "at least one wave");
   const int t = threadIdx.x;
-  if (t == 0) {
-    res[0] = 0u;
-    res[1] = 1u;
-  }
-  const int c = (t < 256) ? (int)hist[255 - t] : 0;
-  int total;
-  const int above = block_excl_scan<NT>(c, itmp, total);  // elements in bins above 255-t
-  if (t < 256 && (unsigned)above < k && k <= (unsigned)(above + c)) {
-    res[0] = (unsigned)(255 - t);
-    res[1] = k - (unsigned)above;
+  if (t < kWave) {
+    unsigned c[4];
+    unsigned sum = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = hist[255 - 4 * t - e];
+      sum += c[e];
+    }
+    unsigned above = (unsigned)wave_incl_scan((int)sum, t) - sum;  // elements in the bins above lane t's
+    if (t == 0) {
+      res[0] = 0u;
+      res[1] = 1u;
+    }
+    // the lane holding the k-th largest writes after the default (same wave, in order)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (above < k && k <= above + c[e]) {
+        res[0] = (unsigned)(255 - 4 * t - e);
+        res[1] = k - above;
+      }
+      above += c[e];
+    }
   }
   __syncthreads();
 }
@@ -423,11 +438,12 @@ __device__ __forceinline__ uint32_t radix_select_block(const float* vals, long l
     }
     __syncthreads();
     digit_of_kth_largest<NT>(hist, k, itmp, res);
+    // the next pass clears hist (no longer read) and writes res only after two barriers
     prefix |= res[0] << shift;
     mask |= 255u << shift;
     k = res[1];
-    __syncthreads();
   }
+  __syncthreads();
   return prefix;
 }
 

@@ -1,7 +1,7 @@
 // Kernels of the SAGA + Atop-N decode step and of the dense GQA baseline (gfx950).
 //
 // Stale-threshold step:  k_qk_select<gather> -> k_split_combine
-// Refresh step:          k_scores_hist -> k_cand_collect -> k_select_finish
+// Refresh step:          k_scores_hist [-> k_cand_collect] -> k_select_finish
 //                        -> k_qk_select<from stored logits, gather> -> k_split_combine
 // Separate stages:       k_qk_select -> k_chunk_gather -> k_split_combine
 // Dense GQA baseline:    k_dense_partial -> k_dense_combine
@@ -76,14 +76,17 @@ struct StreamArgs {
   ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
   float* part;             // [B*h_q, DV/16, nch, 16] chunk records: sum w*v, 16 columns per slice
   unsigned* hist;          // [8, B*h_q, 256] top-digit histogram copies (zero between calls)
-  unsigned* cand_cnt;      // [B*h_q, nsel] threshold candidates of each slice of kSelSlice logits
+  unsigned* cand_cnt;      // [B*h_q, nsel] threshold candidates of each slice of cand_slice logits
   const int32_t* ptab;     // paged caches: [B, ptab_stride] page ids (the kernels' PAGED form)
   long long lpad;
   int h_q, h_k, h_v, g_k, g_v, htiles, l_max, nch, N;  // g_k = h_q/h_k, g_v = h_q/h_v
   int max_l_kv;            // host bound of l_kv[]; larger device values are clamped
   int hsplit;              // blocks sharing one chunk in k_qk_select (heads split among them)
   float scale;
-  int nsel;                // slices of kSelSlice logits per row (the candidate pass's blocks)
+  int nsel;                // candidate slices per row (cand_cnt's row stride)
+  int cand_slice;          // logits per candidate slice: the chunk width (cand_chunk) or kSelSlice
+  int cand_chunk;          // 1: k_scores_hist collects each chunk's candidates in the bin of the
+                           // previous threshold; 0: k_cand_collect collects them
   int ptab_stride, page_shift;  // paged caches: page table row stride, log2(tokens per page)
   int num_pages;           // paged caches: pages per pool (page ids are clamped below it)
 };
@@ -435,6 +438,11 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
 // the top 8 bits of their order keys per query head, accumulated into copy
 // (chunk mod kHistCopies) of a.hist: the logits of a row fall into a few bins, and
 // the copies spread the device atomics of the row's blocks over more addresses.
+// With a.cand_chunk, also the threshold candidates on a guess: the logits whose top
+// 8 bits are those of the row's previous threshold (a bin spans two octaves, and the
+// N-th largest logit of a decoding sequence seldom leaves it between refreshes) go
+// to the chunk's segment of the row's kept-logit buffer, their number to
+// cand_cnt[row, chunk]; k_select_finish checks the guess against the histogram.
 // D is the key head dimension. grid = (nch, h_k * htiles, B), block = 256.
 constexpr int kHistCopies = 8;
 
@@ -454,8 +462,14 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   const int row0 = b * a.h_q + j0;
 
   __shared__ unsigned s_hist[16 * 256];
+  __shared__ float s_cv[16][CH];  // candidates of the chunk per head (cand_chunk)
+  __shared__ int s_cc[16];
   for (int e = tid; e < 16 * 256; e += kBlock) s_hist[e] = 0u;
+  if (tid < 16) s_cc[tid] = 0;
 
+  const bool live = hh < nh;
+  // the guessed bin (256: none, no top digit equals it)
+  const unsigned db = a.cand_chunk && a.tau && live ? order_key(a.tau[row0 + hh]) >> 24 : 256u;
   QK<T, D> qk;
   qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
   const auto kh = key_rows<T, D, PAGED>(a, b, g);
@@ -464,7 +478,6 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
   __syncthreads();
 
-  const bool live = hh < nh;
   if (live) {
     float* srow = a.scores + (long long)(row0 + hh) * a.lpad;
 #pragma unroll
@@ -473,8 +486,13 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = wbase + 16 * t + 4 * kq + r;
-        if (key < L) atomicAdd(&s_hist[hh * 256 + (order_key(v[r]) >> 24)], 1u);
-        else v[r] = -INFINITY;
+        if (key < L) {
+          const unsigned top = order_key(v[r]) >> 24;
+          atomicAdd(&s_hist[hh * 256 + top], 1u);
+          if (top == db) s_cv[hh][atomicAdd(&s_cc[hh], 1)] = v[r];
+        } else {
+          v[r] = -INFINITY;
+        }
       }
       *reinterpret_cast<floatx4*>(srow + wbase + 16 * t + 4 * kq) = v;
     }
@@ -487,11 +505,22 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
       atomicAdd(&a.hist[((c % kHistCopies) * rows + row0 + e / 256) * 256 + (e & 255)], h);
     }
   }
+  if (a.cand_chunk) {  // 16 threads per head
+    const int h = tid >> 4, sub = tid & 15;
+    if (h < nh) {
+      const int n = s_cc[h];
+      const long long r = row0 + h;
+      if (sub == 0) a.cand_cnt[r * a.nsel + c] = (unsigned)n;
+      float* dst = a.surv_val + r * a.lpad + (long long)c * CH;
+      for (int i = sub; i < n; i += 16) dst[i] = s_cv[h][i];
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
-// Refresh, pass 2: candidates for the exact threshold. The sum of the row's
-// histogram copies gives the 8-bit bin that holds its N-th largest logit; each block
+// Refresh, pass 2 for rows of more than kMaxSel chunks (shorter rows get their
+// candidates from k_scores_hist): candidates for the exact threshold. The sum of the
+// row's histogram copies gives the 8-bit bin that holds its N-th largest logit; each block
 // copies the logits of its slice that fall in that bin to the slice's own segment of
 // the row's kept-logit buffer (free at this point of a refresh step; a slice's
 // candidates fit in the slice's kSelSlice places) and their number to
@@ -560,38 +589,88 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
 
 // Refresh, pass 3: the remaining 24 bits of the N-th largest logit resolved on the
 // candidates (counting repeats). The slices' candidate counts give each slice's
-// place in the row's candidate list (a block scan); every candidate is then loaded
-// in one round (each index finds its slice by a binary search of the places) into
-// LDS, or, past kCandLds candidates, into the row's kept-index buffer. Writes tau
+// place in the row's candidate list (a block scan); a group of threads per slice
+// copies the candidates into LDS, or, past kCandLds of them, first finds the second
+// digit on the candidates in place and stages only that digit's. The counts, the
+// first round of candidate loads and the histogram are all requested at once. When
+// k_scores_hist guessed the bin (cand_chunk) and the histogram shows another, the
+// block collects the bin's logits from the row's stored logits instead. Writes tau
 // (-inf when N >= l_kv, unchanged when l_kv == 0) and returns the row's histogram
 // copies to zero. grid = (h_q, B), block = 1024.
-constexpr int kMaxSel = 4096;  // slices of a row of the longest supported context
+constexpr int kMaxSel = 4096;  // candidate slices of a row at most
 
 __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs a, float* tau_out) {
   constexpr int NT = kRowThreads;
   constexpr int PER = kMaxSel / NT;
+  constexpr int kQ = 2;  // 16-byte candidate loads of a thread in flight per round
   const int j = blockIdx.x, b = blockIdx.y;
   const long long rows = (long long)gridDim.y * a.h_q;
   const long long row = (long long)b * a.h_q + j;
-  const int L = min(a.l_kv[b], a.max_l_kv);
   const int N = a.N;
   const int tid = threadIdx.x;
-  if (L <= 0) return;  // no block added to this row's histograms
 
   __shared__ unsigned s_hist[256];
   __shared__ int s_itmp[NT / kWave];
   __shared__ unsigned s_res[2];
+  __shared__ unsigned s_stage;
   __shared__ float s_cand[kCandLds];
   __shared__ int s_off[kMaxSel + 1];
 
-  const int nsl = (L + kSelSlice - 1) / kSelSlice;  // slices holding candidates
+  // The first round of loads is addressed from the host bound max_l_kv, so that none
+  // waits for l_kv: the slices' candidate counts, the first 4 kQ candidates of each
+  // thread's slice (a slice's candidates never outnumber its logits, so these stay
+  // inside the row), the row's histogram copies and the threshold passed in (the
+  // refresh callers always pass one). Slices past the row's own length are dropped
+  // once it is known.
+  const int S = a.cand_slice;
+  const int nsl_max = (a.max_l_kv + S - 1) / S;
+  // the candidate copies: one group of NT / nsl_max threads per slice (one thread per
+  // slice, taking every NT-th, when there are more slices than threads)
+  const int tps = nsl_max <= NT ? NT / nsl_max : 1;
+  const int gsl = tid / tps, sub = tid - gsl * tps, gstep = NT / tps;
+  const float* seg = a.surv_val + row * a.lpad;
   int c[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int sl = tid * PER + u;
-    c[u] = (N < L && sl < nsl) ? (int)a.cand_cnt[row * a.nsel + sl] : 0;
+    c[u] = sl < nsl_max ? (int)a.cand_cnt[row * a.nsel + sl] : 0;
   }
-  if (tid < 256) s_hist[tid] = hist_sum(a.hist, rows, row, tid, true);
+  // thread sub of a slice's group takes the candidates 4 (sub + u tps) .. +3, u < kQ
+  // (16-byte loads: a slice segment starts 16-byte aligned and holds a multiple of 4
+  // places, and a row's padded length covers its logits rounded up to 4)
+  float4 pre[kQ];
+  {
+    const int cap = gsl < nsl_max ? min(S, a.max_l_kv - gsl * S) : 0;
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+      const int i = 4 * (sub + u * tps);
+      pre[u] = i < cap ? *reinterpret_cast<const float4*>(seg + (long long)gsl * S + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  // (relaxed atomic loads: plain vector loads that the compiler neither turns into
+  // scalar loads nor sinks past the l_kv check to their first use)
+  unsigned hv[kHistCopies] = {};
+  if (tid < 256) {
+#pragma unroll
+    for (int cp = 0; cp < kHistCopies; ++cp)
+      hv[cp] = __hip_atomic_load(a.hist + (cp * rows + row) * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  const float tprev = __hip_atomic_load(a.tau + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  if (L <= 0) return;  // no block added to this row's histograms
+  const int nsl = (L + S - 1) / S;  // slices holding candidates
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (tid * PER + u >= nsl) c[u] = 0;
+  if (tid < 256) {  // the row's histogram, and its copies back to zero
+    unsigned h = 0u;
+#pragma unroll
+    for (int cp = 0; cp < kHistCopies; ++cp) {
+      h += hv[cp];
+      a.hist[(cp * rows + row) * 256 + tid] = 0u;
+    }
+    s_hist[tid] = h;
+  }
   if (N >= L) {
     if (tid == 0) tau_out[row] = -INFINITY;
     return;
@@ -612,46 +691,96 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
   __syncthreads();
   digit_of_kth_largest<NT>(s_hist, (unsigned)N, s_itmp, s_res);
   const unsigned d1 = s_res[0], k1 = s_res[1];
-  const float* seg = a.surv_val + row * a.lpad;
+  const unsigned c1 = s_hist[d1];  // the row's logits in bin d1
+  const unsigned db = a.cand_chunk ? order_key(tprev) >> 24 : 256u;  // the guessed bin
   float* gcand = reinterpret_cast<float*>(a.surv_idx) + row * a.lpad;  // free at this point
-  // where candidate i lies: the slice sl with s_off[sl] <= i < s_off[sl + 1]
-  auto where = [&](int i) {
-    int lo = 0, hi = nsl;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_off[mid] <= i) lo = mid;
-      else hi = mid;
-    }
-    return (long long)lo * kSelSlice + (i - s_off[lo]);
-  };
-  if (C <= kCandLds && nsl <= NT) {
-    // a group of NT / nsl threads per slice copies the slice's candidates to their
-    // place, four loads of a thread in flight at once
-    const int tps = NT / nsl;
-    const int sl = tid / tps, sub = tid - sl * tps;
-    if (sl < nsl) {
+  // f(place, logit) for every candidate of the slices, kQ 16-byte loads of a thread
+  // at once (the places past a slice's count that they cover are skipped)
+  auto each_cand = [&](auto&& f) {
+    for (int sl = gsl; sl < nsl; sl += gstep) {
       const int o = s_off[sl], n = s_off[sl + 1] - o;
-      const float* src = seg + (long long)sl * kSelSlice;
-      for (int i0 = sub; i0 < n; i0 += 4 * tps) {
-        float v[4];
+      const float* src = seg + (long long)sl * S;
+      for (int q0 = sub; 4 * q0 < n; q0 += kQ * tps) {
+        const bool first = sl == gsl && q0 == sub;
+        float4 v[kQ];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = i0 + u * tps < n ? src[i0 + u * tps] : 0.f;
+        for (int u = 0; u < kQ; ++u) {
+          const int i = 4 * (q0 + u * tps);
+          v[u] = first ? pre[u] : (i < n ? *reinterpret_cast<const float4*>(src + i) : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i0 + u * tps < n) s_cand[o + i0 + u * tps] = v[u];
+        for (int u = 0; u < kQ; ++u) {
+          const int i = 4 * (q0 + u * tps);
+          const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i + e < n) f(o + i + e, x4[e]);
+        }
       }
     }
+  };
+  uint32_t key;
+  if (a.cand_chunk && d1 != db) {
+    // the guess missed: the bin's logits, c1 of them, from the row's stored logits
+    if (tid == 0) s_stage = 0u;
+    __syncthreads();
+    const bool in_lds = c1 <= (unsigned)kCandLds;
+    const float* lg = a.scores + row * a.lpad;
+    constexpr int V4 = 4;  // 16-byte loads per thread per round
+    for (int i0 = 4 * tid; i0 < L; i0 += 4 * NT * V4) {
+      float4 v[V4];
+#pragma unroll
+      for (int u = 0; u < V4; ++u) {
+        const int i = i0 + u * 4 * NT;  // a multiple of 4 below L: inside the padded row
+        v[u] = i < L ? *reinterpret_cast<const float4*>(lg + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < V4; ++u) {
+        const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (i0 + u * 4 * NT + e < L && (order_key(x4[e]) >> 24) == d1) {
+            const unsigned at = atomicAdd(&s_stage, 1u);
+            if (in_lds) s_cand[at] = x4[e];
+            else gcand[at] = x4[e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    key = in_lds ? radix_select_block<NT>(s_cand, (long long)c1, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res)
+                 : radix_select_block<NT>(gcand, (long long)c1, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
   } else if (C <= kCandLds) {
-    for (int i = tid; i < C; i += NT) s_cand[i] = seg[where(i)];
+    each_cand([&](int i, float x) { s_cand[i] = x; });
+    __syncthreads();
+    key = radix_select_block<NT>(s_cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
   } else {
-    for (int i = tid; i < C; i += NT) gcand[i] = seg[where(i)];
+    // Too many for LDS: the second digit is found on the candidates where they lie,
+    // and only that digit's candidates are staged (in LDS, or past kCandLds of them,
+    // as with many equal logits, in the row's kept-index buffer) for the last two.
+    __syncthreads();  // every thread has read s_hist[d1]
+    if (tid < 256) s_hist[tid] = 0u;
+    __syncthreads();
+    each_cand([&](int, float x) { atomicAdd(&s_hist[(order_key(x) >> 16) & 255u], 1u); });
+    __syncthreads();
+    digit_of_kth_largest<NT>(s_hist, k1, s_itmp, s_res);
+    const unsigned d2 = s_res[0], k2 = s_res[1];
+    const unsigned c2 = s_hist[d2];
+    const uint32_t top = (d1 << 8) | d2;
+    if (tid == 0) s_stage = 0u;
+    __syncthreads();  // every thread has read s_res and s_hist; the counter is zero
+    const bool in_lds = c2 <= (unsigned)kCandLds;
+    each_cand([&](int, float x) {
+      if ((order_key(x) >> 16) == top) {
+        const unsigned at = atomicAdd(&s_stage, 1u);
+        if (in_lds) s_cand[at] = x;
+        else gcand[at] = x;
+      }
+    });
+    __syncthreads();
+    key = in_lds ? radix_select_block<NT>(s_cand, (long long)c2, top << 16, 0xffff0000u, 8, k2, s_hist, s_itmp, s_res)
+                 : radix_select_block<NT>(gcand, (long long)c2, top << 16, 0xffff0000u, 8, k2, s_hist, s_itmp, s_res);
   }
-  __syncthreads();
-  // one call per source, so that each reads through a pointer of known kind (LDS or global)
-  const uint32_t key =
-      C <= kCandLds
-          ? radix_select_block<NT>(s_cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res)
-          : radix_select_block<NT>(gcand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
   if (tid == 0) tau_out[row] = order_key_to_f32(key);
 }
 

@@ -1,10 +1,12 @@
-"""A context of 2^20 keys, eight times the pages' longest (needs an MI355X).
+"""Contexts of 2^20 and 2^21 + 1000 keys, eight and sixteen times the pages' longest
+(needs an MI355X).
 
 The Qwen2.5-1.5B-shaped layer (h_q=12, h_k=1, h_v=4, d=128, bf16, N=512) at
 l_kv = 1,048,576: 2048 chunks of 512 keys (8 tiles per wave) in one sequence, with
 speculative key loads and a combine over 2048 chunk records per row. The oracle is evaluated row by row (every one of the 12
 rows) for the decode step and for the dense kernels (SAGA with full attention
-over all 2^20 keys).
+over all 2^20 keys). The 2^21 + 1000 case has more than 4096 chunks per row, where
+the refresh collects its threshold candidates per slice of 4096 logits.
 """
 import numpy as np
 import pytest
@@ -62,3 +64,21 @@ def test_dense_1m_keys(inputs):
             ref, _ = orc.sparse_softmax_pv(a, V)
             assert np.abs(got[0, j] - ref).max() <= DERIVED * np.abs(ref).max(), j
         del V
+
+
+# Past 4096 chunks per row (2^21 + 1000 keys in chunks of 512) the refresh collects its
+# threshold candidates in slices of 4096 logits (k_cand_collect) instead of per chunk.
+W_2M = wl.QWEN_128K.with_(name="qwen2.5-1.5b-shape-l2m", workload_id=10, l_kv=(1 << 21) + 1000)
+
+
+def test_decode_step_slice_candidates_2m_keys():
+    w = W_2M
+    say(f"generating {w.name}")
+    x = wl.generate(w, seed=0)
+    g = GpuCase(x, w.N)
+    say("refresh step (candidates per slice), then a step reusing the threshold")
+    got0 = g.step(w.refresh_period, 0)
+    got1 = g.step(w.refresh_period, 1)
+    assert np.all(got0["flags"] == 1) and np.all(got1["flags"] == 0)
+    assert np.array_equal(got1["count"], got0["count"])
+    check_sampled_rows(x, w.N, [(0, 0), (0, 5), (0, 11)], [got0, got1], w.dtype)

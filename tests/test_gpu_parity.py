@@ -286,6 +286,55 @@ def test_zero_query_keeps_every_key():
     assert got1["count"][1, 3] == 1500 and got1["flags"][1, 3] == 0
 
 
+def test_refresh_with_more_candidates_than_lds():
+    # N = l_kv / 5 puts the threshold among the logits between 0.5 and 2 (one top
+    # digit of the order key), about 11,000 of a 40,000-key row: more candidates than
+    # the finishing select stages in LDS, so it finds their second digit in place
+    # first; then a step reusing the refreshed threshold
+    w, x = small(2, 4, 1, 2, 64, [40000, 37001], "bf16", seed=37, plant=0.0)
+    N = 8000
+    g = GpuCase(x, N, sel_cap=40000)
+    got = g.step(8, 0)
+    ref = oracle_step(x, N, 8, 0)
+    compare(got, ref, x, "bf16", check_tau=True)
+    got1 = g.step(8, 1)
+    ref1 = oracle_step(x, N, 8, 1, tau_in=ref.tau)
+    compare(got1, ref1, x, "bf16", check_tau=False)
+
+
+@pytest.mark.parametrize("hint", ["exact", "zero", "huge", "nan", "minus_inf"])
+def test_refresh_result_does_not_depend_on_previous_threshold(hint):
+    # a refresh reads the threshold passed in only to guess the bin of the new one (a
+    # right guess saves a pass over the logits); whatever it holds, the refreshed
+    # threshold, the kept sets and the outputs are the oracle's
+    w, x = small(2, 8, 2, 4, 64, [3000, 1701], "bf16", seed=39)
+    N = 24
+    ref = oracle_step(x, N, 4, 0)
+    tau_in = {"exact": ref.tau, "zero": np.zeros_like(ref.tau), "huge": np.full_like(ref.tau, 1e30),
+              "nan": np.full_like(ref.tau, np.nan), "minus_inf": np.full_like(ref.tau, -np.inf)}[hint]
+    g = GpuCase(x, N)
+    got = g.step(4, 0, tau_in=tau_in)
+    compare(got, ref, x, "bf16", check_tau=True)
+    assert np.all(got["flags"] == 1)
+
+
+def test_ties_beyond_lds_capacity():
+    # 9000 identical keys: all logits of a row are one value, so all 9000 are
+    # threshold candidates sharing their second digit too, staged in the row's
+    # global buffer; every key ties with the threshold and is kept
+    w, x = small(1, 4, 1, 2, 64, [9000], "bf16", seed=38)
+    x.k[0, 0, :9000] = x.k[0, 0, 11]
+    g = GpuCase(x, 100, sel_cap=9000)
+    got = g.step(1, 0)
+    ref = oracle_step(x, 100, 1, 0)
+    assert np.all(np.abs(got["tau"] - ref.tau) <= 1e-5 * np.abs(ref.tau))
+    assert np.all(got["count"] == 9000)
+    v = x.v.double().numpy()
+    for j in range(4):
+        mean = v[0, j // 2, :9000].mean(axis=0)
+        assert np.abs(got["O"][0, j] - mean).max() <= DERIVED * np.abs(mean).max()
+
+
 @pytest.mark.parametrize("scale", [0.05, 2.5])
 def test_given_logit_scale(scale):
     # a logit scale other than 1/sqrt(d) (saga_shape.scale): the decode step (refresh
