@@ -311,7 +311,10 @@ dim3 stream_grid(const saga_shape* s, const Layout& w) {
 
 void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, float* tau, hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_TILES(w.W, {
-    hipLaunchKernelGGL((k_scores_hist<T, DK, P, W>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+    if (s->batch == 1)  // one sequence: its chunks reach max_l_kv, key loads need not wait for l_kv
+      hipLaunchKernelGGL((k_scores_hist<T, DK, P, W, true>), stream_grid(s, w), dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_scores_hist<T, DK, P, W, false>), stream_grid(s, w), dim3(kBlock), 0, st, a);
   });););
   if (!a.cand_chunk) hipLaunchKernelGGL(k_cand_collect, dim3(w.P, s->h_q, s->batch), dim3(kBlock), 0, st, a);
   hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);

@@ -377,11 +377,12 @@ __device__ __forceinline__ int block_sum_i(int x, int* tmp) {
 // Given a 256-bin histogram `hist` (shared), find the digit whose bin holds the k-th
 // largest element counting from the top bin; res[0] = digit, res[1] = rank of the
 // element inside that bin. If the bins hold fewer than k elements res is left at
-// (0, 1). The first wave does the search (four bins per lane from the top, a prefix
-// sum over the lanes); one barrier follows. itmp is unused.
+// (0, 1). With `bin_count`, *bin_count = the count of the chosen bin (0 if none). The
+// first wave does the search (four bins per lane from the top, a prefix sum over the
+// lanes); one barrier follows. itmp is unused.
 template <int NT = kBlock>
 __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsigned k, int* /*itmp*/,
-                                                     unsigned* res) {
+                                                     unsigned* res, unsigned* bin_count = nullptr) {
   static_assert(NT >= kWave, "at least one wave");
   const int t = threadIdx.x;
   if (t < kWave) {
@@ -396,6 +397,7 @@ __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsig
     if (t == 0) {
       res[0] = 0u;
       res[1] = 1u;
+      if (bin_count) *bin_count = 0u;
     }
     // the lane holding the k-th largest writes after the default (same wave, in order)
     asm volatile("" ::: "memory");
@@ -404,6 +406,7 @@ __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsig
       if (above < k && k <= above + c[e]) {
         res[0] = (unsigned)(255 - 4 * t - e);
         res[1] = k - above;
+        if (bin_count) *bin_count = c[e];
       }
       above += c[e];
     }
@@ -412,12 +415,17 @@ __device__ __forceinline__ void digit_of_kth_largest(const unsigned* hist, unsig
 }
 
 // The order key of the k-th largest of vals[0..n) among the values whose key
-// matches `prefix` on the bits of `mask`, resolving bits shift_start+7..0.
+// matches `prefix` on the bits of `mask`, resolving bits shift_start+7..0, 8 per
+// pass. Once at most kWave values match the resolved prefix, they are copied to LDS
+// and the first wave ranks them directly (each lane counts the values above and not
+// below its own), which takes the place of the remaining passes.
 // `vals` may point to global or shared memory.
 template <int NT = kBlock>
 __device__ __forceinline__ uint32_t radix_select_block(const float* vals, long long n, uint32_t prefix,
                                                        uint32_t mask, int shift_start, unsigned k,
                                                        unsigned* hist, int* itmp, unsigned* res) {
+  __shared__ uint32_t s_few[kWave];
+  __shared__ unsigned s_nfew, s_left;
   const int tid = threadIdx.x;
   for (int shift = shift_start; shift >= 0; shift -= 8) {
     for (int e = tid; e < 256; e += NT) hist[e] = 0u;
@@ -437,11 +445,47 @@ __device__ __forceinline__ uint32_t radix_select_block(const float* vals, long l
       }
     }
     __syncthreads();
-    digit_of_kth_largest<NT>(hist, k, itmp, res);
-    // the next pass clears hist (no longer read) and writes res only after two barriers
+    digit_of_kth_largest<NT>(hist, k, itmp, res, &s_left);
+    // the next pass clears hist (no longer read) and writes res and s_left only after
+    // two barriers
     prefix |= res[0] << shift;
     mask |= 255u << shift;
     k = res[1];
+    const unsigned left = s_left;  // values matching the new prefix
+    if (shift > 0 && left <= (unsigned)kWave) {
+      if (tid == 0) s_nfew = 0u;
+      __syncthreads();
+      for (long long i0 = 0; i0 < n; i0 += 4LL * NT) {
+        float v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const long long i = i0 + (long long)u * NT + tid;
+          v4[u] = (i < n) ? vals[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const long long i = i0 + (long long)u * NT + tid;
+          const uint32_t key = order_key(v4[u]);
+          if (i < n && (key & mask) == prefix) s_few[atomicAdd(&s_nfew, 1u)] = key;
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        // the k-th largest of the `left` values (k <= left): a lane whose value has
+        // fewer than k values above it and at least k not below it
+        const uint32_t mine = tid < (int)left ? s_few[tid] : 0u;
+        unsigned above = 0u, not_below = 0u;
+        for (unsigned i = 0; i < left; ++i) {
+          const uint32_t o = s_few[i];
+          above += o > mine ? 1u : 0u;
+          not_below += o >= mine ? 1u : 0u;
+        }
+        if (tid < (int)left && above < k && k <= not_below) res[0] = mine;  // equal values write the same
+      }
+      __syncthreads();
+      prefix = res[0];
+      break;
+    }
   }
   __syncthreads();
   return prefix;

@@ -336,6 +336,12 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   if constexpr (MODE == kFromKeysSpeculative) {
     qk.load_q(qbase + (size_t)row0 * DK, nh, lane);
     score_tiles<T, DK, TPW>(sc, qk, kh, wbase, max_l_kv, lane, scale);
+  } else if constexpr (MODE == kFromScores) {
+    // the stored logits lie in the workspace (rows padded to whole chunks): loaded
+    // before l_kv arrives, at any batch size; keys past l_kv are masked below
+    const float* srow = a.scores + (long long)(row0 + (live ? hh : 0)) * a.lpad;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) sc[t] = *reinterpret_cast<const floatx4*>(srow + wbase + 16 * t + 4 * kq);
   }
   const int L = min(a.l_kv[b], a.max_l_kv);
   if (base >= L) return;
@@ -347,11 +353,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   }
   if constexpr (PAGED && GATHER) stage_pages<CH>(kl, a, b, base);
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
-  if constexpr (MODE == kFromScores) {
-    const float* srow = a.scores + (long long)(row0 + (live ? hh : 0)) * a.lpad;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) sc[t] = *reinterpret_cast<const floatx4*>(srow + wbase + 16 * t + 4 * kq);
-  } else if constexpr (MODE == kFromKeys) {
+  if constexpr (MODE == kFromKeys) {
     qk.load_q(qbase + (size_t)row0 * DK, nh, lane);
     score_tiles<T, DK, TPW>(sc, qk, kh, wbase, L, lane, scale);
   }
@@ -443,23 +445,33 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
 // N-th largest logit of a decoding sequence seldom leaves it between refreshes) go
 // to the chunk's segment of the row's kept-logit buffer, their number to
 // cand_cnt[row, chunk]; k_select_finish checks the guess against the histogram.
+// SPEC (one sequence) issues the key loads before l_kv arrives, for rows below
+// max_l_kv (inside the cache); keys past l_kv are masked.
 // D is the key head dimension. grid = (nch, h_k * htiles, B), block = 256.
 constexpr int kHistCopies = 8;
 
-template <typename T, int D, bool PAGED, int W>
+template <typename T, int D, bool PAGED, int W, bool SPEC>
 __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, D, W>::kTPW;
   constexpr int CH = StreamCfg<T, D, W>::kChunk;
   const int c = blockIdx.x, gy = blockIdx.y, b = blockIdx.z;
-  const int L = min(a.l_kv[b], a.max_l_kv);
   const int base = c * CH;
-  if (base >= L) return;
   const int g = gy / a.htiles, ht = gy - g * a.htiles;
   const int j0 = g * a.g_k + ht * 16;
   const int nh = min(16, a.g_k - ht * 16);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int hh = lane & 15, kq = lane >> 4;
   const int row0 = b * a.h_q + j0;
+  const int wbase = base + wv * 16 * TPW;
+  const auto kh = key_rows<T, D, PAGED>(a, b, g);
+  QK<T, D> qk;
+  floatx4 sc[TPW];
+  if constexpr (SPEC) {
+    qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
+    score_tiles<T, D, TPW>(sc, qk, kh, wbase, a.max_l_kv, lane, a.scale);
+  }
+  const int L = min(a.l_kv[b], a.max_l_kv);
+  if (base >= L) return;
 
   __shared__ unsigned s_hist[16 * 256];
   __shared__ float s_cv[16][CH];  // candidates of the chunk per head (cand_chunk)
@@ -470,12 +482,10 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
   const bool live = hh < nh;
   // the guessed bin (256: none, no top digit equals it)
   const unsigned db = a.cand_chunk && a.tau && live ? order_key(a.tau[row0 + hh]) >> 24 : 256u;
-  QK<T, D> qk;
-  qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
-  const auto kh = key_rows<T, D, PAGED>(a, b, g);
-  const int wbase = base + wv * 16 * TPW;
-  floatx4 sc[TPW];
-  score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+  if constexpr (!SPEC) {
+    qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
+    score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
+  }
   __syncthreads();
 
   if (live) {
@@ -726,7 +736,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
     __syncthreads();
     const bool in_lds = c1 <= (unsigned)kCandLds;
     const float* lg = a.scores + row * a.lpad;
-    constexpr int V4 = 4;  // 16-byte loads per thread per round
+    constexpr int V4 = 16;  // 16-byte loads per thread per round (256 KiB per block)
     for (int i0 = 4 * tid; i0 < L; i0 += 4 * NT * V4) {
       float4 v[V4];
 #pragma unroll
