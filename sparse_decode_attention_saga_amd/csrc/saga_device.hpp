@@ -203,6 +203,17 @@ __device__ __forceinline__ int wave_incl_scan(int x, int /*lane*/) {
   return s;
 }
 
+// Inclusive prefix sum within each row of 16 lanes (the row-local steps above).
+__device__ __forceinline__ int row_incl_scan(int x) {
+  int s = x;
+  s += dpp_add_src<0x111>(0, x);             // row_shr:1
+  s += dpp_add_src<0x112>(0, x);             // row_shr:2
+  s += dpp_add_src<0x113>(0, x);             // row_shr:3
+  s += dpp_add_src<0x114, 0xf, 0xe>(0, s);   // row_shr:4, lanes 4..15 of each row
+  s += dpp_add_src<0x118, 0xf, 0xc>(0, s);   // row_shr:8, lanes 8..15 of each row
+  return s;
+}
+
 // Exclusive prefix sum in thread order; `total` gets the block sum. tmp: int[NT/64].
 template <int NT = kBlock>
 __device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {

@@ -148,7 +148,15 @@ __device__ __forceinline__ CacheRows<T, D, PAGED> value_rows(const StreamArgs& a
 // Kept entries of one chunk, per head of the tile, staged in LDS: offset of the key
 // inside the chunk and its logit; plus the count and the largest kept logit (as an
 // order key) per head; with paged caches also the pages of the chunk's tokens.
+// Kept entries of one chunk, per head of the tile, staged in LDS in increasing key
+// order: off[h][e] is the offset inside the chunk of head h's e-th kept key; its logit
+// is val[h][off] (indexed by key offset); the select kernel first marks the kept keys
+// in bits[h] (bit i of word w: offset 32 w + i). Plus the count and the largest kept
+// logit (as an order key) per head; with paged caches also the pages of the chunk's
+// tokens.
 template <int CH> struct KeptLds {
+  static constexpr int kWords = CH / 32;
+  unsigned bits[16][kWords];
   uint16_t off[16][CH];
   float val[16][CH];
   int cnt[16];
@@ -228,7 +236,7 @@ __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const Strea
                            : vrow + (size_t)off * D;
 #pragma unroll
         for (int p = 0; p < PPL; ++p) x[u][p] = ld16(r + 16 * p * EPL);
-        w[u] = expf(kl.val[h][e] - m);
+        w[u] = expf(kl.val[h][off] - m);
       }
     }
 #pragma unroll
@@ -346,11 +354,12 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   const int L = min(a.l_kv[b], a.max_l_kv);
   if (base >= L) return;
 
-  __shared__ KeptLds<GATHER ? CH : 1> kl;
+  __shared__ KeptLds<CH> kl;
   if (tid < 16) {
     kl.cnt[tid] = 0;
     kl.mx[tid] = 0u;
   }
+  for (int e = tid; e < 16 * KeptLds<CH>::kWords; e += kBlock) (&kl.bits[0][0])[e] = 0u;
   if constexpr (PAGED && GATHER) stage_pages<CH>(kl, a, b, base);
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
   if constexpr (MODE == kFromKeys) {
@@ -359,8 +368,10 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   }
   __syncthreads();
 
-  // this lane's kept entries as a bit mask (bit 4t+r: key wbase+16t+4kq+r), one LDS
-  // atomic per lane for their slots, then one short loop over the set bits
+  // This lane's kept entries as a bit mask (bit 4t+r: key wbase+16t+4kq+r). They are
+  // marked in the head's bitmap (order-free atomic ORs) and their logits stored at
+  // their key offsets; after the barrier the kept list is read off the bitmap in key
+  // order, so the lists, and every sum over them, are the same on every run.
   static_assert(TPW * 4 <= 32, "kept mask holds 32 entries");
   unsigned pm = 0u;
 #pragma unroll
@@ -371,33 +382,54 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
       if (live && key < L && sc[t][r] >= tau_l) pm |= 1u << (4 * t + r);
     }
   if (pm) {
-    const long long seg = (long long)(row0 + hh) * a.lpad + base;
-    int slot = atomicAdd(&kl.cnt[hh], __popc(pm));
+    const int wo = wbase - base;  // offset of the wave's keys in the chunk (a multiple of 32)
     float vmax = -INFINITY;
-    do {
-      const int bit = __builtin_ctz(pm);
-      pm &= pm - 1u;
-      float v = sc[0][0];
 #pragma unroll
-      for (int e = 1; e < TPW * 4; ++e) v = (bit == e) ? sc[e >> 2][e & 3] : v;
-      const int key = wbase + 16 * (bit >> 2) + 4 * kq + (bit & 3);
-      a.surv_idx[seg + slot] = key;
-      a.surv_val[seg + slot] = v;
-      if constexpr (GATHER) {
-        kl.off[hh][slot] = (uint16_t)(key - base);
-        kl.val[hh][slot] = v;
+    for (int t = 0; t < TPW; ++t) {
+      const unsigned nib = (pm >> (4 * t)) & 15u;
+      if (nib) {
+        const int pos = wo + 16 * t + 4 * kq;  // 4 consecutive offsets inside one word
+        atomicOr(&kl.bits[hh][pos >> 5], nib << (pos & 31));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((nib >> r) & 1u) {
+            kl.val[hh][pos + r] = sc[t][r];
+            vmax = fmaxf(vmax, sc[t][r]);
+          }
       }
-      vmax = fmaxf(vmax, v);
-      ++slot;
-    } while (pm);
+    }
+    atomicAdd(&kl.cnt[hh], __popc(pm));
     atomicMax(&kl.mx[hh], order_key(vmax));
   }
   __syncthreads();
+  // 16 threads per head, thread s16 takes bitmap word s16: its kept keys follow those
+  // of the words before it (a prefix over the row of 16 lanes). The list goes to LDS
+  // for the value gather first; its copy in memory is written after the gather has
+  // issued its loads.
+  static_assert(KeptLds<CH>::kWords <= 16, "one bitmap word per thread");
+  const int lh = tid >> 4, s16 = tid & 15;
+  const unsigned wb = (lh < nh && s16 < KeptLds<CH>::kWords) ? kl.bits[lh][s16] : 0u;
+  const int first = row_incl_scan(__popc(wb)) - __popc(wb);
+  if constexpr (GATHER) {
+    int at = first;
+    for (unsigned m = wb; m; m &= m - 1u) kl.off[lh][at++] = (uint16_t)(32 * s16 + __builtin_ctz(m));
+    __syncthreads();
+  }
   if (tid < nh && (hsplit == 1 || tid % hsplit == hs)) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
     *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
   }
   if constexpr (GATHER) chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit);
+  if (wb) {
+    const long long seg = (long long)(row0 + lh) * a.lpad + base;
+    int at = first;
+    for (unsigned m = wb; m; m &= m - 1u) {
+      const int off = 32 * s16 + __builtin_ctz(m);
+      a.surv_idx[seg + at] = base + off;
+      a.surv_val[seg + at] = kl.val[lh][off];
+      ++at;
+    }
+  }
 }
 
 // The chunk records of eq. (7) from kept lists already in the workspace (the
@@ -427,8 +459,9 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
     const int h = e / CH, i = e - h * CH;
     if (i < kl.cnt[h]) {
       const long long at = (long long)(row0 + h) * a.lpad + base + i;
-      kl.off[h][i] = (uint16_t)(a.surv_idx[at] - base);
-      kl.val[h][i] = a.surv_val[at];
+      const int off = a.surv_idx[at] - base;
+      kl.off[h][i] = (uint16_t)off;
+      kl.val[h][off] = a.surv_val[at];
     }
   }
   __syncthreads();
@@ -907,7 +940,7 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
   __shared__ float s_ftmp[NW];
   __shared__ int s_list_i[NT];
   __shared__ float s_list_v[NT];
-  __shared__ int s_n;
+  __shared__ int s_scan[NW];
 
   const float* srow = s.scores + rbase;
   float tau = a.tau[row];
@@ -932,19 +965,17 @@ __device__ void exact_row(const GatherArgs& a, int b, int j, int L, bool refresh
   float z = 0.f;
   int kept = 0;
   for (int base = 0; base < L; base += NT) {
-    if (tid == 0) s_n = 0;
-    __syncthreads();
+    // the kept entries of these NT keys in key order (a block prefix sum of the flags)
     const int i = base + tid;
-    if (i < L) {
-      const float v = srow[i];
-      if (v >= tau) {
-        const int slot = atomicAdd(&s_n, 1);
-        s_list_i[slot] = i;
-        s_list_v[slot] = v;
-      }
+    const float v = i < L ? srow[i] : 0.f;
+    const bool keep = i < L && v >= tau;
+    int n;
+    const int slot = block_excl_scan<NT>(keep ? 1 : 0, s_scan, n);
+    if (keep) {
+      s_list_i[slot] = i;
+      s_list_v[slot] = v;
     }
     __syncthreads();
-    const int n = s_n;
     for (int p = grp; p < n; p += RG::NG) {
       const int idx = s_list_i[p];
       const float w = expf(s_list_v[p] - m);

@@ -495,11 +495,10 @@ def test_dense_gqa_full_size(name):
     (1, 12, 1, 4, 128, [4096], 2048, "bf16"),
     (2, 8, 2, 4, 64, [3000, 1234], 100, "f32"),
 ])
-@pytest.mark.skip(reason="needs fixed slots for kept entries; the wavefront-ballot compaction that gave them "
-                         "faulted the GPU on its first run with no cause found, so it is not built")
 def test_repeated_steps_are_bitwise_identical(case):
-    # kept entries take fixed slots (wavefront ballots) and every sum runs in a fixed
-    # order, so the same step on the same inputs gives the same bits every time
+    # kept entries take fixed slots (each lane's first slot is the sum of the kept
+    # counts of the lanes before it) and every sum runs in a fixed order, so the same
+    # step on the same inputs gives the same bits every time
     B, h_q, h_k, h_v, d, lens, N, dtype = case
     w, x = small(B, h_q, h_k, h_v, d, lens, dtype, seed=50)
     g = GpuCase(x, N)
