@@ -402,17 +402,20 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     atomicMax(&kl.mx[hh], order_key(vmax));
   }
   __syncthreads();
-  // 16 threads per head, thread s16 takes bitmap word s16: its kept keys follow those
-  // of the words before it (a prefix over the row of 16 lanes). The list goes to LDS
-  // for the value gather first; its copy in memory is written after the gather has
-  // issued its loads.
-  static_assert(KeptLds<CH>::kWords <= 16, "one bitmap word per thread");
+  // 16 threads per head, thread s16 takes the BPT bitmap bits from offset s16 BPT on:
+  // its kept keys follow those of the threads before it (a prefix over the row of 16
+  // lanes). The list goes to LDS for the value gather first; its copy in memory is
+  // written after the gather has issued its loads.
+  constexpr int BPT = CH / 16;  // 8, 16 or 32 bits, inside one word
+  static_assert(BPT == 8 || BPT == 16 || BPT == 32, "a thread's bits lie in one word");
   const int lh = tid >> 4, s16 = tid & 15;
-  const unsigned wb = (lh < nh && s16 < KeptLds<CH>::kWords) ? kl.bits[lh][s16] : 0u;
+  const int boff = s16 * BPT;
+  const unsigned wb =
+      lh < nh ? (kl.bits[lh][boff >> 5] >> (boff & 31)) & (BPT == 32 ? ~0u : (1u << BPT) - 1u) : 0u;
   const int first = row_incl_scan(__popc(wb)) - __popc(wb);
   if constexpr (GATHER) {
     int at = first;
-    for (unsigned m = wb; m; m &= m - 1u) kl.off[lh][at++] = (uint16_t)(32 * s16 + __builtin_ctz(m));
+    for (unsigned m = wb; m; m &= m - 1u) kl.off[lh][at++] = (uint16_t)(boff + __builtin_ctz(m));
     __syncthreads();
   }
   if (tid < nh && (hsplit == 1 || tid % hsplit == hs)) {
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     const long long seg = (long long)(row0 + lh) * a.lpad + base;
     int at = first;
     for (unsigned m = wb; m; m &= m - 1u) {
-      const int off = 32 * s16 + __builtin_ctz(m);
+      const int off = boff + __builtin_ctz(m);
       a.surv_idx[seg + at] = base + off;
       a.surv_val[seg + at] = kl.val[lh][off];
       ++at;
