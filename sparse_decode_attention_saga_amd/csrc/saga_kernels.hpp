@@ -150,13 +150,9 @@ __device__ __forceinline__ CacheRows<T, D, PAGED> value_rows(const StreamArgs& a
 // order key) per head; with paged caches also the pages of the chunk's tokens.
 // Kept entries of one chunk, per head of the tile, staged in LDS in increasing key
 // order: off[h][e] is the offset inside the chunk of head h's e-th kept key; its logit
-// is val[h][off] (indexed by key offset); the select kernel first marks the kept keys
-// in bits[h] (bit i of word w: offset 32 w + i). Plus the count and the largest kept
-// logit (as an order key) per head; with paged caches also the pages of the chunk's
-// tokens.
+// is val[h][off] (indexed by key offset). Plus the count and the largest kept logit
+// (as an order key) per head; with paged caches also the pages of the chunk's tokens.
 template <int CH> struct KeptLds {
-  static constexpr int kWords = CH / 32;
-  unsigned bits[16][kWords];
   uint16_t off[16][CH];
   float val[16][CH];
   int cnt[16];
@@ -186,16 +182,16 @@ __device__ __forceinline__ void stage_pages(KeptLds<CH>& kl, const StreamArgs& a
 // groups each, taking alternate kept entries); the groups of one head add their sums
 // in LDS. Rows without kept entries in the chunk write nothing. Called by every
 // thread of the block. D is the value head dimension.
+// s_part: LDS scratch of the block, [kBlock / 16][D + 1] floats.
 template <typename T, int D, int CH, bool PAGED>
 __device__ __forceinline__ void chunk_records(const KeptLds<CH>& kl, const StreamArgs& a, int b, int j0, int nh,
-                                              int c, int hs, int hsplit) {
+                                              int c, int hs, int hsplit, float (*s_part)[D + 1]) {
   constexpr int EPL = Unpack<T>::kN;                    // columns per 16-byte piece
   constexpr int PIECES = D / EPL;                       // pieces per value row
   constexpr int RPG = PIECES >= 16 ? 1 : 16 / PIECES;  // rows one group load covers
   constexpr int PPL = PIECES >= 16 ? PIECES / 16 : 1;   // pieces per lane per row
   constexpr int U = 4;                                  // loads in flight per lane
   constexpr int NG = kBlock / 16;                       // groups of 16 lanes
-  __shared__ float s_part[NG][D + 1];
   const int nown = hsplit == 1 ? nh : (nh - hs + hsplit - 1) / hsplit;  // owned heads (uniform)
   if (nown <= 0) return;
   const int gph = NG / nown;                            // groups per owned head
@@ -355,11 +351,18 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   if (base >= L) return;
 
   __shared__ KeptLds<CH> kl;
+  // the kept bitmap of each head (bit i of word w: chunk offset 32 w + i), dead once the
+  // kept lists are built; the value gather's partial sums reuse its LDS
+  constexpr int kWords = CH / 32;
+  __shared__ union {
+    unsigned bits[16][kWords];
+    float part[kBlock / 16][DV + 1];
+  } s_bp;
   if (tid < 16) {
     kl.cnt[tid] = 0;
     kl.mx[tid] = 0u;
   }
-  for (int e = tid; e < 16 * KeptLds<CH>::kWords; e += kBlock) (&kl.bits[0][0])[e] = 0u;
+  for (int e = tid; e < 16 * kWords; e += kBlock) (&s_bp.bits[0][0])[e] = 0u;
   if constexpr (PAGED && GATHER) stage_pages<CH>(kl, a, b, base);
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
   if constexpr (MODE == kFromKeys) {
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
       const unsigned nib = (pm >> (4 * t)) & 15u;
       if (nib) {
         const int pos = wo + 16 * t + 4 * kq;  // 4 consecutive offsets inside one word
-        atomicOr(&kl.bits[hh][pos >> 5], nib << (pos & 31));
+        atomicOr(&s_bp.bits[hh][pos >> 5], nib << (pos & 31));
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if ((nib >> r) & 1u) {
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   const int lh = tid >> 4, s16 = tid & 15;
   const int boff = s16 * BPT;
   const unsigned wb =
-      lh < nh ? (kl.bits[lh][boff >> 5] >> (boff & 31)) & (BPT == 32 ? ~0u : (1u << BPT) - 1u) : 0u;
+      lh < nh ? (s_bp.bits[lh][boff >> 5] >> (boff & 31)) & (BPT == 32 ? ~0u : (1u << BPT) - 1u) : 0u;
   const int first = row_incl_scan(__popc(wb)) - __popc(wb);
   if constexpr (GATHER) {
     int at = first;
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
     *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
   }
-  if constexpr (GATHER) chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit);
+  if constexpr (GATHER) chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit, s_bp.part);
   if (wb) {
     const long long seg = (long long)(row0 + lh) * a.lpad + base;
     int at = first;
@@ -451,6 +454,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
   const int tid = threadIdx.x;
   const int row0 = b * a.h_q + j0;
   __shared__ KeptLds<CH> kl;
+  __shared__ float s_part[kBlock / 16][DV + 1];
   if (tid < nh) {
     const ChunkHdr h = a.chunk_hdr[(long long)(row0 + tid) * a.nch + c];
     kl.cnt[tid] = h.cnt;
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
     }
   }
   __syncthreads();
-  chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, 0, 1);
+  chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, 0, 1, s_part);
 }
 
 // ----------------------------------------------------------------------------
