@@ -325,7 +325,7 @@ def recorded_traffic():
                 rec[k.strip()] = v.strip()
     if rec.get("source_sha256") != build.source_digest():
         return None, "kernel sources changed since the counters were taken"
-    return float(rec["traffic_bytes_per_launch"]), TRAFFIC_FILE
+    return float(rec["traffic_bytes_per_launch"]), os.path.relpath(TRAFFIC_FILE, os.path.dirname(os.path.abspath(__file__)))
 
 
 def rocprof_summary(paths) -> int:
