@@ -234,6 +234,33 @@ __device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {
   return off + inc - x;
 }
 
+// Two exclusive prefix sums at once (one pass of barriers); totals in ta and tb.
+// tmp: int[2 * NT/64].
+template <int NT = kBlock>
+__device__ __forceinline__ int2 block_excl_scan2(int a, int b, int* tmp, int& ta, int& tb) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
+  if (lane == kWave - 1) {
+    tmp[w] = ia;
+    tmp[NW + w] = ib;
+  }
+  __syncthreads();
+  int oa = 0, ob = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int x = tmp[i], y = tmp[NW + i];
+    oa += (i < w) ? x : 0;
+    ob += (i < w) ? y : 0;
+    sa += x;
+    sb += y;
+  }
+  __syncthreads();
+  ta = sa;
+  tb = sb;
+  return make_int2(oa + ia - a, ob + ib - b);
+}
+
 // Wave reductions with DPP row operations (gfx9): sums and maxima within quads, then
 // half-rows, rows of 16, and across the four rows with the row broadcasts of lanes
 // 15 and 31; the total ends in lane 63 and is read back as a wave-uniform value.

@@ -476,15 +476,35 @@ __global__ __launch_bounds__(kBlock) void k_chunk_gather(const StreamArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// The refresh's guess of where the new threshold lies: the order keys within
+// kGuessHalf of the key of the threshold passed in, [lo, hi] (a quarter octave either
+// way for logits of either sign: a threshold that moved by less than about 19% since
+// the last refresh lies inside, wherever it lies on the float scale). Empty (lo > hi,
+// false) for a threshold that is not finite.
+constexpr uint32_t kGuessHalf = 1u << 21;
+__device__ __forceinline__ bool guess_window(float tprev, uint32_t& lo, uint32_t& hi) {
+  if (!__builtin_isfinite(tprev)) {
+    lo = 1u;
+    hi = 0u;
+    return false;
+  }
+  const uint32_t k = order_key(tprev);
+  lo = k > kGuessHalf ? k - kGuessHalf : 0u;
+  hi = k < 0xffffffffu - kGuessHalf ? k + kGuessHalf : 0xffffffffu;
+  return true;
+}
+
+// ----------------------------------------------------------------------------
 // Refresh, pass 1: logits of every cached key stored as fp32, plus a histogram of
 // the top 8 bits of their order keys per query head, accumulated into copy
 // (chunk mod kHistCopies) of a.hist: the logits of a row fall into a few bins, and
 // the copies spread the device atomics of the row's blocks over more addresses.
-// With a.cand_chunk, also the threshold candidates on a guess: the logits whose top
-// 8 bits are those of the row's previous threshold (a bin spans two octaves, and the
-// N-th largest logit of a decoding sequence seldom leaves it between refreshes) go
-// to the chunk's segment of the row's kept-logit buffer, their number to
-// cand_cnt[row, chunk]; k_select_finish checks the guess against the histogram.
+// With a.cand_chunk, also the threshold candidates on a guess: the logits inside the
+// window around the row's previous threshold (guess_window; the N-th largest logit
+// of a decoding sequence moves little between refreshes) go to the chunk's segment
+// of the row's kept-logit buffer; cand_cnt[row, chunk] = their number plus, in the
+// upper 16 bits, the number of logits above the window. k_select_finish checks the
+// guess with those counts.
 // SPEC (one sequence) issues the key loads before l_kv arrives, for rows below
 // max_l_kv (inside the cache); keys past l_kv are masked.
 // D is the key head dimension. grid = (nch, h_k * htiles, B), block = 256.
@@ -515,13 +535,16 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
 
   __shared__ unsigned s_hist[16 * 256];
   __shared__ float s_cv[16][CH];  // candidates of the chunk per head (cand_chunk)
-  __shared__ int s_cc[16];
+  __shared__ int s_cc[16], s_ac[16];
   for (int e = tid; e < 16 * 256; e += kBlock) s_hist[e] = 0u;
-  if (tid < 16) s_cc[tid] = 0;
+  if (tid < 16) {
+    s_cc[tid] = 0;
+    s_ac[tid] = 0;
+  }
 
   const bool live = hh < nh;
-  // the guessed bin (256: none, no top digit equals it)
-  const unsigned db = a.cand_chunk && a.tau && live ? order_key(a.tau[row0 + hh]) >> 24 : 256u;
+  uint32_t wlo = 1u, whi = 0u;  // the guessed window (empty: none)
+  const bool wok = a.cand_chunk && a.tau && live && guess_window(a.tau[row0 + hh], wlo, whi);
   if constexpr (!SPEC) {
     qk.load_q(reinterpret_cast<const T*>(a.q) + (size_t)row0 * D, nh, lane);
     score_tiles<T, D, TPW>(sc, qk, kh, wbase, L, lane, a.scale);
@@ -530,6 +553,7 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
 
   if (live) {
     float* srow = a.scores + (long long)(row0 + hh) * a.lpad;
+    int above = 0;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       floatx4 v = sc[t];
@@ -537,15 +561,17 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int key = wbase + 16 * t + 4 * kq + r;
         if (key < L) {
-          const unsigned top = order_key(v[r]) >> 24;
-          atomicAdd(&s_hist[hh * 256 + top], 1u);
-          if (top == db) s_cv[hh][atomicAdd(&s_cc[hh], 1)] = v[r];
+          const uint32_t ok = order_key(v[r]);
+          atomicAdd(&s_hist[hh * 256 + (ok >> 24)], 1u);
+          if (ok >= wlo && ok <= whi) s_cv[hh][atomicAdd(&s_cc[hh], 1)] = v[r];
+          else if (wok && ok > whi) ++above;
         } else {
           v[r] = -INFINITY;
         }
       }
       *reinterpret_cast<floatx4*>(srow + wbase + 16 * t + 4 * kq) = v;
     }
+    if (above) atomicAdd(&s_ac[hh], above);
   }
   __syncthreads();
   for (int e = tid; e < nh * 256; e += kBlock) {
@@ -560,7 +586,7 @@ __global__ __launch_bounds__(kBlock) void k_scores_hist(const StreamArgs a) {
     if (h < nh) {
       const int n = s_cc[h];
       const long long r = row0 + h;
-      if (sub == 0) a.cand_cnt[r * a.nsel + c] = (unsigned)n;
+      if (sub == 0) a.cand_cnt[r * a.nsel + c] = (unsigned)n | ((unsigned)s_ac[h] << 16);
       float* dst = a.surv_val + r * a.lpad + (long long)c * CH;
       for (int i = sub; i < n; i += 16) dst[i] = s_cv[h][i];
     }
@@ -637,16 +663,17 @@ __global__ __launch_bounds__(kBlock) void k_cand_collect(const StreamArgs a) {
   for (int i = tid; i < cnt; i += kBlock) a.surv_val[rbase + lo + i] = s_cand[i];
 }
 
-// Refresh, pass 3: the remaining 24 bits of the N-th largest logit resolved on the
-// candidates (counting repeats). The slices' candidate counts give each slice's
-// place in the row's candidate list (a block scan); a group of threads per slice
-// copies the candidates into LDS, or, past kCandLds of them, first finds the second
-// digit on the candidates in place and stages only that digit's. The counts, the
-// first round of candidate loads and the histogram are all requested at once. When
-// k_scores_hist guessed the bin (cand_chunk) and the histogram shows another, the
-// block collects the bin's logits from the row's stored logits instead. Writes tau
-// (-inf when N >= l_kv, unchanged when l_kv == 0) and returns the row's histogram
-// copies to zero. grid = (h_q, B), block = 1024.
+// Refresh, pass 3: the N-th largest logit (counting repeats) resolved on the
+// candidates. The slices' candidate counts give each slice's place in the row's
+// candidate list (a block scan); a group of threads per slice copies the candidates
+// into LDS, or, past kCandLds of them, first finds the next digit on the candidates in
+// place and stages only that digit's; a radix select resolves the remaining bits. The
+// counts, the first round of candidate loads, the histogram and the threshold passed
+// in are all requested at once. When k_scores_hist guessed a window (cand_chunk) that
+// does not hold the N-th largest, the block collects the logits of its histogram bin
+// from the row's stored logits instead. Writes tau (-inf when N >= l_kv, unchanged
+// when l_kv == 0) and returns the row's histogram copies to zero.
+// grid = (h_q, B), block = 1024.
 constexpr int kMaxSel = 4096;  // candidate slices of a row at most
 
 __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs a, float* tau_out) {
@@ -661,6 +688,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
 
   __shared__ unsigned s_hist[256];
   __shared__ int s_itmp[NT / kWave];
+  __shared__ int s_itmp2[2 * (NT / kWave)];
   __shared__ unsigned s_res[2];
   __shared__ unsigned s_stage;
   __shared__ float s_cand[kCandLds];
@@ -725,12 +753,23 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
     if (tid == 0) tau_out[row] = -INFINITY;
     return;
   }
-  // places of the slices in the candidate list: thread t holds slices t*PER ..
+  // a slice's count word: its candidates, and with cand_chunk in the upper 16 bits the
+  // logits above the guessed window
+  int above = 0;
+  if (a.cand_chunk) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      above += (int)((unsigned)c[u] >> 16);
+      c[u] &= 0xffff;
+    }
+  }
+  // places of the slices in the candidate list (thread t holds slices t*PER ..), the
+  // row's candidates C and its logits above the window A
   int mine = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) mine += c[u];
-  int C;
-  int off = block_excl_scan<NT>(mine, s_itmp, C);
+  int C, A;
+  int off = block_excl_scan2<NT>(mine, above, s_itmp2, C, A).x;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int sl = tid * PER + u;
@@ -742,7 +781,19 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
   digit_of_kth_largest<NT>(s_hist, (unsigned)N, s_itmp, s_res);
   const unsigned d1 = s_res[0], k1 = s_res[1];
   const unsigned c1 = s_hist[d1];  // the row's logits in bin d1
-  const unsigned db = a.cand_chunk ? order_key(tprev) >> 24 : 256u;  // the guessed bin
+  // Where the select starts: the candidates of top byte d1 (the bin of the N-th
+  // largest), resolving the lower 24 bits. Candidates per slice are that bin: rank k1.
+  // Candidates in the guessed window: the guess holds when the window holds the N-th
+  // largest (A < N <= A + C). The window then spans d1 and at most one neighbour
+  // byte. If it reaches above d1, all of bin d1 lies below its top: every logit
+  // above the N-th largest in bin d1 is in the window, rank k1. Otherwise the
+  // logits above the window are exactly those above the window's part of bin d1:
+  // rank N - A.
+  uint32_t lo = 1u, hi = 0u;
+  const bool wok = a.cand_chunk && guess_window(tprev, lo, hi);
+  const bool hit = !a.cand_chunk || (wok && A < N && N <= A + C);
+  const uint32_t p0 = d1 << 24, m0 = 0xff000000u;
+  const unsigned k0 = (a.cand_chunk && (hi >> 24) == d1) ? (unsigned)(N - A) : k1;
   float* gcand = reinterpret_cast<float*>(a.surv_idx) + row * a.lpad;  // free at this point
   // f(place, logit) for every candidate of the slices, kQ 16-byte loads of a thread
   // at once (the places past a slice's count that they cover are skipped)
@@ -770,7 +821,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
     }
   };
   uint32_t key;
-  if (a.cand_chunk && d1 != db) {
+  if (!hit) {
     // the guess missed: the bin's logits, c1 of them, from the row's stored logits
     if (tid == 0) s_stage = 0u;
     __syncthreads();
@@ -803,33 +854,36 @@ __global__ __launch_bounds__(kRowThreads) void k_select_finish(const StreamArgs 
   } else if (C <= kCandLds) {
     each_cand([&](int i, float x) { s_cand[i] = x; });
     __syncthreads();
-    key = radix_select_block<NT>(s_cand, (long long)C, d1 << 24, 0xff000000u, 16, k1, s_hist, s_itmp, s_res);
+    key = radix_select_block<NT>(s_cand, (long long)C, p0, m0, 16, k0, s_hist, s_itmp, s_res);
   } else {
-    // Too many for LDS: the second digit is found on the candidates where they lie,
-    // and only that digit's candidates are staged (in LDS, or past kCandLds of them,
-    // as with many equal logits, in the row's kept-index buffer) for the last two.
+    // Too many for LDS: the next digit is found on the candidates where they lie, and
+    // only that digit's candidates are staged (in LDS, or past kCandLds of them, as
+    // with many equal logits, in the row's kept-index buffer) for the rest.
     __syncthreads();  // every thread has read s_hist[d1]
     if (tid < 256) s_hist[tid] = 0u;
     __syncthreads();
-    each_cand([&](int, float x) { atomicAdd(&s_hist[(order_key(x) >> 16) & 255u], 1u); });
+    each_cand([&](int, float x) {
+      const uint32_t ok = order_key(x);
+      if ((ok & m0) == p0) atomicAdd(&s_hist[(ok >> 16) & 255u], 1u);
+    });
     __syncthreads();
-    digit_of_kth_largest<NT>(s_hist, k1, s_itmp, s_res);
+    digit_of_kth_largest<NT>(s_hist, k0, s_itmp, s_res);
     const unsigned d2 = s_res[0], k2 = s_res[1];
     const unsigned c2 = s_hist[d2];
-    const uint32_t top = (d1 << 8) | d2;
+    const uint32_t p2 = p0 | (d2 << 16), m2 = m0 | (255u << 16);
     if (tid == 0) s_stage = 0u;
     __syncthreads();  // every thread has read s_res and s_hist; the counter is zero
     const bool in_lds = c2 <= (unsigned)kCandLds;
     each_cand([&](int, float x) {
-      if ((order_key(x) >> 16) == top) {
+      if ((order_key(x) & m2) == p2) {
         const unsigned at = atomicAdd(&s_stage, 1u);
         if (in_lds) s_cand[at] = x;
         else gcand[at] = x;
       }
     });
     __syncthreads();
-    key = in_lds ? radix_select_block<NT>(s_cand, (long long)c2, top << 16, 0xffff0000u, 8, k2, s_hist, s_itmp, s_res)
-                 : radix_select_block<NT>(gcand, (long long)c2, top << 16, 0xffff0000u, 8, k2, s_hist, s_itmp, s_res);
+    key = in_lds ? radix_select_block<NT>(s_cand, (long long)c2, p2, m2, 8, k2, s_hist, s_itmp, s_res)
+                 : radix_select_block<NT>(gcand, (long long)c2, p2, m2, 8, k2, s_hist, s_itmp, s_res);
   }
   if (tid == 0) tau_out[row] = order_key_to_f32(key);
 }

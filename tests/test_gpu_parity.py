@@ -302,15 +302,17 @@ def test_refresh_with_more_candidates_than_lds():
     compare(got1, ref1, x, "bf16", check_tau=False)
 
 
-@pytest.mark.parametrize("hint", ["exact", "zero", "huge", "nan", "minus_inf"])
+@pytest.mark.parametrize("hint", ["exact", "above", "below", "far", "zero", "huge", "nan", "minus_inf"])
 def test_refresh_result_does_not_depend_on_previous_threshold(hint):
-    # a refresh reads the threshold passed in only to guess the bin of the new one (a
-    # right guess saves a pass over the logits); whatever it holds, the refreshed
-    # threshold, the kept sets and the outputs are the oracle's
+    # a refresh reads the threshold passed in only to guess a window around the new
+    # one (a right guess saves a pass over the logits): the exact one and ones 10%
+    # above or 8% below it fall inside, the others not; whatever it holds, the
+    # refreshed threshold, the kept sets and the outputs are the oracle's
     w, x = small(2, 8, 2, 4, 64, [3000, 1701], "bf16", seed=39)
     N = 24
     ref = oracle_step(x, N, 4, 0)
-    tau_in = {"exact": ref.tau, "zero": np.zeros_like(ref.tau), "huge": np.full_like(ref.tau, 1e30),
+    tau_in = {"exact": ref.tau, "above": ref.tau * 1.1, "below": ref.tau * 0.92, "far": ref.tau * 1.5,
+              "zero": np.zeros_like(ref.tau), "huge": np.full_like(ref.tau, 1e30),
               "nan": np.full_like(ref.tau, np.nan), "minus_inf": np.full_like(ref.tau, -np.inf)}[hint]
     g = GpuCase(x, N)
     got = g.step(4, 0, tau_in=tau_in)
