@@ -971,9 +971,9 @@ def main() -> int:
         api.decode_attn(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, refresh_period=1, step=t,
                         max_l_kv=L, out=out, workspace=ws)
 
-    # a refresh reads the threshold passed in as a guess of the new one's top-digit bin
-    # (two octaves wide); alternating q and 4 q (exact in bf16: every logit times 4) on
-    # one shared threshold makes every guess miss, the refresh's slowest path
+    # a refresh reads the threshold passed in as a guess of a window around the new one
+    # (a quarter octave either way); alternating q and 4 q (exact in bf16: every logit
+    # times 4) on one shared threshold makes every guess miss, the refresh's slowest path
     q4 = [qs[0], qs[0] * 4]
     tau_miss = taus[0].clone()
 
@@ -1010,7 +1010,7 @@ def main() -> int:
         Km = min(K, 512)
         ms = time_graph(torch, lambda: [refresh_miss_step(t) for t in range(W, W + Km)], args.reps)
         res["refresh_miss_us"] = pct([1e3 * m / Km for m in ms], 50)
-        log(f"refresh step whose guessed bin misses: {res['refresh_miss_us']:.2f} us/step")
+        log(f"refresh step whose guessed window misses: {res['refresh_miss_us']:.2f} us/step")
     if args.only == "steady":
         ms = time_graph(torch, lambda: [steady_step(t) for t in range(W, W + K)], args.reps)
         res["steady_us"] = pct([1e3 * m / K for m in ms], 50)
