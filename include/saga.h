@@ -97,7 +97,10 @@ saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream);
  *     threshold refresh: when step % refresh_period == 0, tau[b,j] is recomputed as the
  *     N-th largest fp32 logit of its row (-inf when N >= l_kv[b]) before selecting;
  *     otherwise the tau passed in is used as is.
- *   tau [B,h_q] in/out: the per-(sequence, query head) threshold state.
+ *   tau [B,h_q] in/out: the per-(sequence, query head) threshold state. At a refresh
+ *     step the value passed in only guesses where the new threshold lies (a refresh whose
+ *     threshold moved little since the last one takes the faster path); the results
+ *     never depend on it.
  *   Kept set S[b,j] = { i < l_kv[b] : A[b,j,i] >= tau[b,j] } (ties kept). If a stale
  *     threshold keeps nothing, that row is refreshed exactly at this step.
  *   out [B,h_q,d_v] (out_dtype): eq. (7) over S.
@@ -141,7 +144,9 @@ saga_status saga_decode_attn_noalloc(const saga_shape* s, const void* q, const v
 
 /* The exact threshold alone (section "Methodology > Atop-N Attention", refresh step):
  * tau[b,j] = N-th largest fp32 logit of row (b,j), counting repeats; -inf when
- * N >= l_kv[b]; unchanged when l_kv[b] == 0. */
+ * N >= l_kv[b]; unchanged when l_kv[b] == 0. The value tau holds on entry only guesses
+ * where the new one lies (as for saga_decode_attn); any value, NaN included, gives the
+ * same result. */
 saga_status saga_refresh_threshold(const saga_shape* s, const void* q, const void* k,
                                    const int32_t* l_kv, int32_t max_l_kv, int32_t N,
                                    float* tau, void* workspace, size_t workspace_bytes,

@@ -320,6 +320,41 @@ def test_refresh_result_does_not_depend_on_previous_threshold(hint):
     assert np.all(got["flags"] == 1)
 
 
+def test_refresh_window_across_a_top_byte_boundary():
+    # Thresholds near 2.0, where the top byte of the order key changes: the window
+    # guessed around a threshold passed in (about 19% either way) then holds logits of
+    # two top bytes, and the finishing select ranks the N-th largest among the
+    # candidates of its own byte, by the histogram's rank below the boundary and by
+    # the count above the window above it. The thresholds passed in are the exact
+    # ones; every row is compared with the oracle, and the rows are checked to fall
+    # on both sides of the boundary.
+    w, x = small(2, 8, 2, 4, 64, [6000, 5003], "bf16", seed=41, plant=0.0)
+    seen = {"below": 0, "above": 0}
+    for N in (90, 110, 130, 150, 170):
+        ref = oracle_step(x, N, 1, 0)
+        g = GpuCase(x, N, sel_cap=4 * N)
+        got = g.step(1, 0, tau_in=ref.tau)
+        compare(got, ref, x, "bf16", check_tau=True)
+        t = ref.tau[np.isfinite(ref.tau)]
+        seen["below"] += int(np.sum((t > 2.0 * 2 ** -0.25) & (t < 2.0)))
+        seen["above"] += int(np.sum((t >= 2.0) & (t < 2.0 * 2 ** 0.25)))
+    assert seen["below"] > 0 and seen["above"] > 0, seen
+
+
+def test_refresh_window_with_negative_thresholds():
+    # N = 3/4 of the row: the thresholds are negative logits; the window around a
+    # threshold passed in (the exact one, 5% larger or smaller in magnitude) holds
+    # the new one, and the result is the oracle's
+    w, x = small(1, 8, 2, 4, 64, [4000], "bf16", seed=42, plant=0.0)
+    N = 3000
+    ref = oracle_step(x, N, 1, 0)
+    assert np.all(ref.tau < 0)
+    for f in (1.0, 1.05, 0.95):
+        g = GpuCase(x, N, sel_cap=4000)
+        got = g.step(1, 0, tau_in=ref.tau * f)
+        compare(got, ref, x, "bf16", check_tau=True)
+
+
 def test_ties_beyond_lds_capacity():
     # 9000 identical keys: all logits of a row are one value, so all 9000 are
     # threshold candidates sharing their second digit too, staged in the row's
