@@ -388,17 +388,21 @@ def traffic_record(args) -> int:
     w_k = next(v for (k, c), v in ws.items() if name in k and c == "WRITE_SIZE")
     traffic = f_k[0] * 1024 * fetch_scale + w_k[0] * 1024 * write_scale
     alg = args.alg_bytes
+
+    def outdir(csv_path):  # the -d directory of the rocprofv3 run that wrote csv_path
+        return os.path.relpath(os.path.dirname(os.path.abspath(csv_path)), ROOT)
+
     lines = [
         "# HBM traffic of k_qk_select<bf16, d=128, speculative keys, gather> (saga_select_gather) on the",
         "# Qwen2.5-1.5B-shaped layer at l_kv=128K (rotating input sets, so K and V come from HBM).",
         "#",
         "# counter passes (repository root), one counter per run:",
-        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_sel_f -o p --output-format csv -- \\",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir(f_sel)} -o p --output-format csv -- \\",
         "#       python3 -u bench.py --only select --steps 256 --warmup 8 --reps 1 --no-cpu-baseline",
-        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_sel_w -o p --output-format csv -- (the same)",
-        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_copy_f -o p --output-format csv -- \\",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir(w_sel)} -o p --output-format csv -- (the same)",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir(f_copy)} -o p --output-format csv -- \\",
         "#       python3 -u bench.py --probe copy --steps 8",
-        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_copy_w -o p --output-format csv -- (the same)",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir(w_copy)} -o p --output-format csv -- (the same)",
         "#   python3 bench.py --traffic-record <the four counter_collection.csv> --alg-bytes <B>",
         "# calibration: a 256 MiB device copy reads and writes 262144 KiB per dispatch;",
         f"#   FETCH_SIZE reads {cf_copy[0]:.1f} KiB (scale {fetch_scale:.5f}), "
