@@ -51,15 +51,24 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn steps/s + % HBM roofline at l_kv=128K, bs=1 (SAGA+Atop-N vs dense GQA)"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_qk_select_gather_qwen128k_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_qk_select_qwen128k_traffic.txt")
 DEFAULT_WORKLOAD = "qwen2.5-1.5b-shape-l128k"
 
 
-def dominant_kernel(w) -> str:
-    """Name of the select kernel a workload's step spends most of its time in."""
+def dominant_kernel(w, form: str) -> str:
+    """Name of the select kernel a workload's step spends most of its time in; `form`
+    is the step's value gather, "late" (slot records, the combining kernel gathers) or
+    "early" (the select kernel gathers into chunk records)."""
     dims = f"d={w.d}" if w.dv == w.d else f"d_k={w.d}, d_v={w.dv}"
     keys = "speculative keys" if w.batch == 1 else "keys after l_kv"
-    return f"k_qk_select<{w.dtype}, {dims}, {keys}, gather> (saga_select_gather)"
+    out = "slot records" if form == "late" else "gather"
+    return f"k_qk_select<{w.dtype}, {dims}, {keys}, {out}> (saga_select_gather)"
+
+
+def select_kernel_pattern(form: str) -> str:
+    """The dominant kernel's name in rocprofv3 output at the default workload (bf16,
+    d = 128, speculative keys, contiguous caches)."""
+    return f"k_qk_select<unsigned short, 128, 128, 1, {2 if form == 'late' else 1}, false"
 
 
 def log(msg: str) -> None:
@@ -381,7 +390,7 @@ def traffic_record(args) -> int:
     cf_copy = next(v for (k, c), v in cf.items() if "copyBuffer" in k and c == "FETCH_SIZE")
     cw_copy = next(v for (k, c), v in cw.items() if "copyBuffer" in k and c == "WRITE_SIZE")
     fetch_scale, write_scale = copy_kib / cf_copy[0], copy_kib / cw_copy[0]
-    name = "k_qk_select<unsigned short, 128, 128, 1, true, false"  # speculative keys, gather, contiguous
+    name = select_kernel_pattern(args.form)
     fs = counter_averages(f_sel)
     ws = counter_averages(w_sel)
     f_k = next(v for (k, c), v in fs.items() if name in k and c == "FETCH_SIZE")
@@ -392,9 +401,12 @@ def traffic_record(args) -> int:
     def outdir(csv_path):  # the -d directory of the rocprofv3 run that wrote csv_path
         return os.path.relpath(os.path.dirname(os.path.abspath(csv_path)), ROOT)
 
+    kept = "kept-entry slot records (late value gather)" if args.form == "late" else \
+        "value gather into chunk records (early value gather)"
     lines = [
-        "# HBM traffic of k_qk_select<bf16, d=128, speculative keys, gather> (saga_select_gather) on the",
-        "# Qwen2.5-1.5B-shaped layer at l_kv=128K (rotating input sets, so K and V come from HBM).",
+        f"# HBM traffic of k_qk_select<bf16, d=128, speculative keys, {kept}> (saga_select_gather),",
+        "# the select kernel of a step that reuses the threshold, on the Qwen2.5-1.5B-shaped layer at",
+        "# l_kv=128K (rotating input sets, so the caches are read from HBM).",
         "#",
         "# counter passes (repository root), one counter per run:",
         f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir(f_sel)} -o p --output-format csv -- \\",
@@ -403,14 +415,15 @@ def traffic_record(args) -> int:
         f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir(f_copy)} -o p --output-format csv -- \\",
         "#       python3 -u bench.py --probe copy --steps 8",
         f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir(w_copy)} -o p --output-format csv -- (the same)",
-        "#   python3 bench.py --traffic-record <the four counter_collection.csv> --alg-bytes <B>",
+        f"#   python3 bench.py --traffic-record <the four counter_collection.csv> --alg-bytes {alg} --form {args.form}",
         "# calibration: a 256 MiB device copy reads and writes 262144 KiB per dispatch;",
         f"#   FETCH_SIZE reads {cf_copy[0]:.1f} KiB (scale {fetch_scale:.5f}), "
         f"WRITE_SIZE reads {cw_copy[0]:.1f} KiB (scale {write_scale:.5f})",
         "# traffic = FETCH_SIZE * 1024 * fetch_scale + WRITE_SIZE * 1024 * write_scale",
     ]
     if alg:
-        lines.append(f"# algorithmic bytes per launch (K stream + union of selected V rows) = {alg}")
+        what = "K stream" if args.form == "late" else "K stream + union of selected V rows"
+        lines.append(f"# algorithmic bytes per launch ({what}) = {alg}")
         lines.append(f"#   -> traffic / algorithmic = {traffic / alg:.3f}; reads alone = "
                      f"{f_k[0] * 1024 * fetch_scale / alg:.3f}")
     lines += [
@@ -692,8 +705,8 @@ def stages(torch, args) -> int:
     api.qk_select(q0, k0, l_kv, tau, max_l_kv=L, workspace=ws, d_v=w.dv)  # the kept lists the gather reads
     res["sparse_gather"] = timed(lambda t: api.sparse_gather(q0, ks[t % R], vs[t % R], l_kv, tau, N=w.N, max_l_kv=L,
                                                              out=out, workspace=ws))
-    res["select_gather"] = timed(lambda t: api.select_gather(q0, ks[t % R], vs[t % R], l_kv, tau, max_l_kv=L,
-                                                             workspace=ws))
+    res["select_gather"] = timed(lambda t: api.select_gather(q0, ks[t % R], vs[t % R], l_kv, tau, N=w.N,
+                                                             max_l_kv=L, workspace=ws))
     res["split_combine"] = timed(lambda t: api.split_combine(q0, ks[t % R], vs[t % R], l_kv, tau, N=w.N, max_l_kv=L,
                                                              out=out, workspace=ws))
     for k, v in res.items():
@@ -872,6 +885,8 @@ def main() -> int:
     ap.add_argument("--traffic-record", nargs=4, metavar=("SEL_FETCH", "SEL_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the dominant kernel's traffic record from four counter_collection csv files")
     ap.add_argument("--alg-bytes", type=int, default=0, help="algorithmic bytes per launch (--traffic-record)")
+    ap.add_argument("--form", choices=["late", "early"], default="late",
+                    help="value-gather form of the select kernel of --traffic-record")
     ap.add_argument("--out", default=None, help="output file of --traffic-record (default: the profiles record)")
     ap.add_argument("--sweep", action="store_true",
                     help="SAGA vs dense step time over l_kv x N x refresh period (one JSON line)")
@@ -947,6 +962,7 @@ def main() -> int:
     taus = [torch.zeros(w.batch, w.h_q, dtype=torch.float32, device=dev) for _ in range(R)]
     out = torch.empty(w.batch, w.h_q, w.dv, dtype=q0.dtype, device=dev)
     shape = api.make_shape(q0, k0, v0)
+    form = api.gather_form(shape, w.N, L)
     ws = api.Workspace(shape, w.N, L, dev)
     for r in range(R):
         api.refresh_threshold(qs[r], ks[r], l_kv, taus[r], N=w.N, max_l_kv=L, workspace=ws, d_v=w.dv)
@@ -964,7 +980,7 @@ def main() -> int:
 
     def select_only(t):
         r = t % R
-        api.select_gather(qs[r], ks[r], vs[r], l_kv, taus[r], max_l_kv=L, workspace=ws)
+        api.select_gather(qs[r], ks[r], vs[r], l_kv, taus[r], N=w.N, max_l_kv=L, workspace=ws)
 
     def combine_only(t):
         r = t % R
@@ -1104,11 +1120,13 @@ def main() -> int:
     traffic, traffic_src = recorded_traffic() if w.name == DEFAULT_WORKLOAD else (None, None)
     roof = None
     if "select_us" in res:
-        achieved = bytes_step / (res["select_us"] * 1e-6) / 1e9
+        # the late gather's select kernel reads the keys; the early one also the selected value rows
+        bytes_sel = bytes_k if form == "late" else bytes_step
+        achieved = bytes_sel / (res["select_us"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": dominant_kernel(w),
-                "kernel_us": res["select_us"], "bytes_per_launch": bytes_step,
+                "kernel": dominant_kernel(w, form),
+                "kernel_us": res["select_us"], "bytes_per_launch": bytes_sel,
                 "traffic_source": traffic_src}
     line = {
         "metric": METRIC,
@@ -1138,6 +1156,7 @@ def main() -> int:
         "us_per_step_natural_rate": res.get("natural_us"),
         "us_select_kernel": res.get("select_us"),
         "us_combine_kernel": res.get("combine_us"),
+        "value_gather": form,
         "bytes_per_step": bytes_step,
         "bytes_k": bytes_k,
         "bytes_selected_v_union": bytes_v,

@@ -88,6 +88,13 @@ const char* saga_status_str(int32_t status);
  * a smaller max_l_kv (a growing decode context allocates once). */
 size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv);
 
+/* The form of the value gather that saga_decode_attn (and saga_select_gather with
+ * saga_split_combine) takes for `s`, top-N size N and max_l_kv: 1 for the late gather
+ * (the combining kernel reads the kept value rows), 0 for the early gather (the
+ * select kernel does), -1 if the arguments are invalid. Pure host arithmetic; the
+ * results of the step do not depend on the form beyond the rounding of its sums. */
+int32_t saga_gather_form(const saga_shape* s, int32_t N, int32_t max_l_kv);
+
 /* Enqueue a zero fill of `bytes` bytes of `workspace` (first-use initialisation). */
 saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream);
 
@@ -163,8 +170,9 @@ saga_status saga_dense_gqa_attn(const saga_shape* s, const void* q, const void* 
                                 void* stream);
 
 /* The two stages of a non-refresh decode step, callable separately on one stream
- * with one workspace (saga_decode_attn with step % refresh_period != 0 is exactly
- * saga_qk_select followed by saga_sparse_gather).
+ * with one workspace: saga_qk_select followed by saga_sparse_gather computes the step
+ * of saga_decode_attn with step % refresh_period != 0 (the same kept sets, counts and
+ * flags; outputs equal up to the rounding of sums taken in another order).
  * saga_qk_select: scores every cached key of the h_k key heads (eq. (2)) and keeps,
  *   per query head, the entries >= tau into the workspace (Atop-N comparison step).
  * saga_sparse_gather: softmax over the kept entries and the gather of their value
@@ -181,19 +189,25 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
 
 /* The two kernels of a step that reuses the threshold, callable separately on one
  * stream with one workspace (saga_decode_attn with step % refresh_period != 0 is
- * exactly saga_select_gather followed by saga_split_combine).
- * saga_select_gather: eq. (2) logits of every cached key, the comparison with tau,
- *   and for each run of cached keys (the kernel's chunk) and query head the part of
- *   eq. (7) over the chunk's kept entries, relative to the chunk's largest kept logit
- *   m_c: sum exp(A_i - m_c) V[i,:] and sum exp(A_i - m_c), into the workspace.
- * saga_split_combine: the log-sum-exp merge of those chunk parts into out
- *   (O = sum_c e_c o_c / sum_c e_c z_c, e_c = exp(m_c - max_c m_c)); outputs as in
- *   saga_decode_attn (flags bit 0 is never set here). q, k, N and tau are needed for
- *   the forced refresh of a row that kept nothing. */
+ * exactly saga_select_gather followed by saga_split_combine with the same N). Both
+ * take one of two forms, chosen from the shape, N and max_l_kv exactly as
+ * saga_decode_attn chooses it: a head expected to keep at most 2 entries per run of
+ * cached keys (the kernel's chunk, 128 to 512 keys), on rows of at most 512 such runs,
+ * takes the late value gather; other selections the early one.
+ * saga_select_gather: eq. (2) logits of every cached key and the comparison with tau,
+ *   then per chunk and query head, into the workspace:
+ *   - early gather: the part of eq. (7) over the chunk's kept entries relative to
+ *     their largest logit m_c, sum exp(A_i - m_c) V[i,:] and sum exp(A_i - m_c);
+ *   - late gather: the kept (index, logit) pairs, their count and largest logit.
+ * saga_split_combine: eq. (7) into out; early gather: the log-sum-exp merge of the
+ *   chunk parts (O = sum_c e_c o_c / sum_c e_c z_c, e_c = exp(m_c - max_c m_c)); late
+ *   gather: exp(A_i - M) with M the row's largest kept logit, and the gather of the
+ *   kept value rows. Outputs as in saga_decode_attn (flags bit 0 is never set here).
+ *   q, k, N and tau are needed for the forced refresh of a row that kept nothing. */
 saga_status saga_select_gather(const saga_shape* s, const void* q, const void* k,
                                const void* v, const int32_t* l_kv, int32_t max_l_kv,
-                               const float* tau, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               int32_t N, const float* tau, void* workspace,
+                               size_t workspace_bytes, void* stream);
 saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k,
                                const void* v, const int32_t* l_kv, int32_t max_l_kv,
                                int32_t N, float* tau, void* out, int32_t* sel_count,

@@ -21,7 +21,7 @@ EXPORTS = ("saga_status_str", "saga_workspace_bytes", "saga_workspace_init", "sa
            "saga_select_gather", "saga_split_combine", "saga_decode_attn_paged", "saga_dense_gqa_attn_paged",
            "saga_linear", "saga_qkv_append", "saga_layer_workspace_bytes", "saga_decode_layer",
            "saga_merge_workspace_bytes", "saga_merge_losses", "saga_min_weight_pairing", "saga_merge_keys",
-           "saga_decode_attn_noalloc")
+           "saga_decode_attn_noalloc", "saga_gather_form")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SAGA_NOALLOC_SCRATCH_BYTES of include/saga.h
 ATTN_ATOPN, ATTN_DENSE = 0, 1
 FLAG_REFRESHED, FLAG_FORCED = 1, 2
@@ -63,6 +63,7 @@ _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "saga_status_str": (ctypes.c_char_p, [_I32]),
     "saga_workspace_bytes": (_SZ, [_P, _I32, _I32]),
+    "saga_gather_form": (_I32, [_P, _I32, _I32]),
     "saga_workspace_init": (_I32, [_P, _SZ, _P]),
     "saga_decode_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_decode_attn_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P]),
@@ -70,7 +71,7 @@ _SIGS = {
     "saga_dense_gqa_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_qk_select": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_sparse_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
-    "saga_select_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "saga_select_gather": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "saga_split_combine": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "saga_decode_attn_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P,
                                       _SZ, _P]),
@@ -169,6 +170,14 @@ def workspace_bytes(shape: SagaShape, N: int, max_l_kv: int) -> int:
     if n == 0:
         raise ValueError("invalid shape for the workspace")
     return int(n)
+
+
+def gather_form(shape: SagaShape, N: int, max_l_kv: int) -> str:
+    """"late" or "early": where the decode step gathers the kept value rows (saga_gather_form)."""
+    f = lib().saga_gather_form(ctypes.byref(shape), int(N), int(max_l_kv))
+    if f < 0:
+        raise ValueError("invalid shape, N or max_l_kv")
+    return "late" if f == 1 else "early"
 
 
 class Workspace:
@@ -314,13 +323,14 @@ def sparse_gather(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
     return out
 
 
-def select_gather(q, k, v, l_kv, tau, *, max_l_kv: Optional[int] = None, workspace: Optional[Workspace] = None,
-                  scale: float = 0.0, stream=None):
-    """saga_select_gather: scoring, threshold comparison and the per-chunk parts of the
-    softmax-weighted value sum (into the workspace)."""
+def select_gather(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None,
+                  workspace: Optional[Workspace] = None, scale: float = 0.0, stream=None):
+    """saga_select_gather: scoring, threshold comparison and, per chunk, either the parts
+    of the softmax-weighted value sum (early gather) or the kept (index, logit) pairs
+    (late gather), into the workspace; N chooses the form as in decode_attn."""
     shape, max_l_kv, _ = _prep(q, k, v, l_kv, tau, None, None, max_l_kv, scale, need_out=False)
-    ws = _ws(workspace, shape, 1, max_l_kv, q.device)
-    st = lib().saga_select_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv,
+    ws = _ws(workspace, shape, N, max_l_kv, q.device)
+    st = lib().saga_select_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(l_kv), max_l_kv, int(N),
                                   _ptr(tau), _ptr(ws.buf), ws.nbytes, _stream(q.device, stream))
     _check(st, "saga_select_gather")
 
@@ -328,7 +338,7 @@ def select_gather(q, k, v, l_kv, tau, *, max_l_kv: Optional[int] = None, workspa
 def split_combine(q, k, v, l_kv, tau, *, N: int, max_l_kv: Optional[int] = None, out=None, out_dtype=None,
                   sel_count=None, sel_idx=None, flags=None, workspace: Optional[Workspace] = None,
                   scale: float = 0.0, stream=None):
-    """saga_split_combine: merges the chunk parts left by saga_select_gather into `out`."""
+    """saga_split_combine: eq. (7) into `out` from what saga_select_gather left (same N)."""
     shape, max_l_kv, out = _prep(q, k, v, l_kv, tau, out, out_dtype, max_l_kv, scale)
     cap = _row_outputs(shape.batch, shape.h_q, sel_count, sel_idx, flags)
     ws = _ws(workspace, shape, N, max_l_kv, q.device)

@@ -228,6 +228,22 @@ int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
   return hsplit < 1 ? 1 : hsplit;
 }
 
+// The late value gather (k_qk_select<kOutSlots> -> k_sparse_pv): the select kernel
+// leaves each chunk's kept (index, logit) pairs in a slot record and the combining
+// kernel gathers the kept value rows. Taken when a head is expected to keep at most
+// kLateMaxKept entries per chunk (CH * N / max_l_kv) and a row has at most
+// kPvGroupRecs * 64 chunks (one slot record per thread piece). Denser selections keep
+// the early gather (k_qk_select<kOutRecords> -> k_split_combine), which spreads many
+// value rows per chunk over the select kernel's blocks. At the Qwen-shaped 128K layer
+// the late gather takes the value rows' dependent round trip out of the key stream.
+constexpr int kLateMaxKept = 2;
+
+bool late_gather(const Layout& w, int N, int max_l_kv) {
+  if (max_l_kv <= 0 || w.nch > kPvGroupRecs * (kBlock / 4)) return false;
+  const long long n = N < max_l_kv ? N : max_l_kv;
+  return (long long)w.ch * n <= (long long)kLateMaxKept * max_l_kv;
+}
+
 template <typename P>
 P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
@@ -288,7 +304,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.max_l_kv = max_l_kv;
   a.lpad = w.lpad;
   a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
-  a.hsplit = head_split(s, w, N, max_l_kv);
+  a.hsplit = late_gather(w, N, max_l_kv) ? 1 : head_split(s, w, N, max_l_kv);
   return a;
 }
 
@@ -320,20 +336,29 @@ void launch_refresh(const saga_shape* s, const Layout& w, const StreamArgs& a, f
   hipLaunchKernelGGL(k_select_finish, dim3(s->h_q, s->batch), dim3(kRowThreads), 0, st, a, tau);
 }
 
-// Scores and Atop-N comparison; with `gather` also the chunk records of eq. (7).
-void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, bool gather,
+// Scores and Atop-N comparison, leaving `out` (SelectOut): the kept lists only, the
+// chunk records of eq. (7) (early gather) or the slot records (late gather).
+template <int OUT, typename T, int DK, int DV, bool P, int W>
+void launch_select_out(const saga_shape* s, dim3 grid, const StreamArgs& a, bool from_scores, hipStream_t st) {
+  if (from_scores)
+    hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromScores, OUT, P, W>), grid, dim3(kBlock), 0, st, a);
+  else if (s->batch == 1)  // one sequence: its chunks reach max_l_kv, key loads need not wait for l_kv
+    hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeysSpeculative, OUT, P, W>), grid, dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeys, OUT, P, W>), grid, dim3(kBlock), 0, st, a);
+}
+
+void launch_select(const saga_shape* s, const Layout& w, const StreamArgs& a, bool from_scores, int out,
                    hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(a.ptab != nullptr, SAGA_TILES(w.W, {
     dim3 grid = stream_grid(s, w);
     grid.y *= a.hsplit;
-    if (!gather)
-      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeys, false, P, W>), grid, dim3(kBlock), 0, st, a);
-    else if (from_scores)
-      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromScores, true, P, W>), grid, dim3(kBlock), 0, st, a);
-    else if (s->batch == 1)  // one sequence: its chunks reach max_l_kv, key loads need not wait for l_kv
-      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeysSpeculative, true, P, W>), grid, dim3(kBlock), 0, st, a);
+    if (out == kOutList)
+      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeys, kOutList, P, W>), grid, dim3(kBlock), 0, st, a);
+    else if (out == kOutSlots)
+      launch_select_out<kOutSlots, T, DK, DV, P, W>(s, grid, a, from_scores, st);
     else
-      hipLaunchKernelGGL((k_qk_select<T, DK, DV, kFromKeys, true, P, W>), grid, dim3(kBlock), 0, st, a);
+      launch_select_out<kOutRecords, T, DK, DV, P, W>(s, grid, a, from_scores, st);
   });););
 }
 
@@ -344,9 +369,19 @@ void launch_chunk_gather(const saga_shape* s, const Layout& w, const StreamArgs&
   });););
 }
 
-void launch_combine(const saga_shape* s, const Layout& w, const GatherArgs& g, hipStream_t st) {
+// The merge of eq. (7): of the chunk records (early gather) or, with `late`, the value
+// gather over the slot records.
+void launch_combine(const saga_shape* s, const Layout& w, const GatherArgs& g, bool late, hipStream_t st) {
   SAGA_DISPATCH(s->dtype, s->d, value_dim(s), SAGA_PAGED(g.s.ptab != nullptr, SAGA_TILES(w.W, {
-    hipLaunchKernelGGL((k_split_combine<T, DK, DV, P, W>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, st, g);
+    if (late) {
+      // P blocks per row, a row's blocks on one XCD (k_sparse_pv)
+      const int per_row = DV * (int)sizeof(T) / 16;
+      hipLaunchKernelGGL((k_sparse_pv<T, DK, DV, P, W>), dim3(8 * ((g.rows + 7) / 8) * per_row), dim3(kBlock), 0, st,
+                         g);
+    }
+    else
+      hipLaunchKernelGGL((k_split_combine<T, DK, DV, P, W>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, st,
+                         g);
   });););
 }
 
@@ -362,6 +397,7 @@ GatherArgs gather_args(const saga_shape* s, const StreamArgs& sa, float* tau, vo
   g.sel_cap = sel_idx ? sel_cap : 0;
   g.out_bf16 = s->out_dtype == SAGA_BF16;
   g.refreshed = refreshed ? 1 : 0;
+  g.rows = s->batch * s->h_q;
   return g;
 }
 
@@ -378,11 +414,12 @@ saga_status decode_impl(const saga_shape* s, const saga_pages* pg, const void* q
   const bool refresh = (step % refresh_period) == 0;
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N, pg);
+  const bool late = late_gather(w, N, max_l_kv);
   if (max_l_kv > 0) {
     if (refresh) launch_refresh(s, w, a, tau, hs);
-    launch_select(s, w, a, refresh, true, hs);
+    launch_select(s, w, a, refresh, late ? kOutSlots : kOutRecords, hs);
   }
-  launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), hs);
+  launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, refresh), late, hs);
   return launched();
 }
 
@@ -483,6 +520,11 @@ size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv) {
   return layout(s, max_l_kv).total;
 }
 
+int32_t saga_gather_form(const saga_shape* s, int32_t N, int32_t max_l_kv) {
+  if (check_shape(s) != SAGA_OK || N < 1 || max_l_kv < 0 || max_l_kv > s->l_max) return -1;
+  return late_gather(layout(s, max_l_kv), N, max_l_kv) ? 1 : 0;
+}
+
 saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace) return SAGA_ERR_NULL;
   if (bytes == 0) return SAGA_OK;
@@ -565,7 +607,7 @@ saga_status saga_qk_select(const saga_shape* s, const void* q, const void* k, co
   const Layout w = layout(s, max_l_kv);
   (void)hipGetLastError();
   if (max_l_kv > 0)
-    launch_select(s, w, stream_args(s, w, workspace, q, k, nullptr, l_kv, max_l_kv, tau, 1), false, false,
+    launch_select(s, w, stream_args(s, w, workspace, q, k, nullptr, l_kv, max_l_kv, tau, 1), false, kOutList,
                   (hipStream_t)stream);
   return launched();
 }
@@ -583,21 +625,21 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
   if (max_l_kv > 0) launch_chunk_gather(s, w, a, hs);
-  launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false), hs);
+  launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false), false, hs);
   return launched();
 }
 
 saga_status saga_select_gather(const saga_shape* s, const void* q, const void* k, const void* v,
-                               const int32_t* l_kv, int32_t max_l_kv, const float* tau, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               const int32_t* l_kv, int32_t max_l_kv, int32_t N, const float* tau,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!s || !q || !k || !v || !l_kv || !tau) return SAGA_ERR_NULL;
-  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, 1);
+  saga_status st = check_common(s, max_l_kv, workspace, workspace_bytes, N);
   if (st != SAGA_OK) return st;
   const Layout w = layout(s, max_l_kv);
   (void)hipGetLastError();
   if (max_l_kv > 0)
-    launch_select(s, w, stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, 1), false, true,
-                  (hipStream_t)stream);
+    launch_select(s, w, stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N), false,
+                  late_gather(w, N, max_l_kv) ? kOutSlots : kOutRecords, (hipStream_t)stream);
   return launched();
 }
 
@@ -612,7 +654,8 @@ saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k
   const Layout w = layout(s, max_l_kv);
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
-  launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false), (hipStream_t)stream);
+  launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false),
+                 late_gather(w, N, max_l_kv), (hipStream_t)stream);
   return launched();
 }
 

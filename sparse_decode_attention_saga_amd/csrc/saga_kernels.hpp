@@ -58,6 +58,26 @@ struct __align__(16) ChunkHdr {
   int32_t unused;
 };
 
+// Kept entries of one chunk of one row (b, j) for the late value gather: the number
+// of kept entries, the largest kept logit and the first kSlotE kept (index, logit)
+// pairs in key order. 16-byte piece p of the record holds entries 2p-1 and 2p (piece
+// 0: the count, the maximum and entry 0), so four lanes read a record in one load
+// each. Entries past kSlotE stay in the chunk's segment of the kept list, at their
+// place in it.
+constexpr int kSlotE = 7;
+struct __align__(16) ChunkSlots {
+  int32_t cnt;
+  float mx;
+  int2 e[kSlotE];  // (key index, logit bits)
+};
+static_assert(sizeof(ChunkSlots) == 64, "four 16-byte pieces");
+
+// What k_qk_select leaves for the next kernel: the kept list in the chunk's segment
+// (the separate stages), chunk records of eq. (7) with the value rows gathered (the
+// early gather), or slot records whose value rows the combining kernel gathers (the
+// late gather).
+enum SelectOut { kOutList = 0, kOutRecords = 1, kOutSlots = 2 };
+
 // ----------------------------------------------------------------------------
 // Shared argument blocks (passed by value).
 
@@ -74,7 +94,8 @@ struct StreamArgs {
   int32_t* surv_idx;       // [B*h_q, lpad] kept indices, one CH-segment per chunk
   float* surv_val;         // [B*h_q, lpad] kept logits; also the threshold candidates
   ChunkHdr* chunk_hdr;     // [B*h_q, nch] per chunk: kept count, largest kept logit, sum w
-  float* part;             // [B*h_q, DV/16, nch, 16] chunk records: sum w*v, 16 columns per slice
+  float* part;             // [B*h_q, DV/16, nch, 16] chunk records: sum w*v, 16 columns per slice;
+                           // the late gather's slot records [B*h_q, nch] ChunkSlots use the same region
   unsigned* hist;          // [8, B*h_q, 256] top-digit histogram copies (zero between calls)
   unsigned* cand_cnt;      // [B*h_q, nsel] threshold candidates of each slice of cand_slice logits
   const int32_t* ptab;     // paged caches: [B, ptab_stride] page ids (the kernels' PAGED form)
@@ -303,13 +324,16 @@ enum SelectMode { kFromKeys = 0, kFromKeysSpeculative = 1, kFromScores = 2 };
 // logit are recorded. MODE kFromScores reads the logits stored by k_scores_hist (a
 // refresh step: the fp32 values the threshold was selected from); MODE
 // kFromKeysSpeculative (one sequence) issues the key loads before l_kv arrives.
-// With GATHER the block also writes the chunk records of eq. (7) (chunk_records).
+// OUT (SelectOut) chooses what is left for the next kernel: the kept list only, also
+// the chunk records of eq. (7) (chunk_records, the early gather), or slot records
+// (ChunkSlots, the late gather: the first kSlotE entries in the record, the rest in
+// the segment).
 // When hsplit > 1, hsplit blocks share each chunk: block hs compares and gathers only
 // the heads h of the tile with h mod hsplit == hs (every block computes all the
 // tile's logits; its duplicate key reads hit the cache).
 // DK and DV are the key and value head dimensions.
 // grid = (nch, h_k * htiles * hsplit, B), block = 256.
-template <typename T, int DK, int DV, int MODE, bool GATHER, bool PAGED, int W>
+template <typename T, int DK, int DV, int MODE, int OUT, bool PAGED, int W>
 __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   constexpr int TPW = StreamCfg<T, DK, W>::kTPW;
   constexpr int CH = StreamCfg<T, DK, W>::kChunk;
@@ -363,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
     kl.mx[tid] = 0u;
   }
   for (int e = tid; e < 16 * kWords; e += kBlock) (&s_bp.bits[0][0])[e] = 0u;
-  if constexpr (PAGED && GATHER) stage_pages<CH>(kl, a, b, base);
+  if constexpr (PAGED && OUT == kOutRecords) stage_pages<CH>(kl, a, b, base);
   const float tau_l = live ? a.tau[row0 + hh] : 0.f;
   if constexpr (MODE == kFromKeys) {
     qk.load_q(qbase + (size_t)row0 * DK, nh, lane);
@@ -416,23 +440,31 @@ __global__ __launch_bounds__(kBlock) void k_qk_select(const StreamArgs a) {
   const unsigned wb =
       lh < nh ? (s_bp.bits[lh][boff >> 5] >> (boff & 31)) & (BPT == 32 ? ~0u : (1u << BPT) - 1u) : 0u;
   const int first = row_incl_scan(__popc(wb)) - __popc(wb);
-  if constexpr (GATHER) {
+  if constexpr (OUT == kOutRecords) {
     int at = first;
     for (unsigned m = wb; m; m &= m - 1u) kl.off[lh][at++] = (uint16_t)(boff + __builtin_ctz(m));
     __syncthreads();
   }
+  ChunkSlots* const slots = reinterpret_cast<ChunkSlots*>(a.part);
   if (tid < nh && (hsplit == 1 || tid % hsplit == hs)) {
     const long long o = (long long)(row0 + tid) * a.nch + c;
-    *reinterpret_cast<int2*>(a.chunk_hdr + o) = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
+    const int2 h = make_int2(kl.cnt[tid], __float_as_int(order_key_to_f32(kl.mx[tid])));
+    if constexpr (OUT == kOutSlots) *reinterpret_cast<int2*>(slots + o) = h;
+    else *reinterpret_cast<int2*>(a.chunk_hdr + o) = h;
   }
-  if constexpr (GATHER) chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit, s_bp.part);
+  if constexpr (OUT == kOutRecords) chunk_records<T, DV, CH, PAGED>(kl, a, b, j0, nh, c, hs, hsplit, s_bp.part);
   if (wb) {
     const long long seg = (long long)(row0 + lh) * a.lpad + base;
+    ChunkSlots* const rec = slots + (long long)(row0 + lh) * a.nch + c;
     int at = first;
     for (unsigned m = wb; m; m &= m - 1u) {
       const int off = boff + __builtin_ctz(m);
-      a.surv_idx[seg + at] = base + off;
-      a.surv_val[seg + at] = kl.val[lh][off];
+      if (OUT == kOutSlots && at < kSlotE) {
+        rec->e[at] = make_int2(base + off, __float_as_int(kl.val[lh][off]));
+      } else {
+        a.surv_idx[seg + at] = base + off;
+        a.surv_val[seg + at] = kl.val[lh][off];
+      }
       ++at;
     }
   }
@@ -901,6 +933,7 @@ struct GatherArgs {
   int32_t* flags;         // [B*h_q] or null
   StreamArgs s;           // q, k, v, l_kv, logit buffer, kept lists and counts
   int sel_cap, out_bf16, refreshed;
+  int rows;               // B * h_q
 };
 
 template <int D>
@@ -1200,6 +1233,208 @@ __global__ __launch_bounds__(kBlock) void k_split_combine(const GatherArgs a) {
     store_out<DV>(a, row, col + tid, oo / zz);
   }
   if (cb == 0 && tid == 0) {
+    if (a.sel_count) a.sel_count[row] = total;
+    if (a.flags) a.flags[row] = a.refreshed ? 1 : 0;
+  }
+}
+
+// The late value gather: eq. (7) over the kept entries of one row (b, j), from the
+// slot records of k_qk_select<kOutSlots>. M = the row's largest kept logit (the
+// maximum of the records' maxima), O = sum_i w_i V[v(j), i, :] / sum_i w_i with
+// w_i = exp(A_i - M), summed in a fixed order. Each block takes one 16-byte piece of
+// the value rows (EPL output columns) of one row; the P = DV * sizeof(T) / 16 blocks
+// of a row are placed on one XCD (blocks are dealt to the 8 XCDs in turn), so the
+// row's records and value lines are fetched into one L2.
+//   - Group g of 4 threads takes records g KR .. g KR + KR - 1, thread p of the group
+//     piece p of each: one round of 16-byte loads, issued together with l_kv.
+//   - The group lists its records' inline entries in key order in its own LDS rows
+//     (written and read by the group's wave only, so no block barrier); lane p of the
+//     group loads the block's piece of the value rows of entries p, p + 4, ...
+//   - While those loads are in flight, one block pass finds M and each group's place
+//     in the row's kept list (the export of the kept indices, in key order, by the
+//     row's first block).
+//   - Entries past a record's kSlotE inline ones are read from the chunk's segment of
+//     the kept list afterwards (a record keeps that many only at dense selections).
+// A row that kept nothing is recomputed exactly by its first block (the forced
+// refresh). DK and DV are the key and value head dimensions.
+// grid = 8 ceil(B h_q / 8) P blocks, block = 256; a row has at most kPvGroupRecs * 64 chunks.
+constexpr int kPvGroupRecs = 8;  // slot records per group of 4 threads
+constexpr int kPvLoads = 8;      // value rows in flight per lane (32 per group)
+
+// x of the first lane of each quad of lanes, in all four (DPP quad_perm [0,0,0,0]).
+__device__ __forceinline__ int quad_first(int x) { return __builtin_amdgcn_update_dpp(0, x, 0x00, 0xf, 0xf, false); }
+
+template <typename T, int DK, int DV, bool PAGED, int W>
+__global__ __launch_bounds__(kBlock) void k_sparse_pv(const GatherArgs a) {
+  constexpr int CH = StreamCfg<T, DK, W>::kChunk;
+  constexpr int EPL = Unpack<T>::kN;  // columns per 16-byte piece
+  constexpr int P = DV / EPL;         // blocks per row
+  constexpr int KR = kPvGroupRecs;
+  constexpr int NGR = kBlock / 4;     // groups of 4 threads
+  constexpr int U = kPvLoads;
+  constexpr int GE = KR * kSlotE;     // inline entries of a group's records
+  const StreamArgs& sa = a.s;
+  // block -> (row, piece): XCD x = id mod 8 holds rows x, x + 8, ..., P blocks each
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const long long row = xcd + 8LL * (slot / P);
+  const int cp = slot - (slot / P) * P;
+  if (row >= a.rows) return;
+  const int b = (int)(row / sa.h_q), j = (int)(row - (long long)b * sa.h_q);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int grp = tid >> 2, pc = tid & 3;
+  const int nch = sa.nch;
+
+  __shared__ int s_itmp[kWaves];
+  __shared__ float s_ftmp[kWaves];
+  __shared__ int2 s_ent[NGR][GE];
+  __shared__ float s_red[kWaves][DV];
+  __shared__ float s_z[kWaves];
+
+  // records past the row's last chunk load the last one (never used): no branches, so
+  // every load of the round is in flight at once
+  const int4* rec = reinterpret_cast<const int4*>(reinterpret_cast<const ChunkSlots*>(sa.part) + row * nch) + pc;
+  int4 x[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) x[k] = rec[4 * min(grp * KR + k, nch - 1)];
+  const int L = min(sa.l_kv[b], sa.max_l_kv);
+  if (L <= 0) {
+    if (tid < EPL) store_out<DV>(a, row, cp * EPL + tid, 0.f);
+    if (cp == 0 && tid == 0) {
+      if (a.sel_count) a.sel_count[row] = 0;
+      if (a.flags) a.flags[row] = 0;
+    }
+    return;
+  }
+  const int nch_b = (L + CH - 1) / CH;
+  int cnt[KR];
+  float m = -INFINITY;
+  int gsum = 0, gin = 0;
+  const int ea = 2 * pc - 1, eb = 2 * pc;  // the entries in this thread's piece (none at -1)
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    // the count and the maximum are in piece 0: the group's first thread has them
+    const int n0 = quad_first(x[k].x);
+    const float m0 = __int_as_float(quad_first(x[k].y));
+    cnt[k] = grp * KR + k < nch_b ? n0 : 0;
+    if (cnt[k] > 0) m = fmaxf(m, m0);
+    gsum += cnt[k];
+    const int ni = min(cnt[k], kSlotE);
+    if (ea >= 0 && ea < ni) s_ent[grp][gin + ea] = make_int2(x[k].x, x[k].y);
+    if (eb < ni) s_ent[grp][gin + eb] = make_int2(x[k].z, x[k].w);
+    gin += ni;
+  }
+  // the group's LDS rows are written and read by its own wave: the wave executes its
+  // LDS instructions in order, so only the compiler must keep them in order
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const auto vr = value_rows<T, DV, PAGED>(sa, b, j / sa.g_v);
+  const int col0 = cp * EPL;
+  uint4 xv[U];
+  float lg[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = pc + 4 * u;
+    xv[u] = make_uint4(0, 0, 0, 0);
+    lg[u] = -INFINITY;
+    if (e < gin) {
+      const int2 en = s_ent[grp][e];
+      xv[u] = ld16(vr.row(en.x) + col0);
+      lg[u] = __int_as_float(en.y);
+    }
+  }
+
+  float M;
+  int total;
+  const int gbase = quad_first(block_max_excl_scan(m, pc == 0 ? gsum : 0, s_ftmp, s_itmp, M, total));
+  if (total == 0) {
+    if (cp == 0) exact_row<T, DK, DV, kBlock, PAGED>(a, b, j, L, true, s_red, s_z);
+    return;
+  }
+  const long long sbase = row * sa.lpad;
+  if (cp == 0 && a.sel_idx) {
+    // kept indices in key order: entry e of record k at gbase + (counts before k) + e
+    int32_t* const exp_idx = a.sel_idx + row * a.sel_cap;
+    int p = gbase;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      const int n = cnt[k], ni = min(n, kSlotE);
+      if (ea >= 0 && ea < ni && p + ea < a.sel_cap) exp_idx[p + ea] = x[k].x;
+      if (eb < ni && p + eb < a.sel_cap) exp_idx[p + eb] = x[k].z;
+      const long long cb = sbase + (long long)(grp * KR + k) * CH;
+      for (int e = kSlotE + pc; e < n && p + e < a.sel_cap; e += 4) exp_idx[p + e] = sa.surv_idx[cb + e];
+      p += n;
+    }
+  }
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float z = 0.f;
+  auto add = [&](const uint4& v, float logit) {
+    const float w = expf(logit - M);  // 0 for an unused slot (logit -inf)
+    float f[EPL];
+    Unpack<T>::run(v, f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += w * f[e];
+    z += w;
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) add(xv[u], lg[u]);
+  // a group with more than 4 U inline entries
+  for (int u0 = 4 * U; u0 < gin; u0 += 4 * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = u0 + pc + 4 * u;
+      xv[u] = make_uint4(0, 0, 0, 0);
+      lg[u] = -INFINITY;
+      if (e < gin) {
+        const int2 en = s_ent[grp][e];
+        xv[u] = ld16(vr.row(en.x) + col0);
+        lg[u] = __int_as_float(en.y);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) add(xv[u], lg[u]);
+  }
+  // entries past the inline ones, from the chunks' segments of the kept list: lane p of
+  // the group takes entries kSlotE + p, kSlotE + p + 4, ...
+#pragma unroll 1
+  for (int k = 0; k < KR; ++k) {
+    const int n = cnt[k];
+    const long long cb = sbase + (long long)(grp * KR + k) * CH;
+    for (int e0 = kSlotE + pc; e0 < n; e0 += 4 * U) {
+      int idx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + 4 * u;
+        idx[u] = e < n ? sa.surv_idx[cb + e] : -1;
+        lg[u] = e < n ? sa.surv_val[cb + e] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) xv[u] = idx[u] >= 0 ? ld16(vr.row(idx[u]) + col0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) add(xv[u], lg[u]);
+    }
+  }
+  // every lane holds sums over its own entries: the wave sums, then the waves
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = wave_sum(acc[e]);
+  z = wave_sum(z);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_red[wv][e] = acc[e];
+    s_z[wv] = z;
+  }
+  __syncthreads();
+  if (tid < EPL) {
+    float o = 0.f, zz = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      o += s_red[w][tid];
+      zz += s_z[w];
+    }
+    store_out<DV>(a, row, cp * EPL + tid, o / zz);
+  }
+  if (cp == 0 && tid == 0) {
     if (a.sel_count) a.sel_count[row] = total;
     if (a.flags) a.flags[row] = a.refreshed ? 1 : 0;
   }

@@ -138,8 +138,16 @@ int main() {
           SAGA_ERR_UNSUPPORTED);
     CHECK(saga_qk_select(&s, FAKE, FAKE, (const int32_t*)FAKE, 1024, nullptr, FAKE, 1u << 30, nullptr) ==
           SAGA_ERR_NULL);
-    CHECK(saga_select_gather(&s, FAKE, FAKE, nullptr, (const int32_t*)FAKE, 1024, (const float*)FAKE, FAKE, 1u << 30,
-                             nullptr) == SAGA_ERR_NULL);
+    CHECK(saga_select_gather(&s, FAKE, FAKE, nullptr, (const int32_t*)FAKE, 1024, 8, (const float*)FAKE, FAKE,
+                             1u << 30, nullptr) == SAGA_ERR_NULL);
+    CHECK(saga_select_gather(&s, FAKE, FAKE, FAKE, (const int32_t*)FAKE, 1024, 0, (const float*)FAKE, FAKE,
+                             1u << 30, nullptr) == SAGA_ERR_SHAPE);
+    // the gather form: late for a head keeping about 1 entry per chunk, early for dense
+    // selections and rows of more than 512 chunks, -1 for invalid arguments
+    CHECK(saga_gather_form(&s, 512, 131072) == 1);
+    CHECK(saga_gather_form(&s, 2048, 4096) == 0);
+    CHECK(saga_gather_form(&s, 0, 4096) == -1);
+    CHECK(saga_gather_form(nullptr, 8, 4096) == -1);
     saga_pages pg;
     pg.table = (const int32_t*)FAKE;
     pg.max_pages = 4;

@@ -451,7 +451,7 @@ def test_stages_equal_decode_step():
     # the two kernels of the step, one call each: the same launches as the step itself
     out2 = torch.empty_like(g.out)
     cnt = torch.zeros_like(g.sel_count)
-    api.select_gather(g.q, g.k, g.v, g.l_kv, tau, max_l_kv=g.max_l_kv, workspace=g.ws)
+    api.select_gather(g.q, g.k, g.v, g.l_kv, tau, N=64, max_l_kv=g.max_l_kv, workspace=g.ws)
     api.split_combine(g.q, g.k, g.v, g.l_kv, tau, N=64, max_l_kv=g.max_l_kv, out=out2, sel_count=cnt,
                       workspace=g.ws)
     torch.cuda.synchronize()

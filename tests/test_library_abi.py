@@ -48,6 +48,21 @@ def shape(**kw):
     return api.SagaShape(**d)
 
 
+def test_gather_form(lib):
+    """Where the step gathers the kept value rows: late (in the combining kernel) when a
+    head keeps about CH N / l_kv <= 2 entries per chunk of CH keys and a row has at most
+    512 chunks; early (in the select kernel) otherwise."""
+    def form(N, L, **kw):
+        return lib.saga_gather_form(ctypes.byref(shape(**kw)), N, L)
+    assert form(512, 131072) == 1                       # Qwen-shaped 128K: 256-key chunks, ~1 kept each
+    assert form(256, 32768, h_q=32, h_k=2, h_v=8, d=64) == 1  # Llama-shaped 32K
+    assert form(2048, 4096) == 0                        # dense selections: 64 kept per 128-key chunk
+    assert form(512, 16384) == 0                        # 4 kept per chunk
+    assert form(512, 1 << 20, l_max=1 << 20) == 0       # 2048 chunks per row
+    assert form(512, 0) == 0                            # nothing cached: the early form's zero rows
+    assert form(0, 1024) == -1 and form(8, 1 << 20) == -1 and form(8, 1024, h_k=5) == -1
+
+
 def test_workspace_bytes(lib):
     s = shape()
     n = lib.saga_workspace_bytes(ctypes.byref(s), 512, 131072)
@@ -152,8 +167,10 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.saga_qk_select(ctypes.byref(s), FAKE, None, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_NULL
     assert lib.saga_sparse_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, None, None, None, 0,
                                   None, FAKE, big, None) == api.ERR_NULL
-    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, None, FAKE, 1024, FAKE, FAKE, big, None) == api.ERR_NULL
-    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 16, None) == api.ERR_WORKSPACE
+    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, None, FAKE, 1024, 8, FAKE, FAKE, big, None) == api.ERR_NULL
+    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 0, FAKE, FAKE, big,
+                                  None) == api.ERR_SHAPE
+    assert lib.saga_select_gather(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, FAKE, 16, None) == api.ERR_WORKSPACE
     assert lib.saga_split_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 0, FAKE, FAKE, None, None, 0,
                                   None, FAKE, big, None) == api.ERR_SHAPE
     assert lib.saga_split_combine(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1024, 8, FAKE, FAKE, None, FAKE, 0,
