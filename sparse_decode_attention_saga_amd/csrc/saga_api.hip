@@ -230,16 +230,28 @@ int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
 
 // The late value gather (k_qk_select<kOutSlots> -> k_sparse_pv): the select kernel
 // leaves each chunk's kept (index, logit) pairs in a slot record and the combining
-// kernel gathers the kept value rows. Taken when a head is expected to keep at most
-// kLateMaxKept entries per chunk (CH * N / max_l_kv) and a row has at most
-// kPvGroupRecs * 64 chunks (one slot record per thread piece). Denser selections keep
-// the early gather (k_qk_select<kOutRecords> -> k_split_combine), which spreads many
-// value rows per chunk over the select kernel's blocks. At the Qwen-shaped 128K layer
-// the late gather takes the value rows' dependent round trip out of the key stream.
+// kernel gathers the kept value rows. Taken when
+//   - a head is expected to keep at most kLateMaxKept entries per chunk (CH N / max_l_kv),
+//   - a row has at most kPvGroupRecs * 64 chunks (one slot record per thread piece),
+//   - value rows hold at least kLateMinRowBytes bytes, and
+//   - the select kernel has at least two blocks per compute unit (kMinStreamBlocks).
+// Otherwise the early gather (k_qk_select<kOutRecords> -> k_split_combine), which
+// spreads many value rows per chunk over the select kernel's blocks. Measured on
+// MI355X, amortized step, late against early gather:
+//   - taken: the Qwen-shaped 128K layer (256-byte value rows, 512 select blocks) 15.78
+//     against 16.03 us; 16 such sequences (4096 blocks) 124.6 against 129.6 us;
+//   - not taken: the Llama-shaped 32K layer (128-byte rows) 12.13 against 11.45 us, the
+//     ragged batch of 8 with the same heads 59.2 against 55.2 us; the Qwen-shaped layer
+//     with 64-wide keys (512-key chunks, 256 blocks) 17.60 against 16.85 us, and the
+//     Qwen-shaped layer forced to 512-key chunks 18.6 against 16.0 us.
 constexpr int kLateMaxKept = 2;
+constexpr int kLateMinRowBytes = 256;
 
-bool late_gather(const Layout& w, int N, int max_l_kv) {
+bool late_gather(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
   if (max_l_kv <= 0 || w.nch > kPvGroupRecs * (kBlock / 4)) return false;
+  if (value_dim(s) * (s->dtype == SAGA_BF16 ? 2 : 4) < kLateMinRowBytes) return false;
+  const int g_k = s->h_q / s->h_k;
+  if ((long long)w.nch * s->h_k * ((g_k + 15) / 16) * s->batch < kMinStreamBlocks) return false;
   const long long n = N < max_l_kv ? N : max_l_kv;
   return (long long)w.ch * n <= (long long)kLateMaxKept * max_l_kv;
 }
@@ -304,7 +316,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.max_l_kv = max_l_kv;
   a.lpad = w.lpad;
   a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
-  a.hsplit = late_gather(w, N, max_l_kv) ? 1 : head_split(s, w, N, max_l_kv);
+  a.hsplit = late_gather(s, w, N, max_l_kv) ? 1 : head_split(s, w, N, max_l_kv);
   return a;
 }
 
@@ -414,7 +426,7 @@ saga_status decode_impl(const saga_shape* s, const saga_pages* pg, const void* q
   const bool refresh = (step % refresh_period) == 0;
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N, pg);
-  const bool late = late_gather(w, N, max_l_kv);
+  const bool late = late_gather(s, w, N, max_l_kv);
   if (max_l_kv > 0) {
     if (refresh) launch_refresh(s, w, a, tau, hs);
     launch_select(s, w, a, refresh, late ? kOutSlots : kOutRecords, hs);
@@ -522,7 +534,7 @@ size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv) {
 
 int32_t saga_gather_form(const saga_shape* s, int32_t N, int32_t max_l_kv) {
   if (check_shape(s) != SAGA_OK || N < 1 || max_l_kv < 0 || max_l_kv > s->l_max) return -1;
-  return late_gather(layout(s, max_l_kv), N, max_l_kv) ? 1 : 0;
+  return late_gather(s, layout(s, max_l_kv), N, max_l_kv) ? 1 : 0;
 }
 
 saga_status saga_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -639,7 +651,7 @@ saga_status saga_select_gather(const saga_shape* s, const void* q, const void* k
   (void)hipGetLastError();
   if (max_l_kv > 0)
     launch_select(s, w, stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N), false,
-                  late_gather(w, N, max_l_kv) ? kOutSlots : kOutRecords, (hipStream_t)stream);
+                  late_gather(s, w, N, max_l_kv) ? kOutSlots : kOutRecords, (hipStream_t)stream);
   return launched();
 }
 
@@ -655,7 +667,7 @@ saga_status saga_split_combine(const saga_shape* s, const void* q, const void* k
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N);
   launch_combine(s, w, gather_args(s, a, tau, out, sel_count, sel_idx, sel_cap, flags, false),
-                 late_gather(w, N, max_l_kv), (hipStream_t)stream);
+                 late_gather(s, w, N, max_l_kv), (hipStream_t)stream);
   return launched();
 }
 
