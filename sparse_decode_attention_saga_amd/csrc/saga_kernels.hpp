@@ -1,10 +1,13 @@
 // Kernels of the SAGA + Atop-N decode step and of the dense GQA baseline (gfx950).
 //
-// Stale-threshold step:  k_qk_select<gather> -> k_split_combine
+// Stale-threshold step:  k_qk_select<slot records> -> k_sparse_pv          (late value gather)
+//                        k_qk_select<chunk records> -> k_split_combine      (early value gather)
 // Refresh step:          k_scores_hist [-> k_cand_collect] -> k_select_finish
-//                        -> k_qk_select<from stored logits, gather> -> k_split_combine
-// Separate stages:       k_qk_select -> k_chunk_gather -> k_split_combine
+//                        -> k_qk_select<from stored logits, ...> -> the same combining kernel
+// Separate stages:       k_qk_select<kept list> -> k_chunk_gather -> k_split_combine
 // Dense GQA baseline:    k_dense_partial -> k_dense_combine
+// The host picks the value-gather form per call (late: 256-byte value rows, about one
+// kept entry per head and chunk, at least two select blocks per compute unit).
 //
 // No kernel waits on another workgroup and none needs a device-scope fence: every
 // exchange between workgroups goes through a kernel boundary (the threshold
