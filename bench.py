@@ -21,9 +21,11 @@ replayed from a HIP graph and timed with HIP events on the launch stream.
 Prints one JSON line. `value` = SAGA decode steps/s = 1 / t_step (refresh cost
 amortized as above).
 `roofline` is for the dominant kernel, the select kernel of a step that reuses the
-threshold (saga_select_gather: K stream, comparison, value gather): a graph of K
-launches of it alone is timed with HIP events on its stream; its algorithmic bytes
-per launch are bytes(K) + bytes(selected V rows, union per value head). `traffic` is
+threshold (saga_select_gather: K stream and comparison, and the value gather in the
+early form): a graph of K launches of it alone is timed with HIP events on its
+stream; its algorithmic bytes per launch are bytes(K) in the late value-gather form
+(the combining kernel reads the selected V rows) and bytes(K) + bytes(selected V rows,
+union per value head) in the early one (`value_gather` names the form). `traffic` is
 the HBM traffic of that kernel measured with rocprofv3 counters (recorded in
 profiles/ for one build of the kernels; null when the sources differ).
 `cpu_baseline` is the CPU oracle timed on this host on the same workload.
@@ -652,9 +654,9 @@ def stages(torch, args) -> int:
     rotating input sets: the key stream with the Atop-N comparison (saga_qk_select,
     algorithmic bytes = the keys), the value gather into chunk records followed by the
     combine (saga_sparse_gather over the kept lists of one saga_qk_select call,
-    algorithmic bytes = the selected value rows), and the step's fused select kernel
-    and combine (saga_select_gather, saga_split_combine). Under rocprofv3 the same
-    command gives each kernel's duration and counters."""
+    algorithmic bytes = the selected value rows), and the step's own two kernels
+    (saga_select_gather, saga_split_combine) in the value-gather form the step takes.
+    Under rocprofv3 the same command gives each kernel's duration and counters."""
     from sparse_decode_attention_saga_amd import api
     from sparse_decode_attention_saga_amd import bytemodel
     from sparse_decode_attention_saga_amd import workloads as wl
@@ -711,11 +713,15 @@ def stages(torch, args) -> int:
                                                              out=out, workspace=ws))
     for k, v in res.items():
         log(f"{k}: {v:.2f} us/launch")
-    line = {"stages": w.name, "rotating_sets": R, "steps": K, "us": res,
+    form = api.gather_form(api.make_shape(q0, k0, v0), w.N, L)
+    # the late gather's select kernel reads the keys, its combining kernel the value rows
+    sel_bytes = bytes_k if form == "late" else bytes_k + bytes_v
+    line = {"stages": w.name, "rotating_sets": R, "steps": K, "us": res, "value_gather": form,
             "bytes": {"keys": bytes_k, "selected_value_rows": bytes_v},
             "gbs": {"qk_select_keys": bytes_k / res["qk_select"] / 1e3,
                     "sparse_gather_value_rows": bytes_v / res["sparse_gather"] / 1e3,
-                    "select_gather_keys_and_rows": (bytes_k + bytes_v) / res["select_gather"] / 1e3}}
+                    "select_gather_" + ("keys" if form == "late" else "keys_and_rows"):
+                        sel_bytes / res["select_gather"] / 1e3}}
     print(json.dumps(line), flush=True)
     return 0
 

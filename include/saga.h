@@ -91,8 +91,9 @@ size_t saga_workspace_bytes(const saga_shape* s, int32_t N, int32_t max_l_kv);
 /* The form of the value gather that saga_decode_attn (and saga_select_gather with
  * saga_split_combine) takes for `s`, top-N size N and max_l_kv: 1 for the late gather
  * (the combining kernel reads the kept value rows), 0 for the early gather (the
- * select kernel does), -1 if the arguments are invalid. Pure host arithmetic; the
- * results of the step do not depend on the form beyond the rounding of its sums. */
+ * select kernel does), -1 if the arguments are invalid. saga_decode_attn_paged always
+ * takes the early gather. Pure host arithmetic; the results of the step do not depend
+ * on the form beyond the rounding of its sums. */
 int32_t saga_gather_form(const saga_shape* s, int32_t N, int32_t max_l_kv);
 
 /* Enqueue a zero fill of `bytes` bytes of `workspace` (first-use initialisation). */

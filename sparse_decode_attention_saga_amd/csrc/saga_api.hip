@@ -233,8 +233,10 @@ int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
 // kernel gathers the kept value rows. Taken when
 //   - a head is expected to keep at most kLateMaxKept entries per chunk (CH N / max_l_kv),
 //   - a row has at most kPvGroupRecs * 64 chunks (one slot record per thread piece),
-//   - value rows hold at least kLateMinRowBytes bytes, and
-//   - the select kernel has at least two blocks per compute unit (kMinStreamBlocks).
+//   - value rows hold at least kLateMinRowBytes bytes,
+//   - the select kernel has at least two blocks per compute unit (kMinStreamBlocks), and
+//   - the caches are contiguous (with pages, each kept row's page lookup would add a
+//     dependent load to the combining kernel: 18.26 against 17.13 us per step).
 // Otherwise the early gather (k_qk_select<kOutRecords> -> k_split_combine), which
 // spreads many value rows per chunk over the select kernel's blocks. Measured on
 // MI355X, amortized step, late against early gather:
@@ -247,8 +249,8 @@ int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
 constexpr int kLateMaxKept = 2;
 constexpr int kLateMinRowBytes = 256;
 
-bool late_gather(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
-  if (max_l_kv <= 0 || w.nch > kPvGroupRecs * (kBlock / 4)) return false;
+bool late_gather(const saga_shape* s, const Layout& w, int N, int max_l_kv, bool paged = false) {
+  if (paged || max_l_kv <= 0 || w.nch > kPvGroupRecs * (kBlock / 4)) return false;
   if (value_dim(s) * (s->dtype == SAGA_BF16 ? 2 : 4) < kLateMinRowBytes) return false;
   const int g_k = s->h_q / s->h_k;
   if ((long long)w.nch * s->h_k * ((g_k + 15) / 16) * s->batch < kMinStreamBlocks) return false;
@@ -316,7 +318,7 @@ StreamArgs stream_args(const saga_shape* s, const Layout& w, void* ws, const voi
   a.max_l_kv = max_l_kv;
   a.lpad = w.lpad;
   a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
-  a.hsplit = late_gather(s, w, N, max_l_kv) ? 1 : head_split(s, w, N, max_l_kv);
+  a.hsplit = late_gather(s, w, N, max_l_kv, pg != nullptr) ? 1 : head_split(s, w, N, max_l_kv);
   return a;
 }
 
@@ -426,7 +428,7 @@ saga_status decode_impl(const saga_shape* s, const saga_pages* pg, const void* q
   const bool refresh = (step % refresh_period) == 0;
   (void)hipGetLastError();
   const StreamArgs a = stream_args(s, w, workspace, q, k, v, l_kv, max_l_kv, tau, N, pg);
-  const bool late = late_gather(s, w, N, max_l_kv);
+  const bool late = late_gather(s, w, N, max_l_kv, pg != nullptr);
   if (max_l_kv > 0) {
     if (refresh) launch_refresh(s, w, a, tau, hs);
     launch_select(s, w, a, refresh, late ? kOutSlots : kOutRecords, hs);

@@ -14,7 +14,7 @@ import torch
 from oracle import saga_oracle as orc
 from sparse_decode_attention_saga_amd import api
 from sparse_decode_attention_saga_amd import workloads as wl
-from tests.parity import GpuCase, compare, out_bound
+from tests.parity import DERIVED, GpuCase, compare, out_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -60,13 +60,24 @@ class PagedCase:
                     flags=self.flags.cpu().numpy())
 
 
-def same_selection(p, c, where):
-    """Paged result p equals contiguous result c bit for bit."""
+def same_selection(p, c, where, same_form=True):
+    """Paged result p equals contiguous result c: bit for bit when both take the same
+    value-gather form; otherwise (the contiguous call gathers late, the paged call
+    early) the thresholds, counts, flags and kept sets bit for bit, and the outputs,
+    summed in another order, within the derived bound of the arithmetic."""
     assert np.array_equal(p["tau"], c["tau"]), f"{where}: thresholds differ"
     assert np.array_equal(p["count"], c["count"]), f"{where}: counts differ"
     assert np.array_equal(p["flags"], c["flags"]), f"{where}: flags differ"
-    assert np.array_equal(p["idx"], c["idx"]), f"{where}: kept indices differ"
-    assert np.array_equal(p["O"], c["O"]), f"{where}: outputs differ"
+    if same_form:
+        assert np.array_equal(p["idx"], c["idx"]), f"{where}: kept indices differ"
+        assert np.array_equal(p["O"], c["O"]), f"{where}: outputs differ"
+        return
+    cap = p["idx"].shape[-1]
+    for r in np.ndindex(p["count"].shape):
+        n = min(int(p["count"][r]), cap)
+        assert np.array_equal(np.sort(p["idx"][r][:n]), np.sort(c["idx"][r][:n])), f"{where}: kept sets differ at {r}"
+    err = np.abs(p["O"] - c["O"]).max(axis=-1) / np.maximum(np.abs(c["O"]).max(axis=-1), 1e-30)
+    assert err.max() <= DERIVED, f"{where}: outputs differ by {err.max():.2e}"
 
 
 PAGED = [
@@ -114,8 +125,10 @@ def test_paged_batch16_full_size():
     say(f"{w.name}: paged, 256-token pages")
     c = GpuCase(x, w.N, sel_cap=4 * w.N)
     p = PagedCase(x, w.N, 256, -1, seed=1, sel_cap=4 * w.N, max_l_kv=x.k.shape[2])
+    # paged calls always gather early; the contiguous call takes the form of its shape
+    same = api.gather_form(api.make_shape(c.q, c.k, c.v), w.N, x.k.shape[2]) == "early"
     for step in (0, 1):
-        same_selection(p.step(w.refresh_period, step), c.step(w.refresh_period, step), f"step {step}")
+        same_selection(p.step(w.refresh_period, step), c.step(w.refresh_period, step), f"step {step}", same)
 
 
 DENSE_PAGED = [
