@@ -192,11 +192,11 @@ saga_status saga_sparse_gather(const saga_shape* s, const void* q, const void* k
  * stream with one workspace (saga_decode_attn with step % refresh_period != 0 is
  * exactly saga_select_gather followed by saga_split_combine with the same N). Both
  * take one of two forms, chosen from the shape, N and max_l_kv exactly as
- * saga_decode_attn chooses it (saga_gather_form): value rows of at least 256 bytes
- * with a head expected to keep at most 2 entries per run of cached keys (the kernel's
- * chunk, 128 to 512 keys), on rows of at most 512 such runs, and at least 512 runs
- * over all key heads and sequences, take the late value gather; other shapes and
- * selections the early one.
+ * saga_decode_attn chooses it (saga_gather_form): contiguous caches with value rows
+ * of at least 256 bytes, rows of at most 512 runs of cached keys (the kernel's chunk,
+ * 128 to 512 keys), at least 512 runs over all key heads and sequences, and a head
+ * expected to keep at most 1 entry per run (at most 2 with 2048 runs or more) take
+ * the late value gather; other shapes and selections the early one.
  * saga_select_gather: eq. (2) logits of every cached key and the comparison with tau,
  *   then per chunk and query head, into the workspace:
  *   - early gather: the part of eq. (7) over the chunk's kept entries relative to

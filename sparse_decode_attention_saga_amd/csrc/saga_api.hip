@@ -231,31 +231,36 @@ int head_split(const saga_shape* s, const Layout& w, int N, int max_l_kv) {
 // The late value gather (k_qk_select<kOutSlots> -> k_sparse_pv): the select kernel
 // leaves each chunk's kept (index, logit) pairs in a slot record and the combining
 // kernel gathers the kept value rows. Taken when
-//   - a head is expected to keep at most kLateMaxKept entries per chunk (CH N / max_l_kv),
-//   - a row has at most kPvGroupRecs * 64 chunks (one slot record per thread piece),
 //   - value rows hold at least kLateMinRowBytes bytes,
-//   - the select kernel has at least two blocks per compute unit (kMinStreamBlocks), and
 //   - the caches are contiguous (with pages, each kept row's page lookup would add a
-//     dependent load to the combining kernel: 18.26 against 17.13 us per step).
+//     dependent load to the combining kernel: 18.26 against 17.13 us per step),
+//   - a row has at most kPvGroupRecs * 64 chunks (one slot record per thread piece),
+//   - the select kernel has at least two blocks per compute unit (kMinStreamBlocks), and
+//   - a head is expected to keep at most 1 entry per chunk (CH N / max_l_kv), or at most
+//     2 when the select kernel has at least kLateManyBlocks blocks.
 // Otherwise the early gather (k_qk_select<kOutRecords> -> k_split_combine), which
-// spreads many value rows per chunk over the select kernel's blocks. Measured on
-// MI355X, amortized step, late against early gather:
-//   - taken: the Qwen-shaped 128K layer (256-byte value rows, 512 select blocks) 15.78
-//     against 16.03 us; 16 such sequences (4096 blocks) 124.6 against 129.6 us;
-//   - not taken: the Llama-shaped 32K layer (128-byte rows) 12.13 against 11.45 us, the
-//     ragged batch of 8 with the same heads 59.2 against 55.2 us; the Qwen-shaped layer
-//     with 64-wide keys (512-key chunks, 256 blocks) 17.60 against 16.85 us, and the
-//     Qwen-shaped layer forced to 512-key chunks 18.6 against 16.0 us.
-constexpr int kLateMaxKept = 2;
+// spreads the value rows over the select kernel's blocks. Measured on MI355X,
+// amortized step, late against early gather:
+//   - taken: the Qwen-shaped 128K layer (256-byte value rows, 512 blocks, 1 kept per
+//     chunk) 15.78 against 16.03 us; 16 such sequences (4096 blocks, 2 per chunk) 124.4
+//     against 129.2 us;
+//   - not taken: at 512 blocks and 2 kept per chunk, the Qwen-shaped layer with 64-wide
+//     keys 17.60 against 16.82 us and with two key heads (GQA) 23.64 against 22.12 us; the
+//     Qwen-shaped layer forced to 256 blocks of 512 keys 18.6 against 16.0 us; the
+//     Llama-shaped 32K layer (128-byte rows) 12.13 against 11.45 us and the ragged batch
+//     of 8 with the same heads 59.2 against 55.2 us.
 constexpr int kLateMinRowBytes = 256;
+constexpr long long kLateManyBlocks = 2048;
 
 bool late_gather(const saga_shape* s, const Layout& w, int N, int max_l_kv, bool paged = false) {
   if (paged || max_l_kv <= 0 || w.nch > kPvGroupRecs * (kBlock / 4)) return false;
   if (value_dim(s) * (s->dtype == SAGA_BF16 ? 2 : 4) < kLateMinRowBytes) return false;
   const int g_k = s->h_q / s->h_k;
-  if ((long long)w.nch * s->h_k * ((g_k + 15) / 16) * s->batch < kMinStreamBlocks) return false;
+  const long long blocks = (long long)w.nch * s->h_k * ((g_k + 15) / 16) * s->batch;
+  if (blocks < kMinStreamBlocks) return false;
   const long long n = N < max_l_kv ? N : max_l_kv;
-  return (long long)w.ch * n <= (long long)kLateMaxKept * max_l_kv;
+  const long long max_kept = blocks >= kLateManyBlocks ? 2 : 1;
+  return (long long)w.ch * n <= max_kept * max_l_kv;
 }
 
 template <typename P>

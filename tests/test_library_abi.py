@@ -50,14 +50,17 @@ def shape(**kw):
 
 def test_gather_form(lib):
     """Where the step gathers the kept value rows: late (in the combining kernel) for
-    value rows of at least 256 bytes when a head keeps about CH N / l_kv <= 2 entries per
-    chunk of CH keys, a row has at most 512 chunks and the select kernel at least 512
-    blocks; early (in the select kernel) otherwise."""
+    value rows of at least 256 bytes, rows of at most 512 chunks, a select kernel of at
+    least 512 blocks and a head keeping about CH N / l_kv <= 1 entry per chunk of CH keys
+    (<= 2 with 2048 blocks or more); early (in the select kernel) otherwise."""
     def form(N, L, **kw):
         return lib.saga_gather_form(ctypes.byref(shape(**kw)), N, L)
     assert form(512, 131072) == 1                       # Qwen-shaped 128K: 256-key chunks, ~1 kept each
     assert form(512, 131072, batch=16) == 1             # 16 such sequences: 512-key chunks, 4096 blocks
     assert form(512, 131072, d=64, d_v=128) == 0        # 64-wide keys: 512-key chunks, 256 blocks
+    assert form(512, 131072, h_k=2, d=64, d_v=128) == 0  # two such key heads: 512 blocks, 2 kept per chunk
+    assert form(512, 131072, h_k=2, h_v=2) == 0         # GQA heads (2 key heads of 128): the same
+    assert form(2048, 131072) == 0                      # 4 kept per chunk
     assert form(512, 131072, d=64, dtype=api.F32) == 1  # fp32 rows of 64: 256 bytes
     assert form(256, 32768, h_q=32, h_k=2, h_v=8, d=64) == 0  # Llama-shaped 32K: 128-byte value rows
     assert form(2048, 4096) == 0                        # dense selections: 64 kept per 128-key chunk
