@@ -83,15 +83,17 @@ def same_steps(got, ref, where):
 
 
 @pytest.mark.parametrize("case", [
-    # B, h_q, h_k, h_v, d, lens, N, period, steps
-    (2, 12, 1, 4, 128, [5000, 1777], 64, 4, 9),
-    (3, 32, 2, 8, 64, [3000, 0, 4096], 32, 3, 7),
+    # B, h_q, h_k, h_v, d, lens, N, period, steps, value-gather form
+    (2, 12, 1, 4, 128, [5000, 1777], 64, 4, 9, "early"),
+    (3, 32, 2, 8, 64, [3000, 0, 4096], 32, 3, 7, "early"),
+    (2, 12, 1, 4, 128, [65536, 40000], 128, 4, 5, "late"),   # 512 select blocks, < 1 kept per chunk
 ])
 def test_graph_replays_equal_eager_steps(case):
-    B, h_q, h_k, h_v, d, lens, N, period, steps = case
+    B, h_q, h_k, h_v, d, lens, N, period, steps, form = case
     say(f"graph case {case}")
     x = inputs(1, B, h_q, h_k, h_v, d, lens)
     st = Steps(x, N, period, steps)
+    assert api.gather_form(api.make_shape(st.q, st.k, st.v), N, st.L) == form
     st.run()
     torch.cuda.synchronize()
     ref = st.result()

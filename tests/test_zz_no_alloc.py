@@ -2,14 +2,14 @@
 against saga_decode_attn (the same step with a caller's workspace), through the
 C ABI on the same inputs.
 
-Two inputs in a row on one GPU, the second smaller than the first, each with a
-refresh step and a step that reuses the threshold, so the second call runs on
-scratch that still holds the first call's contents. Thresholds, kept counts, flags
-and kept index sets must be identical (the same kernels on the same inputs, the
-threshold select is exact); outputs within 1e-6 of the row's largest output (fp32
-outputs; kept entries of a chunk take their slots in the order the lanes reach
-them, so the order of the fp32 sums inside a chunk can differ). The first input is
-also checked against the CPU oracle with the bar of the parity tests.
+Three inputs in a row on one GPU, each smaller than the one before, each with a
+refresh step and a step that reuses the threshold, so every later call runs on
+scratch that still holds an earlier call's contents. The first (a Qwen-shaped
+sequence of 128K) takes the late value gather, the other two the early one.
+Thresholds, kept counts, flags, kept indices and outputs must be identical bit for
+bit: the same kernels run on the same inputs, kept entries take fixed places and
+every sum runs in a fixed order. The first two inputs are also checked against the
+CPU oracle with the bar of the parity tests.
 """
 import numpy as np
 import pytest
@@ -22,7 +22,8 @@ from sparse_decode_attention_saga_amd import workloads as wl
 DEV = torch.device("cuda:0")
 pytestmark = pytest.mark.gpu
 
-FIRST = wl.QWEN_128K.with_(l_kv=32768, N=256, refresh_period=4)
+FIRST = wl.QWEN_128K.with_(refresh_period=4)
+MIDDLE = wl.QWEN_128K.with_(l_kv=32768, N=256, refresh_period=4)
 SECOND = wl.LLAMA_32K.with_(h_q=8, h_k=2, h_v=4, l_kv=3000, N=64, refresh_period=3)
 
 
@@ -56,30 +57,36 @@ def run_pair(w, steps):
         assert torch.equal(ref.count, na.count), t
         assert torch.equal(ref.flags, na.flags), t
         assert int(ref.count.max()) <= cap
-        assert torch.equal(torch.sort(ref.idx, dim=-1).values, torch.sort(na.idx, dim=-1).values), t
-        o_ref, o_na = ref.out.double(), na.out.double()
-        err = ((o_ref - o_na).abs().amax(dim=-1) / o_ref.abs().amax(dim=-1)).max().item()
-        assert err <= 1e-6, (t, err)
+        assert torch.equal(ref.idx, na.idx), t
+        assert torch.equal(ref.out, na.out), t
         results.append((x, t, na.out.double().cpu().numpy(), na.tau.double().cpu().numpy(),
                         na.count.cpu().numpy(), na.flags.cpu().numpy()))
     return results
 
 
+def form(w):
+    shape = api.SagaShape(w.batch, w.h_q, w.h_k, w.h_v, w.d, 0, w.l_kv, api.BF16, api.F32, 0.0)
+    return api.gather_form(shape, w.N, w.l_kv)
+
+
 def test_noalloc_matches_workspace_entry_point_twice_second_smaller():
+    assert (form(FIRST), form(MIDDLE), form(SECOND)) == ("late", "early", "early")
     first = run_pair(FIRST, steps=[0, 1])
+    middle = run_pair(MIDDLE, steps=[0, 1])
     second = run_pair(SECOND, steps=[0, 2])
-    assert SECOND.l_kv * SECOND.h_q < FIRST.l_kv * FIRST.h_q
-    # the first input's refresh step against the oracle (exact top-N at a refresh)
-    x, t, out, tau, count, flags = first[0]
-    q64, k64, v64 = x.f64()
-    r = orc.saga_decode_step(q64, k64, v64, x.l_kv, FIRST.N, FIRST.refresh_period, t)
-    s = np.maximum(np.abs(r.tau), 1.0)
-    assert np.all(np.abs(tau - r.tau) <= 1e-5 * s)
-    err = (np.abs(out - r.O).max(axis=-1) / np.abs(r.O).max(axis=-1)).max()
-    assert err <= 1e-5, err  # exact bf16 inputs, fp32 arithmetic and outputs
-    assert np.all(flags == 1)
-    # both inputs: every row kept at least N entries at its refresh step
-    for res, w in ((first, FIRST), (second, SECOND)):
+    assert SECOND.l_kv * SECOND.h_q < MIDDLE.l_kv * MIDDLE.h_q < FIRST.l_kv * FIRST.h_q
+    # the refresh steps of the first two inputs against the oracle (exact top-N at a refresh)
+    for res, w in ((first, FIRST), (middle, MIDDLE)):
+        x, t, out, tau, count, flags = res[0]
+        q64, k64, v64 = x.f64()
+        r = orc.saga_decode_step(q64, k64, v64, x.l_kv, w.N, w.refresh_period, t)
+        s = np.maximum(np.abs(r.tau), 1.0)
+        assert np.all(np.abs(tau - r.tau) <= 1e-5 * s)
+        err = (np.abs(out - r.O).max(axis=-1) / np.abs(r.O).max(axis=-1)).max()
+        assert err <= 1e-5, err  # exact bf16 inputs, fp32 arithmetic and outputs
+        assert np.all(flags == 1)
+    # every input: every row kept at least N entries at its refresh step
+    for res, w in ((first, FIRST), (middle, MIDDLE), (second, SECOND)):
         assert np.all(res[0][4] >= w.N)
 
 
