@@ -488,6 +488,7 @@ saga_status dense_impl(const saga_shape* s, const saga_pages* pg, const void* q,
   a.max_l_kv = max_l_kv;
   a.out_bf16 = s->out_dtype == SAGA_BF16;
   a.scale = s->scale > 0.f ? s->scale : (float)(1.0 / std::sqrt((double)s->d));
+  a.rows = s->batch * s->h_q;
   if (pg) {
     a.ptab = pg->table;
     a.ptab_stride = pg->max_pages;
@@ -512,8 +513,8 @@ saga_status dense_impl(const saga_shape* s, const saga_pages* pg, const void* q,
         else hipLaunchKernelGGL((k_dense_partial<T, DK, DV, 16, P, TD, false>), grid, dim3(kBlock), 0, hs, a);
       }
     }
-    hipLaunchKernelGGL((k_dense_combine<DV>), dim3(DV / 16, s->h_q, s->batch), dim3(kBlock), 0, hs, a,
-                       (int)DenseCfg<T, DK, DV>::kChunk);
+    const dim3 cgrid = kDenseCombXcd<DV> ? dim3(8 * ((a.rows + 7) / 8) * (DV / 16)) : dim3(DV / 16, s->h_q, s->batch);
+    hipLaunchKernelGGL((k_dense_combine<DV>), cgrid, dim3(kBlock), 0, hs, a, (int)DenseCfg<T, DK, DV>::kChunk);
   }););
   return launched();
 }
