@@ -7,7 +7,9 @@ thresholds then keep from a few to every key of a row, so records overflow their
 seven inline entries into the chunk's segment of the kept list; a row whose
 threshold keeps nothing takes the forced refresh through the combining kernel.
 Every result is compared with the oracle (tests/parity.py rules), and repeated
-steps must give the same bits.
+steps must give the same bits. Further shapes that take the late form cover the
+kernel's other instantiations: fp32 caches with 64- and 128-wide heads (16 and 32
+blocks per row), and 64-wide keys with 128-wide values.
 """
 import numpy as np
 import pytest
@@ -88,3 +90,29 @@ def test_refresh_step_then_stale_steps():
     compare(r1, ref1, x, "bf16", check_tau=False)
     assert np.array_equal(r1["count"], r0["count"])
     torch.cuda.synchronize()
+
+
+LATE_SHAPES = [
+    # B, h_q, h_k, h_v, d, d_v, L, N, dtype
+    (1, 4, 1, 4, 64, 64, 131072, 256, "f32"),     # 256-byte fp32 value rows
+    (1, 4, 1, 2, 128, 128, 131072, 256, "f32"),   # 512-byte fp32 value rows
+    (4, 12, 1, 4, 64, 128, 65536, 128, "bf16"),   # 64-wide keys, 128-wide values, 512-key chunks
+]
+
+
+@pytest.mark.parametrize("case", range(len(LATE_SHAPES)))
+def test_other_late_instantiations(case):
+    B, h_q, h_k, h_v, d, dv, Lc, Nc, dtype = LATE_SHAPES[case]
+    say(f"late form at {LATE_SHAPES[case]}")
+    w = wl.Workload("late-gather-shapes", 310 + case, batch=B, h_q=h_q, h_k=h_k, h_v=h_v, d=d, d_v=dv, l_kv=Lc, N=Nc,
+                    refresh_period=1, dtype=dtype, plant_frac=0.005)
+    x = wl.generate(w, seed=case, lengths=[Lc] * B)
+    g = GpuCase(x, Nc, sel_cap=4 * Nc)
+    assert api.gather_form(api.make_shape(g.q, g.k, g.v), Nc, Lc) == "late"
+    q64, k64, v64 = x.f64()
+    r0 = g.step(4, 0)
+    ref0 = orc.saga_decode_step(q64, k64, v64, x.l_kv, Nc, 4, 0)
+    compare(r0, ref0, x, dtype, check_tau=True)
+    r1 = g.step(4, 1)
+    ref1 = orc.saga_decode_step(q64, k64, v64, x.l_kv, Nc, 4, 1, tau_in=ref0.tau)
+    compare(r1, ref1, x, dtype, check_tau=False)
