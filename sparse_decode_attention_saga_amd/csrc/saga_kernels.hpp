@@ -1471,22 +1471,27 @@ struct DenseArgs {
 // before l_kv arrives, for rows up to max_l_kv - 1 (inside the caches); logits of rows
 // at or past l_kv are masked and their value registers zeroed before use.
 //
-// P.V on the matrix cores (bf16 caches, d_v = 128, an even number of tiles): lane
+// P.V on the matrix cores (bf16 caches, d_v = 128 or 64, an even number of tiles): lane
 // (x, kq) = (lane & 15, lane >> 4) loads row 16t + 4kq + r of tile t at columns
-// 8x .. 8x+7. The score tile leaves p(head x, key 16t + 4kq + r) in that same lane, so
-// over a pair of tiles a lane holds, for the same 8 keys, the 8 weights of head x and
-// 8 values of each of its 8 columns: exactly the K-slice of a 16x16x32 bf16 MFMA's A
-// operand (rows = heads) and, taking element i of each value load, of its B operand
-// (columns 8n + i for n = 0..15). The fp32 weights enter as three bf16 terms (each the
-// rounding of what the previous ones leave, so their sum is the weight to within 2^-24
-// of it); values are exact in bf16 and products accumulate in fp32.
+// c x .. c x + c - 1, c = d_v / 16 (8 or 4). The score tile leaves p(head x, key
+// 16t + 4kq + r) in that same lane, so over a pair of tiles a lane holds, for the same
+// 8 keys, the 8 weights of head x and 8 values of each of its c columns: exactly the
+// K-slice of a 16x16x32 bf16 MFMA's A operand (rows = heads) and, taking element i of
+// each value load, of its B operand (columns c n + i for n = 0..15). The fp32 weights
+// enter as three bf16 terms (each the rounding of what the previous ones leave, so
+// their sum is the weight to within 2^-24 of it); values are exact in bf16 and
+// products accumulate in fp32.
 template <typename T, int DK, int DV, int GH, bool PAGED, int TPW, bool SPEC>
 __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
-  constexpr bool kMfmaPV = std::is_same<T, bf16_t>::value && DV == 128 && TPW % 2 == 0;
+  constexpr bool kMfmaPV = std::is_same<T, bf16_t>::value && (DV == 128 || DV == 64) && TPW % 2 == 0;
   constexpr int CHD = 16 * TPW * kWaves;
   constexpr int EPL = Unpack<T>::kN;
   constexpr int G = DV / EPL;                        // lanes per value row
-  constexpr int VL = (16 * DV) / (EPL * kWave);      // 16-byte value loads per lane per tile
+  // MFMA form: 4 value rows per lane and tile, DV / 16 columns each (a 16- or 8-byte
+  // load); VALU form: 16-byte loads spread over the tile
+  constexpr int NCOL = DV / 16;
+  using VLoad = typename std::conditional<kMfmaPV && DV == 64, uint2, uint4>::type;
+  constexpr int VL = kMfmaPV ? 4 : (16 * DV) / (EPL * kWave);  // value loads per lane per tile
   constexpr int KL = QK<T, DK>::kLoads;
   const T* const kbase = reinterpret_cast<const T*>(a.k);
   const T* const vbase = reinterpret_cast<const T*>(a.v);
@@ -1518,7 +1523,8 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   qk.load_q(qbase + (size_t)row0 * DK, gq, lane);
   // every key and value load of the wave, rows past L clamped to L - 1 (in bounds;
   // their logits are masked); a clamped tile lies inside one page
-  uint4 kb[TPW][KL], vb[TPW][VL];
+  uint4 kb[TPW][KL];
+  VLoad vb[TPW][VL];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int t0 = min(wbase + 16 * t, (L - 1) & ~15);
@@ -1530,11 +1536,12 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     }
   }
   // value row of load r of tile t (the MFMA form: row 4kq + r of the tile, columns
-  // 8 hh ..; the VALU form: flat element r*64 + lane of the tile's 16 x G grid)
+  // NCOL hh ..; the VALU form: flat element r*64 + lane of the tile's 16 x G grid)
   auto vrow = [&](int t, int r) {
     return wbase + 16 * t + (kMfmaPV ? 4 * kq + r : (r * kWave + lane) / G);
   };
-  const int vcol = kMfmaPV ? 8 * hh : ((lane % G) * EPL);
+  const int vcol = kMfmaPV ? NCOL * hh : ((lane % G) * EPL);
+  auto ldv = [](const T* p) { return *reinterpret_cast<const VLoad*>(p); };
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int t0 = min(wbase + 16 * t, (L - 1) & ~15);
@@ -1543,10 +1550,10 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     for (int r = 0; r < VL; ++r) {
       if constexpr (PAGED) {
         const int key = min(t0 + (vrow(t, r) - wbase - 16 * t), L - 1);
-        vb[t][r] = ld16(vt + (size_t)(key - t0) * DV + vcol);
+        vb[t][r] = ldv(vt + (size_t)(key - t0) * DV + vcol);
       } else {
         const int key = min(vrow(t, r), L - 1);
-        vb[t][r] = ld16(vt + (size_t)key * DV + vcol);
+        vb[t][r] = ldv(vt + (size_t)key * DV + vcol);
       }
     }
   }
@@ -1559,7 +1566,7 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int r = 0; r < VL; ++r)
-        if (vrow(t, r) >= L) vb[t][r] = make_uint4(0, 0, 0, 0);
+        if (vrow(t, r) >= L) vb[t][r] = VLoad{};
   }
   floatx4 sc[TPW];
 #pragma unroll
@@ -1592,9 +1599,9 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
   }
 
   if constexpr (kMfmaPV) {
-    floatx4 acc[8];
+    floatx4 acc[NCOL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NCOL; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tp = 0; tp < TPW; tp += 2) {
       // element e of a K-slice: key 16 (tp + e/4) + 4kq + e%4
@@ -1610,14 +1617,18 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
         w2[e] = h2;
         w3[e] = (__bf16)r2;
       }
-      const uint4* v0 = vb[tp];
-      const uint4* v1 = vb[tp + 1];
+      const VLoad* v0 = vb[tp];
+      const VLoad* v1 = vb[tp + 1];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NCOL; ++i) {
         // element i of each of the 8 value loads: word i/2, half i%2
         const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        auto word = [&](const uint4& u) {
-          return (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+        auto word = [&](const VLoad& u) {
+          if constexpr (NCOL == 4) {
+            return (i >> 1) == 0 ? u.x : u.y;
+          } else {
+            return (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+          }
         };
         V16 bw;
         bw.u.x = __builtin_amdgcn_perm(word(v0[1]), word(v0[0]), sel);
@@ -1629,14 +1640,15 @@ __global__ __launch_bounds__(kBlock) void k_dense_partial(const DenseArgs a) {
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w3, bw.h, acc[i], 0, 0, 0);
       }
     }
-    // lane (x, kq) holds the wave's sum for head 4kq + j, column 8x + i in acc[i][j]
+    // lane (x, kq) holds the wave's sum for head 4kq + j, column NCOL x + i in acc[i][j]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int h = 4 * kq + j;
       if (h < GH) {
-        *reinterpret_cast<float4*>(&s_o[wv][h][8 * hh]) = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
-        *reinterpret_cast<float4*>(&s_o[wv][h][8 * hh + 4]) =
-            make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+        *reinterpret_cast<float4*>(&s_o[wv][h][NCOL * hh]) = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+        if constexpr (NCOL == 8)
+          *reinterpret_cast<float4*>(&s_o[wv][h][8 * hh + 4]) =
+              make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
       }
     }
     __syncthreads();
