@@ -116,3 +116,23 @@ def test_other_late_instantiations(case):
     r1 = g.step(4, 1)
     ref1 = orc.saga_decode_step(q64, k64, v64, x.l_kv, Nc, 4, 1, tau_in=ref0.tau)
     compare(r1, ref1, x, dtype, check_tau=False)
+
+
+def test_stage_entry_points_equal_the_step_in_the_late_form():
+    say("saga_select_gather + saga_split_combine against the step, late form")
+    x = inputs(3)
+    g = GpuCase(x, N, sel_cap=4 * N)
+    g.step(4, 0)
+    ref = g.step(4, 1)                      # a step reusing the threshold of step 0
+    tau = g.tau.clone()
+    out = torch.empty_like(g.out)
+    cnt = torch.zeros_like(g.sel_count)
+    idx = torch.full_like(g.sel_idx, -1)
+    api.select_gather(g.q, g.k, g.v, g.l_kv, tau, N=N, max_l_kv=g.max_l_kv, workspace=g.ws)
+    api.split_combine(g.q, g.k, g.v, g.l_kv, tau, N=N, max_l_kv=g.max_l_kv, out=out, sel_count=cnt, sel_idx=idx,
+                      workspace=g.ws)
+    torch.cuda.synchronize()
+    # the same two launches as the step: the same bits
+    assert np.array_equal(out.double().cpu().numpy(), ref["O"])
+    assert np.array_equal(cnt.cpu().numpy(), ref["count"])
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
